@@ -1,0 +1,358 @@
+/*
+ * KroQuant online activation quantizer: CPU ORACLE.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  The GPU product path never calls it,
+ * and it shares no code, header, table or constant with the GPU library.
+ *
+ * It is deliberately plain and slow: every value is computed in double
+ * precision straight from its definition, one block at a time.
+ *
+ * Sources (the web pages describing arXiv 2607.21446, "KroQuant:
+ * Kronecker-Structured Block Transforms for Efficient Post-Training
+ * Quantization of Diffusion Transformers"):
+ *   [ABS]  the arXiv abstract, as reproduced on the mlsanity.com paper page
+ *          (section "Abstract (arXiv)"): one learned Kronecker-structured
+ *          invertible transform per 32-element activation block, inverse folded
+ *          into the weights, W4A4 MXFP4 ("MXFP4e2") quantization, SmoothQuant
+ *          per-channel scaling as the cheap alternative.
+ *   [KM]   the pith.science verdict record for 2607.21446, field
+ *          pith_extraction.key_machinery: the block-diagonal transform T with
+ *          blocks K^(j) = G1 (x) G2 (x) G3 (x) G4 (x) G5 of 2x2 factors, applied
+ *          online before the MX quantizer, inverse folded into the weights.
+ *   [LBA]  same record, skeptic_critique.load_bearing_attack (paper Section 3.2,
+ *          Eq. 4): T is block diagonal with 32x32 blocks aligned to the
+ *          quantizer's 32-element blocks.
+ *   [OCP]  the element (FP4 E2M1) and shared-scale (E8M0) encodings are not
+ *          spelled out on the pages, which only name MXFP4; they follow the
+ *          public OCP Microscaling Formats (MX) v1.0 specification:
+ *          shared exponent = floor(log2(max |v|)) - emax_elem (emax_elem = 2 for
+ *          E2M1), elements rounded to nearest-even and saturated at +-6.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - Kronecker order: numpy-style kron, so G1 acts on the most significant bit
+ *     of the 5-bit in-block index and G5 on the least significant bit.
+ *   - Orientation: a token row x (1x32) is transformed as y = x . K, so that
+ *     (X T)(T^-1 W^T) = X W^T, the invariance [ABS] relies on.
+ *   - Factor sets: nT = 1 (one set shared by every block) or nT = d/32 (set j
+ *     for the j-th block of every row).  Anything else is rejected.
+ *   - Sign of an element code is set iff y < 0; +0 and -0 both give code 0.
+ *   - An all-zero block gets shared exponent -127 (scale byte 0x00).
+ *   - A block holding a NaN or an infinity gets scale byte 0xFF (the E8M0 NaN
+ *     encoding) and all-zero codes.
+ *   - Nibble order: element 2i in bits 0-3, element 2i+1 in bits 4-7.
+ *   - SmoothQuant: y = fl32(x * fl32(1/s_c)), one rounding per step.
+ *   - The transformed value is rounded once, from its exact (double) value,
+ *     to fp32 before quantization; it is never rounded to bf16.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_ERR_ARG 1
+#define OR_ERR_SHAPE 2
+#define OR_ERR_SINGULAR 4
+
+/* ------------------------------------------------------------------ */
+/* bf16 decoding, written out from the format: 1 sign bit, 8 exponent  */
+/* bits (bias 127), 7 fraction bits.                                   */
+/* ------------------------------------------------------------------ */
+double oracle_bf16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 7) & 0xFF;
+    int frac = h & 0x7F;
+    double mag;
+    if (expo == 0xFF) {
+        mag = (frac == 0) ? INFINITY : NAN;
+    } else if (expo == 0) {
+        /* subnormal: 0.frac x 2^-126 */
+        mag = ldexp((double)frac / 128.0, -126);
+    } else {
+        mag = ldexp(1.0 + (double)frac / 128.0, expo - 127);
+    }
+    return sign ? -mag : mag;
+}
+
+/* ------------------------------------------------------------------ */
+/* The 32x32 Kronecker block  K = A1 (x) A2 (x) A3 (x) A4 (x) A5 [KM].  */
+/* f holds the five factors as f[k][r][c] (k = 0..4 for A1..A5).        */
+/* Entry (r, c): product over k of A_k[r_k][c_k], with r_k, c_k the     */
+/* k-th most significant of the five index bits.                        */
+/* ------------------------------------------------------------------ */
+void oracle_kron_block(const float *f, double *K)
+{
+    for (int r = 0; r < 32; ++r) {
+        for (int c = 0; c < 32; ++c) {
+            double p = 1.0;
+            for (int k = 0; k < 5; ++k) {
+                int rk = (r >> (4 - k)) & 1;
+                int ck = (c >> (4 - k)) & 1;
+                p *= (double)f[k * 4 + rk * 2 + ck];
+            }
+            K[r * 32 + c] = p;
+        }
+    }
+}
+
+/* Inverse block: the inverse of a Kronecker product is the Kronecker
+ * product of the inverses (in the same order), so T^-1 has blocks
+ * A1^-1 (x) ... (x) A5^-1 [ABS], [KM].  Each 2x2 inverse is the adjugate
+ * divided by the determinant. */
+int oracle_kron_block_inverse(const float *f, double *Kinv)
+{
+    double inv[20];
+    for (int k = 0; k < 5; ++k) {
+        double a = f[k * 4 + 0], b = f[k * 4 + 1], c = f[k * 4 + 2], d = f[k * 4 + 3];
+        double det = a * d - b * c;
+        if (!(fabs(det) >= 1e-30) || !isfinite(det))
+            return OR_ERR_SINGULAR;
+        inv[k * 4 + 0] = d / det;
+        inv[k * 4 + 1] = -b / det;
+        inv[k * 4 + 2] = -c / det;
+        inv[k * 4 + 3] = a / det;
+    }
+    for (int r = 0; r < 32; ++r) {
+        for (int c = 0; c < 32; ++c) {
+            double p = 1.0;
+            for (int k = 0; k < 5; ++k) {
+                int rk = (r >> (4 - k)) & 1;
+                int ck = (c >> (4 - k)) & 1;
+                p *= inv[k * 4 + rk * 2 + ck];
+            }
+            Kinv[r * 32 + c] = p;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* OCP MX shared scale [OCP]: E = floor(log2(amax)) - 2, clamped to     */
+/* the E8M0 range [-127, 127]; amax = 0 gives -127.  Returns 128 for a   */
+/* non-finite amax (the caller then writes the NaN byte 0xFF).          */
+/* floor(log2 amax) is taken from frexp, which is exact for every fp32  */
+/* value including subnormals: amax = m * 2^e with m in [0.5, 1).       */
+/* ------------------------------------------------------------------ */
+int oracle_e8m0_exponent(float amax)
+{
+    if (!isfinite(amax))
+        return 128;
+    if (amax == 0.0f)
+        return -127;
+    int e;
+    frexp((double)fabsf(amax), &e);
+    int E = (e - 1) - 2;
+    if (E < -127)
+        E = -127;
+    if (E > 127)
+        E = 127;
+    return E;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP4 E2M1 element code [OCP]: the magnitude |y| / 2^E is rounded to   */
+/* the nearest of the eight E2M1 magnitudes, ties going to the code     */
+/* whose mantissa bit is 0 (the even code), and magnitudes at or above   */
+/* 6 saturate to 6.  Bit 3 of the code is the sign (set iff y < 0).     */
+/* ------------------------------------------------------------------ */
+static const double E2M1_MAGNITUDE[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+int oracle_fp4_code(float y, int E)
+{
+    /* exact in double: |y| has 24 significant bits, the shift is a power of 2 */
+    double m = ldexp(fabs((double)y), -E);
+    int best;
+    if (m >= 6.0) {
+        best = 7;
+    } else {
+        best = 0;
+        double bestd = fabs(m - E2M1_MAGNITUDE[0]);
+        for (int i = 1; i < 8; ++i) {
+            double dist = fabs(m - E2M1_MAGNITUDE[i]);
+            /* strictly nearer wins; on an exact tie keep the even code */
+            if (dist < bestd || (dist == bestd && (i & 1) == 0 && (best & 1) == 1)) {
+                best = i;
+                bestd = dist;
+            }
+        }
+    }
+    return best | ((y < 0.0f) ? 8 : 0);
+}
+
+/* Quantize one block of 32 fp32 values to 16 packed code bytes and one
+ * E8M0 scale byte. */
+void oracle_mx_block(const float *y32, uint8_t *q16, uint8_t *sbyte)
+{
+    int finite = 1;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        if (!isfinite(y32[i]))
+            finite = 0;
+        else if (fabsf(y32[i]) > amax)
+            amax = fabsf(y32[i]);
+    }
+    if (!finite) {
+        *sbyte = 0xFF;
+        memset(q16, 0, 16);
+        return;
+    }
+    int E = oracle_e8m0_exponent(amax);
+    *sbyte = (uint8_t)(E + 127);
+    for (int i = 0; i < 16; ++i) {
+        int lo = oracle_fp4_code(y32[2 * i], E);
+        int hi = oracle_fp4_code(y32[2 * i + 1], E);
+        q16[i] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Shape rules shared by every entry point (same as the library's).     */
+/* ------------------------------------------------------------------ */
+static int check_shape(int64_t M, int64_t d)
+{
+    if (M < 0 || d <= 0)
+        return OR_ERR_ARG;
+    if (d % 32 != 0)
+        return OR_ERR_SHAPE;
+    return OR_OK;
+}
+
+static int check_sets(int64_t d, int64_t nT)
+{
+    if (nT != 1 && nT != d / 32)
+        return OR_ERR_SHAPE;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* KroQuant transform of a bf16 activation matrix [LBA], [KM]:          */
+/*   y[m, 32j + c] = sum_r x[m, 32j + r] * K_j[r][c]      (exact, double) */
+/*   z[m, 32j + c] = sum_r |x[m, 32j + r]| * |K_j[r][c]|                  */
+/* z is the magnitude scale the comparison tolerance is relative to.    */
+/* y or z may be NULL.                                                   */
+/* ------------------------------------------------------------------ */
+int oracle_kq_transform(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                        double *y, double *z)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    st = check_sets(d, nT);
+    if (st)
+        return st;
+    if (!x || !factors)
+        return OR_ERR_ARG;
+    int64_t nB = d / 32;
+    double *K = (double *)malloc((size_t)nT * 1024 * sizeof(double));
+    if (!K)
+        return OR_ERR_ARG;
+    for (int64_t t = 0; t < nT; ++t)
+        oracle_kron_block(factors + t * 20, K + t * 1024);
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nB; ++j) {
+            const double *Kj = K + (nT == 1 ? 0 : j) * 1024;
+            double xb[32];
+            for (int r = 0; r < 32; ++r)
+                xb[r] = oracle_bf16_to_double(x[m * d + j * 32 + r]);
+            for (int c = 0; c < 32; ++c) {
+                double acc = 0.0, mag = 0.0;
+                for (int r = 0; r < 32; ++r) {
+                    acc += xb[r] * Kj[r * 32 + c];
+                    mag += fabs(xb[r]) * fabs(Kj[r * 32 + c]);
+                }
+                if (y)
+                    y[m * d + j * 32 + c] = acc;
+                if (z)
+                    z[m * d + j * 32 + c] = mag;
+            }
+        }
+    }
+    free(K);
+    return OR_OK;
+}
+
+/* KroQuant quantizer: transform, round once to fp32, MX-quantize each
+ * block.  y32 (the fp32 pre-quantization values) may be NULL. */
+int oracle_kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                       uint8_t *q, uint8_t *s, float *y32)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    st = check_sets(d, nT);
+    if (st)
+        return st;
+    if (!x || !factors || !q || !s)
+        return OR_ERR_ARG;
+    int64_t nB = d / 32;
+    double *K = (double *)malloc((size_t)nT * 1024 * sizeof(double));
+    if (!K)
+        return OR_ERR_ARG;
+    for (int64_t t = 0; t < nT; ++t)
+        oracle_kron_block(factors + t * 20, K + t * 1024);
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nB; ++j) {
+            const double *Kj = K + (nT == 1 ? 0 : j) * 1024;
+            double xb[32];
+            float yb[32];
+            for (int r = 0; r < 32; ++r)
+                xb[r] = oracle_bf16_to_double(x[m * d + j * 32 + r]);
+            for (int c = 0; c < 32; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < 32; ++r)
+                    acc += xb[r] * Kj[r * 32 + c];
+                yb[c] = (float)acc; /* one rounding, to nearest even */
+            }
+            int64_t b = m * nB + j;
+            oracle_mx_block(yb, q + b * 16, s + b);
+            if (y32)
+                memcpy(y32 + m * d + j * 32, yb, sizeof yb);
+        }
+    }
+    free(K);
+    return OR_OK;
+}
+
+/* SmoothQuant-style per-channel scaling [ABS]: x_c / s_c, taken as a
+ * multiply by the fp32 reciprocal, then the same MX quantizer. */
+int oracle_sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale,
+                       uint8_t *q, uint8_t *s, float *y32)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    if (!x || !scale || !q || !s)
+        return OR_ERR_ARG;
+    int64_t nB = d / 32;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nB; ++j) {
+            float yb[32];
+            for (int c = 0; c < 32; ++c) {
+                float recip = 1.0f / scale[j * 32 + c];
+                float xf = (float)oracle_bf16_to_double(x[m * d + j * 32 + c]);
+                yb[c] = xf * recip;
+            }
+            int64_t b = m * nB + j;
+            oracle_mx_block(yb, q + b * 16, s + b);
+            if (y32)
+                memcpy(y32 + m * d + j * 32, yb, sizeof yb);
+        }
+    }
+    return OR_OK;
+}
+
+/* Plain MXFP4 quantization of an fp32 matrix (no transform). */
+int oracle_mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    if (!x || !q || !s)
+        return OR_ERR_ARG;
+    int64_t nblk = M * (d / 32);
+    for (int64_t b = 0; b < nblk; ++b)
+        oracle_mx_block(x + b * 32, q + b * 16, s + b);
+    return OR_OK;
+}

@@ -1,0 +1,64 @@
+"""The pins must catch plausible mistakes.  Each case plants one mistake in a
+copy of the oracle source (on the CPU), builds it, and checks that the pin
+meant to guard that step fails against the mutated oracle."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import tests.test_oracle_pins as pins
+from oracle import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.LIB_PATH), "kq_oracle.c")
+
+MUTATIONS = {
+    # name: (original text, replacement, pin that must fail, pin arguments)
+    "kron_bit_order_lsb_first": (
+        "int rk = (r >> (4 - k)) & 1;\n                int ck = (c >> (4 - k)) & 1;\n                p *= (double)f",
+        "int rk = (r >> k) & 1;\n                int ck = (c >> k) & 1;\n                p *= (double)f",
+        "test_kron_block_equals_numpy_kron", {"seed": 1}),
+    "transposed_block": (
+        "acc += xb[r] * Kj[r * 32 + c];\n                    mag",
+        "acc += xb[r] * Kj[c * 32 + r];\n                    mag",
+        "test_transform_equals_modewise_product", {}),
+    "ties_round_up": (
+        "if (dist < bestd || (dist == bestd && (i & 1) == 0 && (best & 1) == 1)) {",
+        "if (dist <= bestd) {",
+        "test_mx_block_handcases", {"case": pins._load_handcases()[1]}),
+    "scale_exponent_off_by_one": (
+        "int E = (e - 1) - 2;",
+        "int E = e - 2;",
+        "test_mx_block_handcases", {"case": pins._load_handcases()[0]}),
+    "sign_from_signbit": (
+        "return best | ((y < 0.0f) ? 8 : 0);",
+        "return best | (signbit(y) ? 8 : 0);",
+        "test_mx_block_handcases", {"case": pins._load_handcases()[7]}),
+    "zero_block_scale_one": (
+        "if (amax == 0.0f)\n        return -127;",
+        "if (amax == 0.0f)\n        return 0;",
+        "test_mx_block_handcases", {"case": pins._load_handcases()[6]}),
+    "inverse_wrong_order": (
+        "p *= inv[k * 4 + rk * 2 + ck];",
+        "p *= inv[k * 4 + ck * 2 + rk];",
+        "test_inverse_is_kron_of_factor_inverses", {"seed": 4}),
+    "sq_divides_in_double": (
+        "float recip = 1.0f / scale[j * 32 + c];\n                float xf = (float)oracle_bf16_to_double(x[m * d + j * 32 + c]);\n                yb[c] = xf * recip;",
+        "float recip = 1.0f / scale[j * 32 + c];\n                float xf = (float)oracle_bf16_to_double(x[m * d + j * 32 + c]);\n                yb[c] = (float)((double)xf / (double)scale[j * 32 + c]); (void)recip;",
+        "test_sq_rounds_once_per_step", {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pin_catches_planted_mistake(name, tmp_path, monkeypatch):
+    old, new, pin, kwargs = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut_c = tmp_path / "kq_oracle_mut.c"
+    mut_c.write_text(src.replace(old, new))
+    mut_so = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", str(mut_so), str(mut_c), "-lm"], check=True)
+    L = oracle.bind(ctypes.CDLL(str(mut_so)))
+    monkeypatch.setattr(oracle, "_lib", L)
+    with pytest.raises(AssertionError):
+        getattr(pins, pin)(oracle_lib=oracle, **kwargs)

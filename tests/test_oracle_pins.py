@@ -1,0 +1,279 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself (a library routine, a closed form, a hand-derived fixture, brute force).
+
+Sources: the abstract on the mlsanity.com page for arXiv 2607.21446 (block
+transform + inverse on the weights, MXFP4), the pith.science verdict record
+for the same paper (pith_extraction.key_machinery: K = G1 (x) ... (x) G5 of
+2x2 factors; pith_extraction.core_discovery: Hadamard is five identical 2x2
+factors; skeptic_critique.load_bearing_attack, paper Section 3.2 Eq. 4:
+block-diagonal 32x32 blocks), and the OCP MX v1.0 encodings for E2M1 / E8M0.
+"""
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from synth import inputs as I
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def kron5(f5):
+    """numpy's kron chain A1 (x) A2 (x) A3 (x) A4 (x) A5 in float64."""
+    K = np.array([[1.0]])
+    for k in range(5):
+        K = np.kron(K, f5[k].astype(np.float64))
+    return K
+
+
+# ---------------------------------------------------------------------------
+# bf16 decoding: every one of the 65536 patterns against numpy's bit view
+# ---------------------------------------------------------------------------
+def test_bf16_decode_all_patterns(oracle_lib):
+    import ctypes
+    L = oracle_lib.lib()
+    pats = np.arange(65536, dtype=np.uint32)
+    ref = (pats << 16).view(np.float32).astype(np.float64)
+    got = np.array([L.oracle_bf16_to_double(ctypes.c_uint16(int(p))) for p in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zero preserved
+    assert math.copysign(1.0, got[0x8000]) == -1.0
+
+
+# ---------------------------------------------------------------------------
+# Kronecker block: library kron, mode-wise product, inverse, det, cond
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_kron_block_equals_numpy_kron(oracle_lib, seed):
+    f = I.random_factors(1, seed)[0]
+    K = oracle_lib.kron_block(f)
+    R = kron5(f)
+    assert np.allclose(K, R, rtol=1e-15, atol=0.0)
+
+
+def test_kron_bit_order_is_msb_first(oracle_lib):
+    # A1 = diag(1, 2) and the rest identity: the factor 2 must land on the
+    # second half of the block (index bit 4 set), as numpy's kron does.
+    f = I.identity_factors(1)[0].copy()
+    f[0] = np.diag([1.0, 2.0])
+    K = oracle_lib.kron_block(f)
+    assert np.array_equal(np.diag(K), np.array([1.0] * 16 + [2.0] * 16))
+    f = I.identity_factors(1)[0].copy()
+    f[4] = np.diag([1.0, 2.0])
+    K = oracle_lib.kron_block(f)
+    assert np.array_equal(np.diag(K), np.array([1.0, 2.0] * 16))
+
+
+def test_transform_equals_modewise_product(oracle_lib):
+    M, d = 7, 256
+    x = I.act_gaussian_outliers(M, d, 11, 3, 30.0)[0]
+    f = I.random_factors(d // 32, 12)
+    y, z = oracle_lib.kq_transform(x, f)
+    X = I.bf16_bits_to_f32(x).astype(np.float64).reshape(M, d // 32, 2, 2, 2, 2, 2)
+    F = f.astype(np.float64)
+    ref = np.einsum("mjabcde,jaA,jbB,jcC,jdD,jeE->mjABCDE", X, F[:, 0], F[:, 1], F[:, 2], F[:, 3], F[:, 4],
+                    optimize=True).reshape(M, d)
+    assert np.all(np.abs(y - ref) <= 1e-12 * z)
+    # and the dense product x_blk @ K_j with numpy's kron
+    dense = np.concatenate([X.reshape(M, d // 32, 32)[:, j] @ kron5(f[j]) for j in range(d // 32)], axis=1)
+    assert np.all(np.abs(y - dense) <= 1e-12 * z)
+    # z is the same contraction on magnitudes
+    zref = np.concatenate([np.abs(X.reshape(M, d // 32, 32)[:, j]) @ np.abs(kron5(f[j])) for j in range(d // 32)],
+                          axis=1)
+    assert np.allclose(z, zref, rtol=1e-13, atol=0)
+
+
+def test_shared_factor_set_applies_to_every_block(oracle_lib):
+    M, d = 3, 128
+    x = I.act_gaussian_outliers(M, d, 5, 2, 10.0)[0]
+    f1 = I.random_factors(1, 9)
+    y1 = oracle_lib.kq_transform(x, f1, want_z=False)
+    y4 = oracle_lib.kq_transform(x, np.repeat(f1, d // 32, axis=0), want_z=False)
+    assert np.array_equal(y1, y4)
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_inverse_is_kron_of_factor_inverses(oracle_lib, seed):
+    f = I.random_factors(1, seed)[0]
+    K = oracle_lib.kron_block(f)
+    Kinv = oracle_lib.kron_block_inverse(f)
+    cond = np.linalg.cond(K)
+    assert np.abs(Kinv @ K - np.eye(32)).max() <= 1e-12 * cond
+    assert np.allclose(Kinv, np.linalg.inv(K), rtol=0, atol=1e-12 * cond * np.abs(Kinv).max())
+    # determinant: det(A (x) B) = det(A)^m det(B)^n, so det K = prod det(A_k)^16
+    sign, logdet = np.linalg.slogdet(K)
+    dets = [np.linalg.det(f[k].astype(np.float64)) for k in range(5)]
+    expect = np.prod(np.array(dets) ** 16)
+    assert sign > 0 and np.isclose(logdet, math.log(expect), rtol=0, atol=1e-10)
+    # condition number of a Kronecker product is the product of the conditions
+    conds = [np.linalg.cond(f[k].astype(np.float64)) for k in range(5)]
+    assert np.isclose(cond, np.prod(conds), rtol=1e-9)
+
+
+def test_lu_factors_have_det_minus_one_and_block_det_plus_one(oracle_lib):
+    # G = L U with L = [[1,0],[c,1]], U = [[a,b],[0,-1/a]] has det -1 per factor;
+    # five such factors give det K = (-1)^(16*5) = +1, not -1.
+    rng = np.random.default_rng(3)
+    f = np.empty((5, 2, 2), np.float32)
+    for k in range(5):
+        a, b, c = rng.uniform(0.5, 1.5), rng.uniform(-1, 1), rng.uniform(-1, 1)
+        L = np.array([[1, 0], [c, 1]])
+        U = np.array([[a, b], [0, -1 / a]])
+        f[k] = (L @ U).astype(np.float32)
+    K = oracle_lib.kron_block(f)
+    dets = [np.linalg.det(f[k].astype(np.float64)) for k in range(5)]
+    assert all(abs(dd + 1) < 1e-6 for dd in dets)
+    assert np.isclose(np.linalg.det(K), np.prod(np.array(dets) ** 16), rtol=1e-9)
+    assert np.linalg.det(K) > 0
+
+
+def test_singular_factor_is_rejected(oracle_lib):
+    f = I.identity_factors(1)[0].copy()
+    f[2] = np.array([[1.0, 2.0], [2.0, 4.0]])
+    with pytest.raises(oracle_lib.OracleError):
+        oracle_lib.kron_block_inverse(f)
+
+
+# ---------------------------------------------------------------------------
+# exact invariance (X T)(T^-1 W^T) = X W^T with integer unimodular factors
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shared", [True, False])
+def test_exact_invariance_integer_factors(oracle_lib, shared):
+    rng = np.random.default_rng(21)
+    M, d, N = 5, 128, 6
+    nB = d // 32
+    f = I.integer_unimodular_factors(1 if shared else nB, 33)
+    x_int = rng.integers(-3, 4, size=(M, d)).astype(np.float32)
+    w_int = rng.integers(-3, 4, size=(N, d)).astype(np.float64)
+    x = I.f32_to_bf16_bits(x_int)  # small integers are exact in bf16
+    y = oracle_lib.kq_transform(x, f, want_z=False)
+    assert np.array_equal(y, np.round(y)), "integer factors and inputs give integer outputs"
+    blocks = [oracle_lib.kron_block_inverse(f[0 if shared else j]) for j in range(nB)]
+    Tinv = scipy.linalg.block_diag(*blocks)
+    assert np.array_equal(Tinv, np.round(Tinv))
+    lhs = y @ (Tinv @ w_int.T)
+    rhs = x_int.astype(np.float64) @ w_int.T
+    assert np.array_equal(lhs, rhs)
+
+
+def test_invariance_real_factors(oracle_lib):
+    rng = np.random.default_rng(22)
+    M, d, N = 4, 96, 3
+    f = I.random_factors(d // 32, 44)
+    x = I.act_gaussian_outliers(M, d, 23, 2, 30.0)[0]
+    w = rng.standard_normal((N, d))
+    y = oracle_lib.kq_transform(x, f, want_z=False)
+    Tinv = scipy.linalg.block_diag(*[oracle_lib.kron_block_inverse(f[j]) for j in range(d // 32)])
+    cond = max(np.linalg.cond(oracle_lib.kron_block(f[j])) for j in range(d // 32))
+    lhs = y @ (Tinv @ w.T)
+    rhs = I.bf16_bits_to_f32(x).astype(np.float64) @ w.T
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-10 * cond * np.abs(rhs).max())
+
+
+# ---------------------------------------------------------------------------
+# special factor sets
+# ---------------------------------------------------------------------------
+def test_identity_factors_reduce_to_plain_mxfp4(oracle_lib):
+    x, _, _ = I.act_sweep_special(64, 1024, 77, special_frac=0.02)
+    q1, s1, y1 = oracle_lib.kq_quantize(x, I.identity_factors(1), want_y32=True)
+    q2, s2 = oracle_lib.mx_quantize_f32(I.bf16_bits_to_f32(x))
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    # the transformed values are the inputs themselves (as real numbers)
+    assert np.array_equal(y1, I.bf16_bits_to_f32(x) + np.float32(0.0))
+    # and SmoothQuant with unit scales is the same quantizer
+    q3, s3 = oracle_lib.sq_quantize(x, np.ones(1024, np.float32))
+    assert np.array_equal(q1, q3) and np.array_equal(s1, s3)
+
+
+def test_hadamard_factors_give_normalised_wht32(oracle_lib):
+    M, d = 9, 64
+    x = I.act_gaussian_outliers(M, d, 31, 2, 30.0)[0]
+    y, z = oracle_lib.kq_transform(x, I.hadamard_factors(1))
+    H = scipy.linalg.hadamard(32).astype(np.float64)  # Sylvester order
+    assert np.array_equal(H @ H.T, 32 * np.eye(32))
+    X = I.bf16_bits_to_f32(x).astype(np.float64).reshape(M, d // 32, 32)
+    c = float(np.float32(1.0 / math.sqrt(2.0))) ** 5  # the fp32 factors, exactly
+    ref = (X @ H).reshape(M, d) * c
+    assert np.all(np.abs(y - ref) <= 1e-12 * z)
+    # against the exact normalised WHT: off only by fl32(1/sqrt 2)^5 vs 1/sqrt(32)
+    ref_exact = (X @ H).reshape(M, d) / math.sqrt(32.0)
+    assert np.all(np.abs(y - ref_exact) <= 5 * 2.0 ** -24 * z)
+
+
+# ---------------------------------------------------------------------------
+# MX quantizer: hand-derived fixtures and exhaustive element / scale sweeps
+# ---------------------------------------------------------------------------
+def _load_handcases():
+    with open(os.path.join(HERE, "golden", "mx_handcases.json")) as fh:
+        return json.load(fh)["cases"]
+
+
+@pytest.mark.parametrize("case", _load_handcases(), ids=lambda c: c["name"])
+def test_mx_block_handcases(oracle_lib, case):
+    y = np.array([float.fromhex(v) if v.lower().lstrip("-").startswith("0x") else float(v) for v in case["y"]],
+                 np.float32)
+    q, sbyte = oracle_lib.mx_block(y)
+    codes = np.array(case["codes"], np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    assert sbyte == case["scale_byte"]
+    assert np.array_equal(q, packed), (q, packed)
+
+
+def test_grid_and_scale_bruteforce(oracle_lib, tmp_path):
+    exe = tmp_path / "grid_bruteforce"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-o", str(exe),
+                    os.path.join(HERE, "pins", "grid_bruteforce.c"), "-ldl", "-lpthread", "-lm"], check=True)
+    nth = str(min(16, os.cpu_count() or 1))
+    args = [str(exe), oracle_lib.LIB_PATH, nth]
+    if os.environ.get("KQ_PIN_FULL"):
+        args.append("full")
+    r = subprocess.run(args, capture_output=True, text=True, timeout=1200)
+    print(r.stdout)
+    assert r.returncode == 0 and r.stdout.strip().endswith("PASS"), r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------
+# SmoothQuant reading and shape rules
+# ---------------------------------------------------------------------------
+def test_sq_power_of_two_scales_are_exact_division(oracle_lib):
+    M, d = 6, 128
+    x = I.act_gaussian_outliers(M, d, 41, 4, 30.0)[0]
+    k = np.random.default_rng(5).integers(-6, 7, size=d)
+    scale = np.ldexp(np.ones(d, np.float32), k).astype(np.float32)
+    _, _, y = oracle_lib.sq_quantize(x, scale, want_y32=True)
+    assert np.array_equal(y, np.ldexp(I.bf16_bits_to_f32(x), -k[None, :]).astype(np.float32))
+
+
+def test_sq_rounds_once_per_step(oracle_lib):
+    # y = fl32(x * fl32(1/s)): check against python's correctly rounded doubles
+    M, d = 4, 64
+    x = I.act_gaussian_outliers(M, d, 42, 2, 30.0)[0]
+    scale = (1.0 + np.random.default_rng(6).random(d) * 7).astype(np.float32)
+    _, _, y = oracle_lib.sq_quantize(x, scale, want_y32=True)
+    xf = I.bf16_bits_to_f32(x).astype(np.float64)
+    recip = np.array([np.float32(1.0 / float(s)) for s in scale], np.float64)  # 1/s correctly rounded to fp32
+    # the exact product of two fp32 values fits a double, so one cast rounds it once
+    assert np.array_equal(y, (xf * recip[None, :]).astype(np.float32))
+
+
+def test_shape_rules(oracle_lib):
+    import ctypes
+    L = oracle_lib.lib()
+    x = np.zeros((2, 64), np.uint16)
+    f = I.identity_factors(2)
+    q = np.zeros((2, 32), np.uint8)
+    s = np.zeros((2, 2), np.uint8)
+    P = lambda a: a.ctypes.data  # noqa: E731
+    assert L.oracle_kq_quantize(P(x), 2, 64, P(f), 2, P(q), P(s), None) == 0
+    assert L.oracle_kq_quantize(P(x), 2, 64, P(f), 1, P(q), P(s), None) == 0
+    assert L.oracle_kq_quantize(P(x), 2, 48, P(f), 1, P(q), P(s), None) == 2  # d % 32
+    assert L.oracle_kq_quantize(P(x), 2, 64, P(f), 3, P(q), P(s), None) == 2  # nT not in {1, d/32}
+    assert L.oracle_kq_quantize(P(x), -1, 64, P(f), 1, P(q), P(s), None) == 1
+    assert L.oracle_kq_quantize(P(x), 0, 64, P(f), 1, P(q), P(s), None) == 0  # empty is fine
+    del ctypes
