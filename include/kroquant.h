@@ -1,0 +1,144 @@
+/*
+ * kroquant.h - C ABI of the MI355X (gfx950) KroQuant activation quantizer.
+ *
+ * What the library computes (pages describing arXiv 2607.21446, "KroQuant:
+ * Kronecker-Structured Block Transforms for Efficient Post-Training
+ * Quantization of Diffusion Transformers"):
+ *   - the abstract (mlsanity.com paper page, section "Abstract (arXiv)"): a
+ *     learned Kronecker-structured invertible transform applied online to each
+ *     32-element block of an activation row, its inverse folded into the
+ *     weights offline, W4A4 with MXFP4 ("MXFP4e2"); per-channel scaling
+ *     (SmoothQuant) is the cheap alternative it is compared with;
+ *   - the pith.science verdict record for 2607.21446, field
+ *     pith_extraction.key_machinery: every 32x32 block is
+ *     K = A1 (x) A2 (x) A3 (x) A4 (x) A5 of five 2x2 factors, applied before
+ *     the MX quantizer;
+ *   - same record, skeptic_critique.load_bearing_attack (paper Section 3.2,
+ *     Eq. 4): the transform is block diagonal, blocks aligned with the
+ *     quantizer's 32-element blocks.
+ * Element and scale encodings follow the OCP Microscaling (MX) v1.0 spec:
+ * FP4 E2M1 codes (sign in bit 3), round to nearest even, saturating at +-6;
+ * one E8M0 byte per 32 elements holding E + 127 with
+ * E = clamp(floor(log2(max|y|)) - 2, -127, 127).
+ *
+ * Conventions shared by every entry point
+ *   - Layouts are dense row-major.  x[M, d] is bf16 (passed as its uint16 bit
+ *     patterns), q[M, d/2] holds packed codes (element 2i in bits 0-3 of byte
+ *     i, element 2i+1 in bits 4-7), s[M, d/32] holds one E8M0 byte per block
+ *     of 32 consecutive elements of a row.
+ *   - Block b = m * (d/32) + j covers x[m, 32j .. 32j+31], q bytes
+ *     [16b, 16b+16) and s byte b.
+ *   - factors is float32 [nT, 5, 2, 2]: factors[t][k][r][c] is entry (r, c) of
+ *     A_{k+1} of set t.  nT = 1 shares one set among all blocks; nT = d/32
+ *     gives set j to block column j.  A1 acts on the most significant bit of
+ *     the 5-bit in-block index (numpy kron order).  A row block x (1x32) is
+ *     transformed as y = x . K, so (X T)(T^-1 W^T) = X W^T.
+ *   - Sign of a code is set iff its value is < 0 (+0 and -0 give code 0).  An
+ *     all-zero block has scale byte 0x00.  A block whose transformed values
+ *     contain a NaN or an infinity gets scale byte 0xFF and zero codes.
+ *   - "dev" pointers are device (HBM) pointers, "host" pointers are host
+ *     memory.  The caller owns every buffer.  Device entry points never
+ *     allocate, free or synchronise: they check their arguments on the host,
+ *     enqueue kernels on `stream` (a hipStream_t; NULL is the default stream)
+ *     and return.  A kernel fault surfaces at the caller's next
+ *     synchronisation.  Inputs are read-only; q and s are fully overwritten.
+ *   - M == 0 is a successful no-op (pointers are not inspected).
+ *   - Argument errors are reported before any HIP call and launch nothing.
+ *   - Every entry point is stateless and reentrant.
+ */
+#ifndef KROQUANT_H
+#define KROQUANT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define KQ_OK 0
+#define KQ_ERR_ARG 1      /* null pointer, M < 0, d <= 0, bad variant */
+#define KQ_ERR_SHAPE 2    /* d % 32 != 0, nT not in {1, d/32}, size too large for a launch */
+#define KQ_ERR_ALIGN 3    /* x, q, y not 16-byte aligned, factors / scale not 4-byte aligned */
+#define KQ_ERR_SINGULAR 4 /* host helpers: a 2x2 factor with |det| < 1e-30 or a non-finite entry */
+#define KQ_ERR_HIP 5      /* the HIP runtime reported an error at launch */
+#define KQ_ERR_OVERLAP 6  /* an output buffer overlaps an input or another output */
+
+/* transform variants for kq_quantize_ex / kq_transform_f32 */
+#define KQ_VARIANT_AUTO 0      /* the library's default (the faster one on MI355X) */
+#define KQ_VARIANT_MFMA 1      /* dense 32x32 block on bf16 MFMA, K as an exact 3-term bf16 split */
+#define KQ_VARIANT_BUTTERFLY 2 /* five 2x2 stages in fp32 registers, cross-lane stages via DPP */
+
+/*
+ * kq_quantize: KroQuant online quantizer.  For every block, y = x_blk . K_j in
+ * fp32 accumulation, then MXFP4 quantization of y (abstract; key_machinery).
+ *   x        dev, bf16 bits [M, d], 16-byte aligned
+ *   factors  dev, float32 [nT, 5, 2, 2], nT = 1 or d/32, 4-byte aligned
+ *   q        dev, uint8 [M, d/2], 16-byte aligned
+ *   s        dev, uint8 [M, d/32], any alignment
+ *   stream   hipStream_t or NULL
+ * Returns KQ_OK or an error code (nothing launched on error).
+ */
+int kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                uint8_t *s, void *stream);
+
+/* kq_quantize with an explicit transform variant (KQ_VARIANT_*). */
+int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                   uint8_t *s, int variant, void *stream);
+
+/*
+ * kq_transform_f32: the transformed values y = x_blk . K_j (fp32) that
+ * kq_quantize quantizes, written out for inspection.  Same transform code as
+ * the quantizer for the chosen variant.
+ *   y  dev, float32 [M, d], 16-byte aligned
+ */
+int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                     int variant, void *stream);
+
+/*
+ * sq_quantize: SmoothQuant-style comparison quantizer (abstract: per-channel
+ * scaling).  y[m, c] = x[m, c] * fl32(1 / scale[c]) rounded once to fp32, then
+ * the same MXFP4 quantization.
+ *   scale  dev, float32 [d], 4-byte aligned
+ */
+int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
+                void *stream);
+
+/*
+ * mx_quantize_f32: plain MXFP4 quantization of an fp32 matrix (no transform).
+ *   x  dev, float32 [M, d], 16-byte aligned
+ */
+int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream);
+
+/* ---------------- host helpers for the offline weight side --------------- */
+/* All pointers are host memory; the calls are synchronous and touch no GPU.  */
+
+/* inv[t][k] = A_k^-1 of set t, for every set and factor (abstract: the
+ * inverse goes to the weights; key_machinery: inverse of a Kronecker product
+ * is the Kronecker product of the inverses).  inv: float32 [nT, 5, 2, 2]. */
+int kq_factor_inverse(const float *factors, int64_t nT, float *inv);
+
+/* K[t] = A1 (x) ... (x) A5 of set t as a dense float32 [nT, 32, 32] matrix
+ * (row r = input index, column c = output index: y = x . K). */
+int kq_block_matrix(const float *factors, int64_t nT, float *K);
+
+/* Kinv[t] = A1^-1 (x) ... (x) A5^-1 = K[t]^-1, float32 [nT, 32, 32]. */
+int kq_block_inverse(const float *factors, int64_t nT, float *Kinv);
+
+/* Fold T^-1 into a weight matrix W[N, d] (float32, row-major), so that for
+ * Y = X T the product Y W_out^T equals X W^T:  W_out = W T^-T, i.e. for every
+ * row n and block j, W_out[n, 32j:32j+32] = W[n, 32j:32j+32] . (K_j^-1)^T.
+ * Accumulates in double, rounds once to float32.  W_out may equal W. */
+int kq_fold_weight(const float *W, int64_t N, int64_t d, const float *factors, int64_t nT, float *W_out);
+
+/* Text for a status code (static storage). */
+const char *kq_status_string(int status);
+
+/* Build description (target, variant defaults), static storage. */
+const char *kq_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KROQUANT_H */

@@ -1,0 +1,236 @@
+"""ctypes binding of libkroquant.so: argument marshalling only.
+
+Every computation runs in the library (HIP kernels on the GPU, or the C++
+host helpers).  Device functions take torch tensors that already live on the
+GPU and enqueue on the given stream (default: torch's current stream); they
+return without synchronising.  There is no fallback: if the library is not
+built, importing this module raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkroquant.so")
+
+KQ_OK = 0
+KQ_ERR_ARG = 1
+KQ_ERR_SHAPE = 2
+KQ_ERR_ALIGN = 3
+KQ_ERR_SINGULAR = 4
+KQ_ERR_HIP = 5
+KQ_ERR_OVERLAP = 6
+
+KQ_VARIANT_AUTO = 0
+KQ_VARIANT_MFMA = 1
+KQ_VARIANT_BUTTERFLY = 2
+
+# every symbol the public header declares
+EXPORTS = (
+    "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
+    "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
+    "kq_status_string", "kq_build_info",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m mxfp4_act_quantizer_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+_lib.kq_quantize.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
+_lib.kq_quantize_ex.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _INT, _P]
+_lib.kq_transform_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _INT, _P]
+_lib.sq_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
+_lib.mx_quantize_f32.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
+_lib.kq_block_matrix.argtypes = [_P, _I64, _P]
+_lib.kq_block_inverse.argtypes = [_P, _I64, _P]
+_lib.kq_fold_weight.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+_lib.kq_status_string.argtypes = [_INT]
+_lib.kq_status_string.restype = ctypes.c_char_p
+_lib.kq_build_info.argtypes = []
+_lib.kq_build_info.restype = ctypes.c_char_p
+_lib.kq_set_tuning.argtypes = [_INT, _INT]
+for _name in EXPORTS + ("kq_set_tuning",):
+    if _name not in ("kq_status_string", "kq_build_info"):
+        getattr(_lib, _name).restype = _INT
+
+
+class KQError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {kq_status_string(status)} (status {status})")
+
+
+def kq_status_string(status):
+    return _lib.kq_status_string(int(status)).decode()
+
+
+def kq_build_info():
+    return _lib.kq_build_info().decode()
+
+
+def lib():
+    """The loaded ctypes library (raw C entry points)."""
+    return _lib
+
+
+def _check(st, where):
+    if st != KQ_OK:
+        raise KQError(st, where)
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors on the GPU)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtypes, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _outputs(x, M, d, q, s):
+    torch = _torch()
+    if q is None:
+        q = torch.empty((M, d // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, d // 32), dtype=torch.uint8, device=x.device)
+    return q, s
+
+
+def _md(x):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, d]")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def _nT(factors):
+    n = factors.numel()
+    if n % 20:
+        raise ValueError("factors must hold [nT, 5, 2, 2] float32 values")
+    return n // 20
+
+
+def kq_quantize(x, factors, q=None, s=None, stream=None, variant=KQ_VARIANT_AUTO):
+    """KroQuant quantizer: returns (q [M, d/2] u8, s [M, d/32] u8)."""
+    torch = _torch()
+    M, d = _md(x)
+    q, s = _outputs(x, M, d, q, s)
+    st = _lib.kq_quantize_ex(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
+                             _nT(factors), _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"),
+                             int(variant), _stream_handle(stream))
+    _check(st, "kq_quantize")
+    return q, s
+
+
+def kq_quantize_ex(x, factors, q, s, variant, stream=None):
+    return kq_quantize(x, factors, q, s, stream, variant)
+
+
+def kq_transform_f32(x, factors, y=None, stream=None, variant=KQ_VARIANT_AUTO):
+    """Transformed values y = x_blk . K_j (fp32) as the quantizer computes them."""
+    torch = _torch()
+    M, d = _md(x)
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    st = _lib.kq_transform_f32(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
+                               _nT(factors), _dev(y, (torch.float32,), "y"), int(variant), _stream_handle(stream))
+    _check(st, "kq_transform_f32")
+    return y
+
+
+def sq_quantize(x, scale, q=None, s=None, stream=None):
+    """SmoothQuant comparison quantizer: y = x * fl32(1/scale_c), then MXFP4."""
+    torch = _torch()
+    M, d = _md(x)
+    q, s = _outputs(x, M, d, q, s)
+    st = _lib.sq_quantize(_dev(x, _bf16_types(), "x"), M, d, _dev(scale, (torch.float32,), "scale"),
+                          _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    _check(st, "sq_quantize")
+    return q, s
+
+
+def mx_quantize_f32(x, q=None, s=None, stream=None):
+    """Plain MXFP4 quantization of an fp32 matrix."""
+    torch = _torch()
+    M, d = _md(x)
+    q, s = _outputs(x, M, d, q, s)
+    st = _lib.mx_quantize_f32(_dev(x, (torch.float32,), "x"), M, d, _dev(q, (torch.uint8,), "q"),
+                              _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    _check(st, "mx_quantize_f32")
+    return q, s
+
+
+def set_tuning(key, value):
+    """Launch-shape knobs for measurements: 0 MFMA tiles/wave, 1 butterfly rows/wave,
+    2 SmoothQuant/fp32 rows/wave (0 = automatic)."""
+    _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
+
+
+# ---------------------------------------------------------------------------
+# host helpers (numpy arrays, synchronous)
+# ---------------------------------------------------------------------------
+def _host_f32(a, name):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def kq_factor_inverse(factors):
+    f = _host_f32(factors, "factors")
+    nT = f.size // 20
+    out = np.empty((nT, 5, 2, 2), np.float32)
+    _check(_lib.kq_factor_inverse(f.ctypes.data, nT, out.ctypes.data), "kq_factor_inverse")
+    return out
+
+
+def kq_block_matrix(factors):
+    f = _host_f32(factors, "factors")
+    nT = f.size // 20
+    out = np.empty((nT, 32, 32), np.float32)
+    _check(_lib.kq_block_matrix(f.ctypes.data, nT, out.ctypes.data), "kq_block_matrix")
+    return out
+
+
+def kq_block_inverse(factors):
+    f = _host_f32(factors, "factors")
+    nT = f.size // 20
+    out = np.empty((nT, 32, 32), np.float32)
+    _check(_lib.kq_block_inverse(f.ctypes.data, nT, out.ctypes.data), "kq_block_inverse")
+    return out
+
+
+def kq_fold_weight(W, factors):
+    """W_out = W . T^-T so that (X T) W_out^T = X W^T."""
+    w = _host_f32(W, "W")
+    f = _host_f32(factors, "factors")
+    N, d = w.shape
+    out = np.empty_like(w)
+    _check(_lib.kq_fold_weight(w.ctypes.data, N, d, f.ctypes.data, f.size // 20, out.ctypes.data), "kq_fold_weight")
+    return out

@@ -1,0 +1,188 @@
+// extern "C" entry points of libkroquant.so: argument checks on the host, then
+// one kernel launch on the caller's stream.  See include/kroquant.h for the
+// contract of every function.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kroquant.h"
+#include "kq_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [p, p + n) and [r, r + m) overlap?
+bool overlap(const void *p, int64_t n, const void *r, int64_t m)
+{
+    const uintptr_t a0 = (uintptr_t)p, a1 = a0 + (uintptr_t)n;
+    const uintptr_t b0 = (uintptr_t)r, b1 = b0 + (uintptr_t)m;
+    return n > 0 && m > 0 && a0 < b1 && b0 < a1;
+}
+
+int check_md(int64_t M, int64_t d)
+{
+    if (M < 0 || d <= 0)
+        return KQ_ERR_ARG;
+    if (d % 32 != 0)
+        return KQ_ERR_SHAPE;
+    if (d > kq::kMaxD || (M > 0 && (M * (d / 32)) > kq::kMaxBlocksTotal))
+        return KQ_ERR_SHAPE;
+    return KQ_OK;
+}
+
+int check_sets(int64_t d, int64_t nT)
+{
+    if (nT != 1 && nT != d / 32)
+        return KQ_ERR_SHAPE;
+    return KQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
+
+// shared checks of the quantizing entry points (x is bf16 or fp32)
+int check_quant_io(const void *x, int64_t xbytes, const uint8_t *q, const uint8_t *s, int64_t M, int64_t d)
+{
+    if (!x || !q || !s)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t qbytes = M * (d / 2), sbytes = M * (d / 32);
+    if (overlap(x, xbytes, q, qbytes) || overlap(x, xbytes, s, sbytes) || overlap(q, qbytes, s, sbytes))
+        return KQ_ERR_OVERLAP;
+    return KQ_OK;
+}
+
+int check_param(const float *p, int64_t count, const void *x, int64_t xbytes, const void *o1, int64_t n1,
+                const void *o2, int64_t n2)
+{
+    if (!p)
+        return KQ_ERR_ARG;
+    if (!aligned(p, 4))
+        return KQ_ERR_ALIGN;
+    const int64_t pb = count * 4;
+    if (overlap(p, pb, o1, n1) || overlap(p, pb, o2, n2))
+        return KQ_ERR_OVERLAP;
+    (void)x;
+    (void)xbytes;
+    return KQ_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                   uint8_t *s, int variant, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (variant != KQ_VARIANT_AUTO && variant != KQ_VARIANT_MFMA && variant != KQ_VARIANT_BUTTERFLY)
+        return KQ_ERR_ARG;
+    if ((st = check_sets(d, nT)))
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    const int64_t xb = M * d * 2;
+    if ((st = check_quant_io(x, xb, q, s, M, d)))
+        return st;
+    if ((st = check_param(factors, nT * 20, x, xb, q, M * (d / 2), s, M * (d / 32))))
+        return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (variant == KQ_VARIANT_BUTTERFLY)
+        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, q, s, nullptr, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, q, s, nullptr, hs));
+}
+
+int kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                uint8_t *s, void *stream)
+{
+    return kq_quantize_ex(x, M, d, factors, nT, q, s, KQ_VARIANT_AUTO, stream);
+}
+
+int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                     int variant, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (variant != KQ_VARIANT_AUTO && variant != KQ_VARIANT_MFMA && variant != KQ_VARIANT_BUTTERFLY)
+        return KQ_ERR_ARG;
+    if ((st = check_sets(d, nT)))
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if (!x || !y)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t xb = M * d * 2, yb = M * d * 4;
+    if (overlap(x, xb, y, yb))
+        return KQ_ERR_OVERLAP;
+    if ((st = check_param(factors, nT * 20, x, xb, y, yb, nullptr, 0)))
+        return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (variant == KQ_VARIANT_BUTTERFLY)
+        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, nullptr, nullptr, y, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, nullptr, nullptr, y, hs));
+}
+
+int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    const int64_t xb = M * d * 2;
+    if ((st = check_quant_io(x, xb, q, s, M, d)))
+        return st;
+    if ((st = check_param(scale, d, x, xb, q, M * (d / 2), s, M * (d / 32))))
+        return st;
+    return hip_status(kq::launch_sq(x, M, d, scale, q, s, (hipStream_t)stream));
+}
+
+int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if ((st = check_quant_io(x, M * d * 4, q, s, M, d)))
+        return st;
+    return hip_status(kq::launch_mx_f32(x, M, d, q, s, (hipStream_t)stream));
+}
+
+const char *kq_status_string(int status)
+{
+    switch (status) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_ARG: return "invalid argument (null pointer, negative size or unknown variant)";
+    case KQ_ERR_SHAPE: return "invalid shape (d % 32 != 0, nT not in {1, d/32}, or too large)";
+    case KQ_ERR_ALIGN: return "misaligned pointer (x, q, y need 16 bytes; factors, scale 4 bytes)";
+    case KQ_ERR_SINGULAR: return "singular or non-finite 2x2 factor";
+    case KQ_ERR_HIP: return "HIP runtime error at launch";
+    case KQ_ERR_OVERLAP: return "an output buffer overlaps another buffer";
+    default: return "unknown status";
+    }
+}
+
+const char *kq_build_info(void)
+{
+    return "kroquant gfx950: default variant=mfma (v_mfma_f32_32x32x16_bf16, 3-term bf16 split of K), "
+           "butterfly=DPP quad stages; FP4 via v_cvt_scalef32_pk_fp4_f32";
+}
+
+// Tuning knobs for measurements (not part of the stable header).
+int kq_set_tuning(int key, int value)
+{
+    switch (key) {
+    case 0: kq::tuning().mfma_tiles_per_wave = value; return KQ_OK;
+    case 1: kq::tuning().bfly_rows_per_wave = value; return KQ_OK;
+    case 2: kq::tuning().stream_rows_per_wave = value; return KQ_OK;
+    default: return KQ_ERR_ARG;
+    }
+}
+
+} // extern "C"

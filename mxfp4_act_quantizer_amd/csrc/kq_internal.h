@@ -1,0 +1,29 @@
+// Internal launch interface between the C ABI (kq_capi.hip) and the kernels
+// (kq_kernels.hip).  Arguments are already validated when these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+// Launch tuning knobs (chosen on MI355X measurements; see the launch code).
+struct Tuning {
+    int mfma_tiles_per_wave;  // 0 = automatic
+    int bfly_rows_per_wave;   // 0 = automatic
+    int stream_rows_per_wave; // 0 = automatic
+};
+Tuning &tuning();
+
+hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                          uint8_t *s, float *y, hipStream_t stream);
+hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                               uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
+hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
+                     hipStream_t stream);
+hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream);
+
+// Largest row count / width the launchers accept (grid and 32-bit lane math).
+constexpr int64_t kMaxD = (int64_t)1 << 20;
+constexpr int64_t kMaxBlocksTotal = (int64_t)1 << 40;
+
+} // namespace kq

@@ -1,0 +1,106 @@
+"""GPU-vs-oracle comparison rules for the quantizer outputs.
+
+Tolerance on the transformed values: |y_gpu - y| <= 2e-6 * z elementwise,
+where y is the exact (float64) transformed value and z = sum_r |x_r| |K_rc|
+is its magnitude scale.  A bound relative to |y| alone cannot hold for any
+fp32 accumulation under cancellation; z >= |y| is the loosest sound reading
+that still catches a wrong factor, index or sign.
+
+Codes and scales are compared bit for bit, except where a value within that
+tolerance of the oracle's fp32 value could legitimately round the other way:
+  - an element is flagged when [|y32| - delta, |y32| + delta] / 2^E contains an
+    E2M1 rounding threshold (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), or when
+    |y32| <= delta (a value that close to zero may come out with either sign,
+    e.g. an exact cancellation computed as a tiny negative or an underflow to -0);
+  - a block (and every element in it) is flagged when the shared exponent of
+    amax - delta_blk and of amax + delta_blk differ;
+  with delta = 2e-6 * max(z, |y32|) and delta_blk its maximum over the block.
+Every mismatching code must be flagged, every mismatching scale byte must be
+on a flagged block; both counts are reported.
+"""
+import numpy as np
+
+TOL = 2e-6
+THRESHOLDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def unpack_codes(q):
+    q = np.asarray(q, np.uint8)
+    M = q.shape[0]
+    out = np.empty((M, q.shape[1] * 2), np.uint8)
+    out[:, 0::2] = q & 0xF
+    out[:, 1::2] = q >> 4
+    return out
+
+
+def shared_exponent(amax):
+    """E = clamp(floor(log2 amax) - 2, -127, 127), amax = 0 -> -127 (vectorised)."""
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(amax)  # amax = f 2^e, f in [0.5, 1)
+    E = (e - 1) - 2
+    E = np.where(amax == 0, -127, E)
+    return np.clip(E, -127, 127)
+
+
+def boundary_flags(z, y32, tol=TOL):
+    """Flags (elements [M, d], blocks [M, d/32]) where a tolerance-sized change
+    of the transformed value may change the code or the scale."""
+    M, d = y32.shape
+    nB = d // 32
+    a = np.abs(y32.astype(np.float64))
+    delta = tol * np.maximum(z, a)
+    ab = a.reshape(M, nB, 32)
+    db = delta.reshape(M, nB, 32)
+    amax = ab.max(axis=2)
+    dmax = db.max(axis=2)
+    E_lo = shared_exponent(np.maximum(amax - dmax, 0.0))
+    E_hi = shared_exponent(amax + dmax)
+    blk = E_lo != E_hi
+    E = shared_exponent(amax)  # the oracle's own exponent
+    scale = np.ldexp(1.0, -E)[:, :, None]
+    lo = (ab - db) * scale
+    hi = (ab + db) * scale
+    elem = np.zeros((M, nB, 32), bool)
+    for t in THRESHOLDS:
+        elem |= (lo <= t) & (t <= hi)
+    # within delta of zero: the computed value may carry either sign (code 0 vs 8)
+    elem |= ab <= db
+    elem |= blk[:, :, None]
+    return elem.reshape(M, d), blk
+
+
+def compare(q_gpu, s_gpu, q_ref, s_ref, elem_flag=None, blk_flag=None):
+    """Returns a dict of counts; 'ok' is True when every mismatch is flagged
+    (or, with no flags given, when there is no mismatch at all)."""
+    cg, cr = unpack_codes(q_gpu), unpack_codes(q_ref)
+    s_gpu = np.asarray(s_gpu, np.uint8)
+    s_ref = np.asarray(s_ref, np.uint8)
+    code_mis = cg != cr
+    scale_mis = s_gpu != s_ref
+    res = {
+        "elements": int(cg.size),
+        "blocks": int(s_ref.size),
+        "code_mismatch": int(code_mis.sum()),
+        "scale_mismatch": int(scale_mis.sum()),
+    }
+    if elem_flag is None:
+        res["flagged_elements"] = 0
+        res["flagged_blocks"] = 0
+        res["unflagged_code_mismatch"] = res["code_mismatch"]
+        res["unflagged_scale_mismatch"] = res["scale_mismatch"]
+    else:
+        res["flagged_elements"] = int(elem_flag.sum())
+        res["flagged_blocks"] = int(blk_flag.sum())
+        res["unflagged_code_mismatch"] = int((code_mis & ~elem_flag).sum())
+        res["unflagged_scale_mismatch"] = int((scale_mis & ~blk_flag).sum())
+    res["ok"] = res["unflagged_code_mismatch"] == 0 and res["unflagged_scale_mismatch"] == 0
+    return res
+
+
+def transform_error(y_gpu, y_ref, z):
+    """max |y_gpu - y| / z over elements with z > 0, and the count above TOL."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    err = np.abs(y_gpu - y_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(z > 0, err / z, np.where(err == 0, 0.0, np.inf))
+    return float(rel.max()) if rel.size else 0.0, int((rel > TOL).sum())

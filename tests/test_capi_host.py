@@ -1,0 +1,181 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every declared
+symbol, rejects bad arguments before touching the GPU, and its host helpers
+(T^-1, dense blocks, weight folding) agree with the oracle."""
+import os
+import re
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import mxfp4_act_quantizer_amd as K
+from synth import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kroquant.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kq_\w+|sq_\w+|mx_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11, names
+    L = K.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in kroquant.h but not exported"
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_library_is_the_in_tree_build():
+    assert os.path.dirname(K.LIB_PATH) == os.path.join(ROOT, "mxfp4_act_quantizer_amd")
+    assert "gfx950" in K.kq_build_info()
+
+
+def test_status_strings():
+    for st in range(7):
+        assert K.kq_status_string(st) != "unknown status"
+    assert K.kq_status_string(99) == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# argument checks: every one returns before any HIP call
+# ---------------------------------------------------------------------------
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def raw(name, *args):
+    return getattr(K.lib(), name)(*args)
+
+
+def test_kq_validation():
+    q, s, f, x = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    assert raw("kq_quantize", x, 4, 48, f, 1, q, s, None) == K.KQ_ERR_SHAPE  # d % 32
+    assert raw("kq_quantize", x, 4, 64, f, 3, q, s, None) == K.KQ_ERR_SHAPE  # nT
+    assert raw("kq_quantize", x, -1, 64, f, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", x, 4, 0, f, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", None, 4, 64, f, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", x, 4, 64, None, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", x, 4, 64, f, 1, None, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", x, 4, 64, f, 1, q, None, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize", x + 2, 4, 64, f, 1, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize", x, 4, 64, f, 1, q + 8, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize", x, 4, 64, f + 2, 1, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize", x, 4, 64, f, 1, x + 64, s, None) == K.KQ_ERR_OVERLAP  # q inside x
+    assert raw("kq_quantize", x, 4, 64, f, 1, q, q + 16, None) == K.KQ_ERR_OVERLAP  # s inside q
+    assert raw("kq_quantize", x, 4, 64, q + 32, 1, q, s, None) == K.KQ_ERR_OVERLAP  # factors inside q
+    assert raw("kq_quantize_ex", x, 4, 64, f, 1, q, s, 7, None) == K.KQ_ERR_ARG  # variant
+    assert raw("kq_quantize", x, 0, 64, f, 1, q, s, None) == K.KQ_OK  # empty: no launch
+    assert raw("kq_quantize", None, 0, 64, None, 1, None, None, None) == K.KQ_OK
+    assert raw("kq_quantize", x, 4, 64 << 20, f, 1, q, s, None) == K.KQ_ERR_SHAPE  # too wide
+
+
+def test_transform_and_sq_mx_validation():
+    y, f, x, sc = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    q, s = FAKE + (4 << 30), FAKE + (5 << 30)
+    assert raw("kq_transform_f32", x, 4, 64, f, 2, y + 4, 1, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_transform_f32", x, 4, 64, f, 5, y, 1, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_transform_f32", x, 4, 64, f, 2, x + 16, 1, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_transform_f32", x, 4, 64, f, 2, y, 9, None) == K.KQ_ERR_ARG
+    assert raw("sq_quantize", x, 4, 96, None, q, s, None) == K.KQ_ERR_ARG
+    assert raw("sq_quantize", x, 4, 96, sc + 1, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("sq_quantize", x, 4, 100, sc, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("sq_quantize", x, 0, 96, sc, q, s, None) == K.KQ_OK
+    assert raw("mx_quantize_f32", x + 8, 4, 64, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("mx_quantize_f32", x, 4, 64, x + 32, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("mx_quantize_f32", x, -2, 64, q, s, None) == K.KQ_ERR_ARG
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        K.kq_quantize(x, torch.zeros(20))
+
+
+# ---------------------------------------------------------------------------
+# host helpers against the oracle
+# ---------------------------------------------------------------------------
+def test_block_matrix_and_inverse_match_oracle(oracle_lib):
+    f = I.random_factors(4, 17)
+    Kd = K.kq_block_matrix(f)
+    Ki = K.kq_block_inverse(f)
+    for t in range(4):
+        Kref = oracle_lib.kron_block(f[t])
+        Kiref = oracle_lib.kron_block_inverse(f[t])
+        assert np.allclose(Kd[t], Kref, rtol=2 ** -23, atol=0)
+        assert np.allclose(Ki[t], Kiref, rtol=2 ** -22, atol=1e-7 * np.abs(Kiref).max())
+        cond = np.linalg.cond(Kref)
+        assert np.abs(Ki[t].astype(np.float64) @ Kref - np.eye(32)).max() < 1e-6 * cond
+
+
+def test_factor_inverse(oracle_lib):
+    f = I.random_factors(3, 18)
+    inv = K.kq_factor_inverse(f)
+    for t in range(3):
+        for k in range(5):
+            assert np.allclose(inv[t, k].astype(np.float64) @ f[t, k].astype(np.float64), np.eye(2), atol=1e-6)
+
+
+def test_singular_factor_reported():
+    f = I.identity_factors(2)
+    f[1, 3] = np.array([[1, 2], [2, 4]], np.float32)
+    with pytest.raises(K.KQError) as e:
+        K.kq_block_inverse(f)
+    assert e.value.status == K.KQ_ERR_SINGULAR
+    f[1, 3] = np.array([[np.nan, 0], [0, 1]], np.float32)
+    with pytest.raises(K.KQError):
+        K.kq_factor_inverse(f)
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_fold_weight_exact_invariance(oracle_lib, shared):
+    """(X T)(W_out)^T == X W^T exactly with integer unimodular factors."""
+    rng = np.random.default_rng(5)
+    M, d, N = 6, 160, 7
+    f = I.integer_unimodular_factors(1 if shared else d // 32, 6)
+    x_int = rng.integers(-4, 5, (M, d)).astype(np.float32)
+    W = rng.integers(-4, 5, (N, d)).astype(np.float32)
+    Wf = K.kq_fold_weight(W, f)
+    y = oracle_lib.kq_transform(I.f32_to_bf16_bits(x_int), f, want_z=False)
+    assert np.array_equal(y @ Wf.astype(np.float64).T, x_int.astype(np.float64) @ W.astype(np.float64).T)
+
+
+def test_fold_weight_real_factors(oracle_lib):
+    rng = np.random.default_rng(7)
+    M, d, N = 5, 128, 9
+    f = I.random_factors(d // 32, 8)
+    x = I.make_activation("tiny", M=M, d=d)
+    W = rng.standard_normal((N, d)).astype(np.float32)
+    Wf = K.kq_fold_weight(W, f)
+    y = oracle_lib.kq_transform(x, f, want_z=False)
+    Tinv = scipy.linalg.block_diag(*[oracle_lib.kron_block_inverse(f[j]) for j in range(d // 32)])
+    ref = W.astype(np.float64) @ Tinv.T
+    assert np.allclose(Wf, ref, rtol=1e-6, atol=1e-6 * np.abs(ref).max())
+    lhs = y @ Wf.astype(np.float64).T
+    rhs = I.bf16_bits_to_f32(x).astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(lhs, rhs, rtol=0, atol=1e-4 * np.abs(rhs).max())
+
+
+def test_fold_weight_in_place():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((3, 64)).astype(np.float32)
+    f = I.random_factors(2, 10)
+    ref = K.kq_fold_weight(W, f)
+    L = K.lib()
+    Wc = W.copy()
+    fc = np.ascontiguousarray(f)
+    assert L.kq_fold_weight(Wc.ctypes.data, 3, 64, fc.ctypes.data, 2, Wc.ctypes.data) == 0
+    assert np.array_equal(Wc, ref)
+
+
+def test_fold_weight_shape_errors():
+    L = K.lib()
+    W = np.zeros((2, 64), np.float32)
+    f = np.ascontiguousarray(I.identity_factors(3))
+    assert L.kq_fold_weight(W.ctypes.data, 2, 64, f.ctypes.data, 3, W.ctypes.data) == K.KQ_ERR_SHAPE
+    assert L.kq_fold_weight(W.ctypes.data, 2, 60, f.ctypes.data, 1, W.ctypes.data) == K.KQ_ERR_SHAPE
+    assert L.kq_fold_weight(None, 2, 64, f.ctypes.data, 1, W.ctypes.data) == K.KQ_ERR_ARG

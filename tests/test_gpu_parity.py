@@ -1,0 +1,309 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Every case prints its name, shape and seed before it touches the GPU.
+Bars (see tests/parity.py for the exact rules):
+  - kq_transform_f32 values within 2e-6 * z of the exact transform;
+  - kq_quantize codes/scales bit-exact except tolerance-boundary elements;
+  - sq_quantize, mx_quantize_f32 and kq_quantize with identity factors fully
+    bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from synth import inputs as I
+from tests import parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {"mfma": 1, "butterfly": 2}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; none is visible")
+
+
+@pytest.fixture(scope="module")
+def K():
+    _need_gpu()
+    import mxfp4_act_quantizer_amd as K
+    return K
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(x_bits):
+    return torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def run_kq(K, x_bits, f, variant):
+    x = dev_bf16(x_bits)
+    q, s = K.kq_quantize(x, dev_f32(f), variant=variant)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def check_kq(K, name, x_bits, f, variant, exact=False):
+    M, d = x_bits.shape
+    say(f"[kq {name}] M={M} d={d} nT={f.shape[0]} variant={variant}")
+    qg, sg = run_kq(K, x_bits, f, variant)
+    qr, sr, y32 = O.kq_quantize(x_bits, f, want_y32=True)
+    if exact:
+        res = P.compare(qg, sg, qr, sr)
+    else:
+        _, z = O.kq_transform(x_bits, f)
+        ef, bf = P.boundary_flags(z, y32)
+        res = P.compare(qg, sg, qr, sr, ef, bf)
+    say(f"    {res}")
+    assert res["ok"], res
+    return res
+
+
+# ---------------------------------------------------------------------------
+# transformed values
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+@pytest.mark.parametrize("case", ["tiny_shared", "per_block_ragged", "student_t", "hadamard", "lu_factors"])
+def test_transform_values_within_tolerance(K, variant, case):
+    if case == "tiny_shared":
+        x = I.make_activation("tiny")
+        f = I.make_factors("tiny")
+    elif case == "per_block_ragged":
+        x = I.make_activation("dit_1152", M=97)
+        f = I.make_factors("dit_1152")
+    elif case == "student_t":
+        x = I.make_activation("mid_2240", M=45)
+        f = I.make_factors("mid_2240")
+    elif case == "hadamard":
+        x = I.make_activation("sweep_4096", M=33, d=1024)
+        f = I.hadamard_factors(1)
+    else:
+        rng = np.random.default_rng(8)
+        f = np.empty((3, 5, 2, 2), np.float32)
+        for t in range(3):
+            for k in range(5):
+                a, b, c = rng.uniform(0.5, 1.5), rng.uniform(-1, 1), rng.uniform(-1, 1)
+                f[t, k] = (np.array([[1, 0], [c, 1]]) @ np.array([[a, b], [0, -1 / a]])).astype(np.float32)
+        x = I.make_activation("tiny", M=40, d=96)
+    M, d = x.shape
+    say(f"[transform {case}] M={M} d={d} nT={f.shape[0]} variant={variant}")
+    y = K.kq_transform_f32(dev_bf16(x), dev_f32(f), variant=VARIANTS[variant])
+    torch.cuda.synchronize()
+    yr, z = O.kq_transform(x, f)
+    worst, nbad = P.transform_error(y.cpu().numpy(), yr, z)
+    say(f"    max |y_gpu - y| / z = {worst:.3e}, elements above 2e-6: {nbad}")
+    assert nbad == 0
+
+
+# ---------------------------------------------------------------------------
+# quantized outputs, oracle-sized cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kq_tiny_config(K, variant):
+    check_kq(K, "tiny", I.make_activation("tiny"), I.make_factors("tiny"), VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+@pytest.mark.parametrize("name,M", [("dit_1152", 130), ("dit_4608", 33), ("mid_2240", 70), ("mid_8960", 9),
+                                    ("dbl_3072", 72), ("sweep_4096", 21)])
+def test_kq_per_block_configs_small_rows(K, variant, name, M):
+    x = I.make_activation(name, M=M)
+    f = I.make_factors(name)
+    check_kq(K, name, x, f, VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+@pytest.mark.parametrize("M,d", [(1, 32), (1, 64), (31, 96), (32, 64), (33, 160), (65, 2240), (257, 32)])
+def test_kq_ragged_shapes(K, variant, M, d):
+    x = I.make_activation("dit_1152", M=M, d=d, seed=M * 7 + d)
+    for shared in (True, False):
+        f = I.random_factors(1 if shared else d // 32, M + d)
+        check_kq(K, f"ragged shared={shared}", x, f, VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kq_identity_is_plain_mxfp4_bit_exact(K, variant):
+    x, _, sp = I.act_sweep_special(48, 1536, 5151, special_frac=0.02)
+    assert len(sp) > 0
+    # a block of -0 and tiny negatives: sign handling must not depend on op order
+    x[0, :32] = I.f32_to_bf16_bits(-np.zeros(32, np.float32))
+    x[1, 32:64] = I.f32_to_bf16_bits(np.full(32, -1e-40, np.float32))
+    for nT in (1, 1536 // 32):
+        check_kq(K, f"identity nT={nT}", x, I.identity_factors(nT), VARIANTS[variant], exact=True)
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kq_hadamard(K, variant):
+    x = I.make_activation("sweep_4096", M=40, d=2048)
+    check_kq(K, "hadamard", x, I.hadamard_factors(1), VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kq_nonfinite_blocks(K, variant):
+    x = I.make_activation("tiny", M=8, d=256)
+    xf = I.bf16_bits_to_f32(x).copy()
+    xf[0, 3] = np.nan
+    xf[2, 40] = np.inf
+    xf[3, 100] = -np.inf
+    x = I.f32_to_bf16_bits(xf)
+    qr, sr = O.kq_quantize(x, I.random_factors(8, 3))
+    assert sr[0, 0] == 0xFF and sr[2, 1] == 0xFF and sr[3, 3] == 0xFF
+    check_kq(K, "nonfinite", x, I.random_factors(8, 3), VARIANTS[variant])
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_kq_deterministic_and_no_stray_writes(K, variant):
+    M, d = 77, 1152
+    x = I.make_activation("dit_1152", M=M)
+    f = I.make_factors("dit_1152")
+    xd, fd = dev_bf16(x), dev_f32(f)
+    guard = 4096
+    qbuf = torch.full((M * d // 2 + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((M * d // 32 + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    q = qbuf[guard:guard + M * d // 2].view(M, d // 2)
+    s = sbuf[guard:guard + M * d // 32].view(M, d // 32)
+    say(f"[canary] M={M} d={d} variant={variant}")
+    K.kq_quantize(xd, fd, q, s, variant=VARIANTS[variant])
+    torch.cuda.synchronize()
+    q1, s1 = q.cpu().numpy().copy(), s.cpu().numpy().copy()
+    K.kq_quantize(xd, fd, q, s, variant=VARIANTS[variant])
+    torch.cuda.synchronize()
+    assert np.array_equal(q1, q.cpu().numpy()) and np.array_equal(s1, s.cpu().numpy())
+    qb, sb = qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (qb[:guard] == 0xA5).all() and (qb[-guard:] == 0xA5).all()
+    assert (sb[:guard] == 0x5A).all() and (sb[-guard:] == 0x5A).all()
+
+
+def test_kq_variants_agree_off_boundary(K):
+    x = I.make_activation("dbl_3072", M=64)
+    f = I.make_factors("dbl_3072")
+    qa, sa = run_kq(K, x, f, 1)
+    qb, sb = run_kq(K, x, f, 2)
+    _, z = O.kq_transform(x, f)
+    _, _, y32 = O.kq_quantize(x, f, want_y32=True)
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(qa, sa, qb, sb, ef, bf)
+    say(f"[mfma vs butterfly] {res}")
+    assert res["ok"]
+
+
+def test_kq_empty_is_noop(K):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s = K.kq_quantize(x, dev_f32(I.identity_factors(1)))
+    assert q.shape == (0, 32) and s.shape == (0, 2)
+
+
+def test_kq_misaligned_rejected(K):
+    x = torch.zeros((4 * 64 + 8,), dtype=torch.bfloat16, device="cuda")
+    xv = x[1:1 + 4 * 64].view(4, 64)  # 2-byte offset
+    with pytest.raises(K.KQError) as e:
+        K.kq_quantize(xv, dev_f32(I.identity_factors(1)))
+    assert e.value.status == K.KQ_ERR_ALIGN
+
+
+# ---------------------------------------------------------------------------
+# SmoothQuant and fp32 MX: fully bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,M", [("tiny", 256), ("dit_4608", 41), ("mid_2240", 33), ("dbl_12288", 17),
+                                    ("sweep_4096", 19)])
+def test_sq_bit_exact(K, name, M):
+    x = I.make_activation(name, M=M)
+    scale = I.smoothquant_scale(x)
+    M, d = x.shape
+    say(f"[sq {name}] M={M} d={d}")
+    q, s = K.sq_quantize(dev_bf16(x), dev_f32(scale))
+    torch.cuda.synchronize()
+    qr, sr = O.sq_quantize(x, scale)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+    say(f"    {res}")
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0
+
+
+def test_sq_ragged_and_odd_scales(K):
+    rng = np.random.default_rng(12)
+    for M, d in [(1, 32), (5, 96), (37, 2240), (3, 544)]:
+        x = I.make_activation("mid_2240", M=M, d=d, seed=M + d)
+        scale = np.exp(rng.uniform(-12, 12, d)).astype(np.float32)
+        scale[:3] = [1e-30, 3e30, 1.0]
+        say(f"[sq ragged] M={M} d={d}")
+        q, s = K.sq_quantize(dev_bf16(x), dev_f32(scale))
+        torch.cuda.synchronize()
+        qr, sr = O.sq_quantize(x, scale)
+        res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+        assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0, res
+
+
+def _special_f32_matrix():
+    rng = np.random.default_rng(99)
+    rows = []
+    grid = np.array([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 7, 7.99], np.float32)
+    for E in (-127, -126, -100, -3, 0, 5, 100, 125):
+        v = np.resize(grid, 32).astype(np.float32) * np.float32(2.0 ** E if E > -126 else 1.0)
+        if E <= -126:
+            v = np.ldexp(np.resize(grid, 32).astype(np.float64), E).astype(np.float32)
+        v[1::3] *= -1
+        rows.append(v)
+    rows.append(np.full(32, -0.0, np.float32))
+    rows.append(np.ldexp(rng.standard_normal(32), -140).astype(np.float32))  # fp32 subnormals
+    rows.append(np.float32(3.4028235e38) * np.sign(rng.standard_normal(32)).astype(np.float32))
+    rows.append((rng.standard_normal(32) * 1e-3).astype(np.float32))
+    nf = rng.standard_normal(32).astype(np.float32)
+    nf[5] = np.nan
+    rows.append(nf)
+    inf = rng.standard_normal(32).astype(np.float32)
+    inf[30] = -np.inf
+    rows.append(inf)
+    m = np.concatenate(rows).reshape(-1, 64)  # 2 blocks per row
+    return m
+
+
+def test_mx_f32_bit_exact_specials(K):
+    x = _special_f32_matrix()
+    M, d = x.shape
+    say(f"[mx f32 specials] M={M} d={d}")
+    q, s = K.mx_quantize_f32(dev_f32(x))
+    torch.cuda.synchronize()
+    qr, sr = O.mx_quantize_f32(x)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+    say(f"    {res}")
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0
+
+
+@pytest.mark.parametrize("M,d", [(256, 1152), (67, 2240), (3, 12288)])
+def test_mx_f32_bit_exact_random(K, M, d):
+    rng = np.random.default_rng(M + d)
+    x = (rng.standard_normal((M, d)) * np.exp(rng.uniform(-30, 30, (M, 1)))).astype(np.float32)
+    say(f"[mx f32] M={M} d={d}")
+    q, s = K.mx_quantize_f32(dev_f32(x))
+    torch.cuda.synchronize()
+    qr, sr = O.mx_quantize_f32(x)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0, res
+
+
+def test_mx_f32_exhaustive_bf16_patterns(K):
+    # every bf16 bit pattern (as fp32) once, in blocks with controlled maxima
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    fin = vals[np.isfinite(vals)]
+    rng = np.random.default_rng(4)
+    fin = fin[rng.permutation(fin.size)]
+    n = (fin.size // 1024) * 1024
+    x = fin[:n].reshape(-1, 1024)
+    say(f"[mx f32 all bf16 patterns] M={x.shape[0]} d=1024")
+    q, s = K.mx_quantize_f32(dev_f32(x))
+    torch.cuda.synchronize()
+    qr, sr = O.mx_quantize_f32(x)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0, res

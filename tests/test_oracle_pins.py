@@ -263,7 +263,6 @@ def test_sq_rounds_once_per_step(oracle_lib):
 
 
 def test_shape_rules(oracle_lib):
-    import ctypes
     L = oracle_lib.lib()
     x = np.zeros((2, 64), np.uint16)
     f = I.identity_factors(2)
@@ -276,4 +275,3 @@ def test_shape_rules(oracle_lib):
     assert L.oracle_kq_quantize(P(x), 2, 64, P(f), 3, P(q), P(s), None) == 2  # nT not in {1, d/32}
     assert L.oracle_kq_quantize(P(x), -1, 64, P(f), 1, P(q), P(s), None) == 1
     assert L.oracle_kq_quantize(P(x), 0, 64, P(f), 1, P(q), P(s), None) == 0  # empty is fine
-    del ctypes
