@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the KroQuant online quantizer on one MI355X.
+
+One step = the quantizer pass over one CFG-doubled DiT batch: both activation
+matrices of the DiT configuration (M = 8192 tokens, d = 1152 with 36 factor
+sets and d = 4608 with 144 factor sets, bf16, synthetic: per-token lognormal
+rows, 1% outlier channels x50), each through kq_quantize (bf16 -> per-block
+Kronecker transform -> MXFP4 codes + E8M0 scales).
+
+  value     = algorithmic bytes of the step / step time  (GB/s)
+              algorithmic bytes = 2.53125 B per element (2 read, 0.5 + 1/32 written)
+  roofline  = the quantizer kernel's average launch against the 8 TB/s HBM peak,
+              timed with HIP events on the launch stream
+  cpu_baseline = the CPU oracle on a bounded sample of the same workload
+
+Inputs and outputs rotate over enough buffer sets (>= 1 GB per cycle) that
+every launch reads from HBM rather than the 256 MB last-level cache.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantizer GB/s (bf16→MXFP4+E8M0) and % HBM peak, KroQuant vs SmoothQuant"
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
+ROTATE_BYTES = 1 << 30
+WORKLOAD = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608)]
+KERNEL_SYMBOL = "kq_mfma_kernel<true>"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 mfma, 2 butterfly")
+    ap.add_argument("--no-extras", action="store_true", help="skip the SmoothQuant / butterfly comparison legs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of each matrix in the CPU sample (0 = 32 per host thread, about 15 s)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kq_kernels.hip", "kq_capi.hip", "kq_internal.h"):
+        with open(os.path.join(ROOT, "mxfp4_act_quantizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic_kq_mfma_dit.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def make_inputs():
+    from synth import inputs as I
+    mats = []
+    for name, M, d in WORKLOAD:
+        x = I.make_activation(name)
+        f = I.make_factors(name)
+        scale = I.smoothquant_scale(x)
+        assert x.shape == (M, d)
+        mats.append((name, x, f, scale))
+    return mats
+
+
+def cpu_baseline(mats, rows):
+    """The oracle, as it stands, on the first `rows` rows of each matrix, spread
+    over host threads by row ranges (ctypes releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as O
+    O.lib()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    jobs = []
+    for _, x, f, _ in mats:
+        xs = x[:rows]
+        chunk = max(1, (rows + threads - 1) // threads)
+        for r0 in range(0, rows, chunk):
+            jobs.append((np.ascontiguousarray(xs[r0:r0 + chunk]), f))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda a: O.kq_quantize(a[0], a[1]), jobs))
+    dt = time.perf_counter() - t0
+    elems = sum(rows * x.shape[1] for _, x, _, _ in mats)
+    return {
+        "value": round(elems * BYTES_PER_ELEM / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {rows} of 8192 rows of each DiT matrix (d=1152 and d=4608, per-block factor sets); "
+                  f"{elems} elements in {dt:.1f} s, same byte formula as the GPU value",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
+              f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mxfp4_act_quantizer_amd as K
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    mats = make_inputs()
+
+    # ---- device buffers, rotated so one cycle touches >= 1 GB
+    step_bytes = sum(x.size * BYTES_PER_ELEM for _, x, _, _ in mats)
+    nsets = max(2, int(np.ceil(ROTATE_BYTES / step_bytes)))
+    sets = []
+    for _ in range(nsets):
+        one = []
+        for name, x, f, scale in mats:
+            M, d = x.shape
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            one.append(dict(x=xd, f=torch.from_numpy(f).to(dev), scale=torch.from_numpy(scale).to(dev),
+                            q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
+                            s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
+        sets.append(one)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step_kq(i, variant, evs=None):
+        for k, b in enumerate(sets[i % nsets]):
+            if evs is not None:
+                evs[k][0].record(stream)
+            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=stream, variant=variant)
+            if evs is not None:
+                evs[k][1].record(stream)
+
+    def step_sq(i, evs=None):
+        for k, b in enumerate(sets[i % nsets]):
+            if evs is not None:
+                evs[k][0].record(stream)
+            K.sq_quantize(b["x"], b["scale"], b["q"], b["s"], stream=stream)
+            if evs is not None:
+                evs[k][1].record(stream)
+
+    def timed(step_fn, steps, warmup):
+        for i in range(warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in mats] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step_fn(i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_ms = [[evs[i][k][0].elapsed_time(evs[i][k][1]) for i in range(steps)] for k in range(len(mats))]
+        return wall, launch_ms
+
+    variant = args.variant
+    wall, launch_ms = timed(lambda i, e=None: step_kq(i, variant, e), args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    # roofline of the quantizer kernel: all its launches in the timed region
+    launch_bytes = [x.size * BYTES_PER_ELEM for _, x, _, _ in mats]
+    tot_dur = sum(sum(v) for v in launch_ms) / 1e3
+    n_launch = sum(len(v) for v in launch_ms)
+    achieved = sum(launch_bytes[k] * len(launch_ms[k]) for k in range(len(mats))) / tot_dur / 1e9
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    per_shape = {}
+    for k, (name, x, _, _) in enumerate(mats):
+        avg = float(np.mean(launch_ms[k]))
+        per_shape[name] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(launch_ms[k])) * 1e3, 2),
+                           "GB/s": round(launch_bytes[k] / (avg / 1e3) / 1e9, 1),
+                           "rows/s": round(x.shape[0] / (avg / 1e3), 1)}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": KERNEL_SYMBOL if variant in (0, 1) else "stream_kernel<2>",
+                "avg_launch_us": round(tot_dur / n_launch * 1e6, 2), "launches": n_launch,
+                "algorithmic_bytes_per_launch": round(sum(launch_bytes) / len(launch_bytes)),
+                "per_shape": per_shape}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "DiT CFG batch: 2x4096 tokens, d=1152 (36 factor sets) + d=4608 (144 factor sets), "
+                               "bf16 in, MXFP4 + E8M0 out, per-block Kronecker transforms",
+                   "M": 8192, "d": [1152, 4608], "nT": [36, 144], "variant": ["auto", "mfma", "butterfly"][variant],
+                   "rows_per_step": 2 * 8192, "rotating_sets": nsets, "accumulate": "fp32",
+                   "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
+                   "rows_per_s": round(2 * 8192 / (wall / args.steps), 1),
+                   "kernel_source_hash": src_hash},
+        "roofline": roofline,
+    }
+
+    if not args.no_extras:
+        sq_wall, sq_ms = timed(lambda i, e=None: step_sq(i, e), args.steps, args.warmup)
+        sq_value = step_bytes / (sq_wall / args.steps) / 1e9
+        other = 2 if variant in (0, 1) else 1
+        bf_wall, _ = timed(lambda i, e=None: step_kq(i, other, e), args.steps, args.warmup)
+        out["comparison"] = {
+            "smoothquant_GB/s": round(sq_value, 1),
+            "smoothquant_hbm_pct": round(100 * sq_value / HBM_PEAK_GBS, 2),
+            "kroquant_over_smoothquant_speed": round(sq_wall / wall, 4),
+            ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (bf_wall / args.steps) / 1e9, 1),
+        }
+
+    if not args.no_cpu:
+        rows = args.cpu_rows or min(8192, 32 * max(1, min(16, os.cpu_count() or 1)))
+        out["cpu_baseline"] = cpu_baseline(mats, rows)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

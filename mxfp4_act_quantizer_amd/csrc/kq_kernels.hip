@@ -77,6 +77,16 @@ __device__ __forceinline__ unsigned cvt8(float v0, float v1, float v2, float v3,
     return w;
 }
 
+// Raw buffer resources for the outputs.  Stores whose offset is at or past
+// num_records are dropped by the hardware range check, which masks lanes
+// (tail rows, a missing block) without a branch in the hot loop.
+constexpr unsigned kBufWord3 = 0x00020000u; // gfx9-family raw buffer descriptor flags
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_buffer(void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufWord3);
+}
+
 __device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -93,13 +103,9 @@ __device__ __forceinline__ float dpp_xor2(float v)
 // ---------------------------------------------------------------------------
 // MFMA variant
 // ---------------------------------------------------------------------------
-constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kWavesKQ = 8; // waves per workgroup of the MFMA kernel (one block each)
+constexpr unsigned kXcds = 8; // MI355X: 8 accelerator dies, workgroups dealt round-robin
 constexpr int kTileT = 32; // tokens per wave tile
-
-// A operand table of one workgroup: [block of the pair][split lo/mid/hi][mfma j][lane][8 bf16]
-struct __align__(16) KTable {
-    unsigned short v[2][3][2][64][8];
-};
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ unsigned short bf16_rne(float f)
@@ -109,181 +115,241 @@ __device__ __forceinline__ unsigned short bf16_rne(float f)
 }
 __device__ __forceinline__ float bf16_val(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
+// MFMA A operands of one wave for its block, built in registers.
 // The 32x32 block enters the MFMA as A = K^T with rows permuted (output
 // channel order) so that accumulator v of a lane in half h is channel 16h+v:
 // A row i holds output channel pi(i) = 16*((i>>2)&1) + 4*(i>>3) + (i&3).
-// A lane l of MFMA j holds A[i = l%32][k = 8*(l/32) + e] = K[16j + 8h + e][pi(i)].
-__device__ __forceinline__ void build_ktable(KTable &T, const float *__restrict__ factors, int per_block, int j0,
-                                             int nB)
+// Lane l of MFMA j holds A[i = l%32][k = 8h + e] = K[16j + 8h + e][pi(i)]
+// (h = l/32), i.e. input index bits (r4 r3 r2 r1 r0) = (j, h, e2, e1, e0).
+// Each entry K = A1[r4][c4] A2[r3][c3] A3[r2][c2] A4[r1][c1] A5[r0][c0] is
+// formed in fp32 and split exactly into hi + mid + lo bf16 terms (each step
+// keeps the next 8 significant bits, so the third remainder fits bf16).
+__device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lane)
 {
-    const int tid = threadIdx.x;
-    const int blk = tid >> 7;
-    const int j = (tid >> 6) & 1;
-    const int l = tid & 63;
-    const int hh = l >> 5;
-    const int i = l & 31;
+    const int h = lane >> 5;
+    const int i = lane & 31;
     const int c = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
-    const int jb = j0 + blk;
-    const int set = per_block ? (jb < nB ? jb : 0) : 0;
-    const float *F = factors + (int64_t)set * 20; // F[k*4 + r*2 + col]
     const int c4 = (c >> 4) & 1, c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
-    // K[r][c] = A1[r4][c4] A2[r3][c3] A3[r2][c2] A4[r1][c1] A5[r0][c0] with r4 = j, r3 = hh, (r2 r1 r0) = e
-    const float p = F[0 + j * 2 + c4] * F[4 + hh * 2 + c3];
+    // F[k*4 + r*2 + col] is entry (r, col) of factor A_{k+1}
+    const float a2 = F[4 + h * 2 + c3];
     const float a3_0 = F[8 + c2], a3_1 = F[10 + c2];
     const float a4_0 = F[12 + c1], a4_1 = F[14 + c1];
     const float a5_0 = F[16 + c0], a5_1 = F[18 + c0];
-    unsigned short hi[8], mid[8], lo[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float k = ((p * ((e & 4) ? a3_1 : a3_0)) * ((e & 2) ? a4_1 : a4_0)) * ((e & 1) ? a5_1 : a5_0);
-        // exact split: k == hi + mid + lo (each step drops 8 significant bits)
-        const unsigned short bh = bf16_rne(k);
-        const float r1 = k - bf16_val(bh);
-        const unsigned short bm = bf16_rne(r1);
-        const float r2 = r1 - bf16_val(bm);
-        hi[e] = bh;
-        mid[e] = bm;
-        lo[e] = bf16_rne(r2);
-    }
+    for (int j = 0; j < 2; ++j) {
+        const float p = F[0 + j * 2 + c4] * a2;
+        bf16x8 hi, mid, lo;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        T.v[blk][0][j][l][e] = lo[e];
-        T.v[blk][1][j][l][e] = mid[e];
-        T.v[blk][2][j][l][e] = hi[e];
+        for (int e = 0; e < 8; ++e) {
+            const float k = ((p * ((e & 4) ? a3_1 : a3_0)) * ((e & 2) ? a4_1 : a4_0)) * ((e & 1) ? a5_1 : a5_0);
+            const unsigned short bh = bf16_rne(k);
+            const float r1 = k - bf16_val(bh);
+            const unsigned short bm = bf16_rne(r1);
+            const float r2 = r1 - bf16_val(bm);
+            hi[e] = __builtin_bit_cast(__bf16, bh);
+            mid[e] = __builtin_bit_cast(__bf16, bm);
+            lo[e] = __builtin_bit_cast(__bf16, bf16_rne(r2));
+        }
+        A[0][j] = lo;
+        A[1][j] = mid;
+        A[2][j] = hi;
     }
 }
 
-__device__ __forceinline__ void load_tile(bf16x8 (&xv)[2][2], const uint16_t *__restrict__ x, int64_t M, int d,
-                                          int j0, bool has1, int64_t t, int h)
+// ---- workgroup tile of the MFMA variant ----------------------------------
+// A workgroup owns a strip of eight adjacent blocks (256 channels, 512 bytes
+// of a token row) and walks 32-token tiles.  x arrives with contiguous loads
+// (16 bytes per lane, two 512-byte row strips per wave instruction), goes
+// through a padded LDS tile, and is read back in the MFMA operand layout.
+constexpr int kStrip = kWavesKQ * 64;  // bytes of x per token row and workgroup
+constexpr int kXRow = kStrip + 16;     // padded LDS row: 16 consecutive tokens hit distinct banks
+constexpr int kQRow = kWavesKQ * 16 + 16; // padded LDS row of staged codes (128 bytes + pad)
+
+struct __align__(16) WgStage {
+    unsigned char x[2][kTileT][kXRow];      // x tile, double-buffered by tile parity
+    unsigned char q[2][kTileT][kQRow];      // staged codes
+    unsigned char s[2][kTileT][kWavesKQ];   // staged scale bytes
+};
+
+// Raw x of one tile for one wave: rows 4w + 2k + (lane / 32), 16-byte chunk lane % 32.
+struct XIn {
+    u32x4 v[2];
+};
+
+// Load this wave's share of a tile.  Chunks of blocks past the row end read
+// the row start instead, rows past M read row M-1: every load is in bounds,
+// and neither result is ever stored.
+__device__ __forceinline__ void load_x(XIn &in, const uint16_t *__restrict__ x, int64_t M, int d, int bg, int nB,
+                                       int64_t t0, int wave, int lane)
 {
-    const bf16x8 z = {};
-    xv[0][0] = z;
-    xv[0][1] = z;
-    xv[1][0] = z;
-    xv[1][1] = z;
-    if (t < M) {
-        const uint16_t *row = x + t * d + j0 * 32 + 8 * h;
-        xv[0][0] = *(const bf16x8 *)(row);
-        xv[0][1] = *(const bf16x8 *)(row + 16);
-        if (has1) {
-            xv[1][0] = *(const bf16x8 *)(row + 32);
-            xv[1][1] = *(const bf16x8 *)(row + 48);
+    const int chunk = lane & 31;
+    const int blk = bg * kWavesKQ + (chunk >> 2);
+    const int col = (blk < nB ? bg * (kStrip / 2) + chunk * 8 : 0); // element offset in the row
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        int64_t t = t0 + 4 * wave + 2 * k + (lane >> 5);
+        t = t < M ? t : M - 1;
+        in.v[k] = *(const u32x4 *)(x + t * d + col);
+    }
+}
+
+__device__ __forceinline__ void stage_x(WgStage &st, int par, const XIn &in, int wave, int lane)
+{
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        *(u32x4 *)&st.x[par][4 * wave + 2 * k + (lane >> 5)][(lane & 31) * 16] = in.v[k];
+}
+
+// Transform one tile on the matrix cores; quantize into the staging buffer
+// (or write y directly).  Lane l takes token l%32 and, for MFMA j, channels
+// 16j + 8h .. +7 of block `wave` of the strip (h = l/32).
+template <bool kQuant>
+__device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, int par, const bf16x8 (&A)[3][2],
+                                               int64_t t, int64_t M, int d, int jb, int h, int wave, int tl,
+                                               float *__restrict__ y)
+{
+    bf16x8 bv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        bv[j] = *(const bf16x8 *)&stc.x[par][tl][wave * 64 + 32 * j + 16 * h];
+    f32x16 acc = {};
+    // smallest terms first: lo, mid, hi
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][j], bv[j], acc, 0, 0, 0);
+    if constexpr (kQuant) {
+        float m = __builtin_fabsf(acc[0]);
+#pragma unroll
+        for (int v = 1; v < 16; ++v)
+            m = amax_step(m, acc[v]);
+        // the other 16 channels of the token sit in lane l^32
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        const unsigned b = e8m0_byte(m);
+        const float sc = scale_operand(b);
+        unsigned w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
+        unsigned w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
+        if (b == 0xFFu)
+            w0 = w1 = 0u;
+        // lane half h holds q bytes 8h..8h+7 of block `wave` of the strip
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        *(u32x2 *)&st.q[par][tl][wave * 16 + 8 * h] = u32x2{w0, w1};
+        if (h == 0)
+            st.s[par][tl][wave] = (unsigned char)b;
+    } else {
+        if (t < M) {
+            f32x4 *o = (f32x4 *)(y + t * d + jb * 32 + 16 * h);
+            o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+            o[2] = f32x4{acc[8], acc[9], acc[10], acc[11]};
+            o[3] = f32x4{acc[12], acc[13], acc[14], acc[15]};
         }
     }
 }
 
-// One workgroup: block pair (j0, j0+1) and a run of 32-token tiles; the four
-// waves interleave over the tiles.  Each wave loads its next tile before it
-// computes the current one.
-template <bool kQuant>
-__global__ __launch_bounds__(256) void kq_mfma_kernel(const uint16_t *__restrict__ x, int64_t M, int d,
-                                                      const float *__restrict__ factors, int per_block,
-                                                      uint8_t *__restrict__ q, uint8_t *__restrict__ s,
-                                                      float *__restrict__ y, int nP, int tiles_per_wave)
+// Store one staged tile: waves 0-3 write the codes (eight tokens each, eight
+// lanes x 16 bytes per token row: one contiguous 128-byte segment), waves 4-7
+// the scale bytes (eight consecutive bytes per token).  Rows past M fall
+// outside the workgroup's ranges; blocks past the row end set bit 31 of
+// their offsets, which the range check drops.
+__device__ __forceinline__ void store_tile(const WgStage &st, int par, int tr0, int bg, int nB, int d, int wave,
+                                           int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
 {
-    __shared__ KTable T;
+    const int c = lane & 7;
+    const int blk = bg * kWavesKQ + c;
+    const unsigned drop = (unsigned)(blk >= nB || tr0 < 0) << 31;
+    if (wave < 4) {
+        const int tt = wave * 8 + (lane >> 3);
+        const u32x4 v = *(const u32x4 *)&st.q[par][tt][c * 16];
+        __builtin_amdgcn_raw_buffer_store_b128(v, rq, (int)((unsigned)((tr0 + tt) * (d >> 1) + blk * 16) | drop), 0,
+                                               0);
+    } else {
+        const int tt = (wave - 4) * 8 + (lane >> 3);
+        __builtin_amdgcn_raw_buffer_store_b8(st.s[par][tt][c], rs, (int)((unsigned)((tr0 + tt) * nB + blk) | drop), 0,
+                                             0);
+    }
+}
+
+// One workgroup: a strip of eight blocks (one per wave for the transform) and
+// a run of 32-token tiles the eight waves walk together.  Per tile, in order:
+// stage the tile's x (loaded three tiles earlier) in LDS, issue the loads of
+// the tile three ahead, barrier, store the previous tile's staged codes,
+// transform this tile from LDS into the staging buffer.  One barrier per tile
+// orders all of it (the LDS buffers alternate by tile parity).  Loads past the
+// last tile re-read that tile (an L2 hit), so every load is unconditional.
+template <bool kQuant>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
+    const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg)
+{
+    __shared__ WgStage st;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int pair = (int)(blockIdx.x % (unsigned)nP);
-    const int64_t group = blockIdx.x / (unsigned)nP;
+    // Workgroups go round-robin to the 8 XCDs (blockIdx % 8).  All strips of
+    // one token group run on the same XCD, one after another, so partial
+    // lines written into the same q and s rows merge in that L2.
+    const unsigned xcd = blockIdx.x % kXcds;
+    const unsigned slot = blockIdx.x / kXcds;
+    const int bg = (int)(slot % (unsigned)nBG);
+    const int64_t group = (int64_t)(slot / (unsigned)nBG) * kXcds + xcd;
     const int nB = d >> 5;
-    const int j0 = 2 * pair;
-    const bool has1 = (j0 + 1) < nB;
+    const int64_t nTiles = (M + kTileT - 1) / kTileT;
+    const int64_t tile0 = group * tiles_per_wg;
+    if (tile0 >= nTiles)
+        return; // padding workgroup: uniform over the workgroup, before any barrier
+    const int jb_raw = bg * kWavesKQ + wave;
+    // waves past the row end take part in loads and barriers and transform block
+    // nB-1 (their results are never stored)
+    const int jb = jb_raw < nB ? jb_raw : nB - 1;
+    const int n = (int)((nTiles - tile0) < tiles_per_wg ? (nTiles - tile0) : tiles_per_wg);
     const int h = lane >> 5;
     const int tl = lane & 31;
-    const int64_t tile_base = group * (int64_t)(kWaves * tiles_per_wave) + wave;
+    const int64_t t_wg = tile0 * kTileT;
+    const int64_t rows_wg = (M - t_wg) < (int64_t)n * kTileT ? (M - t_wg) : (int64_t)n * kTileT;
+    // this workgroup's token rows [t_wg, t_wg + rows_wg) bound its output ranges
+    __amdgpu_buffer_rsrc_t rq = out_buffer(kQuant ? q + t_wg * (d >> 1) : nullptr, kQuant ? rows_wg * (d >> 1) : 0);
+    __amdgpu_buffer_rsrc_t rs = out_buffer(kQuant ? s + t_wg * nB : nullptr, kQuant ? rows_wg * nB : 0);
+    auto tbase = [&](int k) -> int64_t { return t_wg + (int64_t)(k < n ? k : n - 1) * kTileT; };
 
-    bf16x8 cur[2][2];
-    load_tile(cur, x, M, d, j0, has1, tile_base * kTileT + tl, h);
+    XIn b0, b1, b2, b3;
+    load_x(b0, x, M, d, bg, nB, tbase(0), wave, lane);
+    load_x(b1, x, M, d, bg, nB, tbase(1), wave, lane);
+    load_x(b2, x, M, d, bg, nB, tbase(2), wave, lane);
 
-    build_ktable(T, factors, per_block, j0, nB);
-    __syncthreads();
-    bf16x8 A[2][3][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                A[b][sp][j] = *(const bf16x8 *)&T.v[b][sp][j][lane][0];
+    bf16x8 A[3][2];
+    build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * 20, lane);
 
-    for (int it = 0; it < tiles_per_wave; ++it) {
-        const int64_t tile = tile_base + (int64_t)it * kWaves;
-        const int64_t t0 = tile * kTileT;
-        if (t0 >= M)
-            break;
-        bf16x8 nxt[2][2];
-        const bool more = (it + 1 < tiles_per_wave);
-        if (more)
-            load_tile(nxt, x, M, d, j0, has1, t0 + kWaves * kTileT + tl, h);
+#define KQ_STEP(cur, ld, k)                                                                                        \
+    {                                                                                                              \
+        const int kk = it + (k);                                                                                   \
+        stage_x(st, kk & 1, cur, wave, lane);                                                                      \
+        load_x(ld, x, M, d, bg, nB, tbase(kk + 3), wave, lane);                                                    \
+        __syncthreads();                                                                                           \
+        if (kQuant)                                                                                                \
+            store_tile(st, (kk - 1) & 1, (kk - 1) * kTileT, bg, nB, d, wave, lane, rq, rs);                        \
+        transform_tile<kQuant>(st, st, kk & 1, A, t_wg + (int64_t)kk * kTileT + tl, M, d, jb, h, wave, tl, y);     \
+    }
 
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][sp][j], cur[0][j], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][sp][j], cur[1][j], acc1, 0, 0, 0);
-            }
-
-        const int64_t t = t0 + tl;
-        const bool tok_ok = t < M;
-        if constexpr (kQuant) {
-            float m0 = __builtin_fabsf(acc0[0]), m1 = __builtin_fabsf(acc1[0]);
-#pragma unroll
-            for (int v = 1; v < 16; ++v) {
-                m0 = amax_step(m0, acc0[v]);
-                m1 = amax_step(m1, acc1[v]);
-            }
-            // the other 16 channels of the token sit in lane l^32
-            const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m0), false, false);
-            const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false, false);
-            m0 = vmax(__uint_as_float(r0[0]), __uint_as_float(r0[1]));
-            m1 = vmax(__uint_as_float(r1[0]), __uint_as_float(r1[1]));
-            const unsigned b0 = e8m0_byte(m0), b1 = e8m0_byte(m1);
-            const float sc0 = scale_operand(b0), sc1 = scale_operand(b1);
-            unsigned w00 = cvt8(acc0[0], acc0[1], acc0[2], acc0[3], acc0[4], acc0[5], acc0[6], acc0[7], sc0);
-            unsigned w01 = cvt8(acc0[8], acc0[9], acc0[10], acc0[11], acc0[12], acc0[13], acc0[14], acc0[15], sc0);
-            unsigned w10 = cvt8(acc1[0], acc1[1], acc1[2], acc1[3], acc1[4], acc1[5], acc1[6], acc1[7], sc1);
-            unsigned w11 = cvt8(acc1[8], acc1[9], acc1[10], acc1[11], acc1[12], acc1[13], acc1[14], acc1[15], sc1);
-            if (b0 == 0xFFu)
-                w00 = w01 = 0u;
-            if (b1 == 0xFFu)
-                w10 = w11 = 0u;
-            // lanes < 32 gather block j0 (own bytes 0-7, partner's 8-15);
-            // lanes >= 32 gather block j0+1 (partner's bytes 0-7, own 8-15)
-            const auto e0 = __builtin_amdgcn_permlane32_swap(w00, w10, false, false);
-            const auto e1 = __builtin_amdgcn_permlane32_swap(w01, w11, false, false);
-            if (tok_ok && (h == 0 || has1)) {
-                const int jb = j0 + h;
-                u32x4 out = {e0[0], e1[0], e0[1], e1[1]};
-                *(u32x4 *)(q + t * (d >> 1) + jb * 16) = out;
-                s[t * nB + jb] = (uint8_t)(h ? b1 : b0);
-            }
-        } else {
-            if (tok_ok) {
-                float *yr = y + t * d + j0 * 32 + 16 * h;
-                f32x4 *o0 = (f32x4 *)yr;
-                o0[0] = f32x4{acc0[0], acc0[1], acc0[2], acc0[3]};
-                o0[1] = f32x4{acc0[4], acc0[5], acc0[6], acc0[7]};
-                o0[2] = f32x4{acc0[8], acc0[9], acc0[10], acc0[11]};
-                o0[3] = f32x4{acc0[12], acc0[13], acc0[14], acc0[15]};
-                if (has1) {
-                    f32x4 *o1 = (f32x4 *)(yr + 32);
-                    o1[0] = f32x4{acc1[0], acc1[1], acc1[2], acc1[3]};
-                    o1[1] = f32x4{acc1[4], acc1[5], acc1[6], acc1[7]};
-                    o1[2] = f32x4{acc1[8], acc1[9], acc1[10], acc1[11]};
-                    o1[3] = f32x4{acc1[12], acc1[13], acc1[14], acc1[15]};
-                }
-            }
-        }
-        if (more) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    cur[b][j] = nxt[b][j];
-        }
+    int it = 0;
+    for (; it + 3 < n; it += 4) {
+        KQ_STEP(b0, b3, 0)
+        KQ_STEP(b1, b0, 1)
+        KQ_STEP(b2, b1, 2)
+        KQ_STEP(b3, b2, 3)
+    }
+    // at most three tiles left, already loaded in b0..b2 (their prefetches re-read the last tile)
+    if (it < n)
+        KQ_STEP(b0, b3, 0)
+    if (it + 1 < n)
+        KQ_STEP(b1, b3, 1)
+    if (it + 2 < n)
+        KQ_STEP(b2, b3, 2)
+#undef KQ_STEP
+    if (kQuant) {
+        __syncthreads();
+        store_tile(st, (n - 1) & 1, (n - 1) * kTileT, bg, nB, d, wave, lane, rq, rs);
     }
 }
 
@@ -338,26 +404,137 @@ __device__ __forceinline__ void bfly_inlane(float (&v)[8], const float (&A)[4])
     }
 }
 
+constexpr int kStreamU = 4; // rows per pipeline stage of the streaming kernels
+
+// Raw loads of U rows of one lane's 8 channels.  Rows past the end re-read the
+// last row of the wave's run (results not stored), so every load is in bounds.
+template <int kMode>
+struct RowsIn {
+    u32x4 v[kStreamU][kMode == kMXF32 ? 2 : 1];
+};
+
+template <int kMode>
+__device__ __forceinline__ void load_rows(RowsIn<kMode> &in, const void *__restrict__ xin, int64_t m, int64_t m1,
+                                          int d, int octc)
+{
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        const int64_t mm = (m + u < m1) ? m + u : m1 - 1;
+        if constexpr (kMode == kMXF32) {
+            const u32x4 *p = (const u32x4 *)((const float *)xin + mm * d + (int64_t)octc * 8);
+            in.v[u][0] = p[0];
+            in.v[u][1] = p[1];
+        } else {
+            in.v[u][0] = *(const u32x4 *)((const uint16_t *)xin + mm * d + (int64_t)octc * 8);
+        }
+    }
+}
+
+template <int kMode>
+__device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m, int64_t m0, int64_t m1, int d, int nB,
+                                             int oct, bool cok, int qp, const float (&r)[8], const Bfly &B,
+                                             __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
+                                             float *__restrict__ y)
+{
+#pragma unroll
+    for (int u = 0; u < kStreamU; ++u) {
+        float v[8];
+        if constexpr (kMode == kMXF32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = __uint_as_float(in.v[u][0][i]) + 0.0f; // -0 -> +0
+                v[4 + i] = __uint_as_float(in.v[u][1][i]) + 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16lo(in.v[u][0][i]);
+                v[2 * i + 1] = bf16hi(in.v[u][0][i]);
+            }
+        }
+        if constexpr (kMode == kSQ) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_fmaf(v[i], r[i], 0.0f); // one rounding; -0 -> +0
+        }
+        if constexpr (kMode == kBflyQ || kMode == kBflyT) {
+            // cross-lane stages first (index bits 4 and 3), then in-lane bits 2, 1, 0
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float other = dpp_xor2(v[i]);
+                v[i] = __builtin_fmaf(B.o1, other, B.s1 * v[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float other = dpp_xor1(v[i]);
+                v[i] = __builtin_fmaf(B.o2, other, B.s2 * v[i]);
+            }
+            bfly_inlane<4, false>(v, B.a3);
+            bfly_inlane<2, false>(v, B.a4);
+            bfly_inlane<1, true>(v, B.a5);
+        }
+        const int64_t mm = m + u;
+        if constexpr (kMode == kBflyT) {
+            if (mm < m1 && cok) {
+                f32x4 *o = (f32x4 *)(y + mm * d + (int64_t)oct * 8);
+                o[0] = f32x4{v[0], v[1], v[2], v[3]};
+                o[1] = f32x4{v[4], v[5], v[6], v[7]};
+            }
+        } else {
+            float am = __builtin_fabsf(v[0]);
+#pragma unroll
+            for (int i = 1; i < 8; ++i)
+                am = amax_step(am, v[i]);
+            am = vmax(am, dpp_xor1(am));
+            am = vmax(am, dpp_xor2(am));
+            const unsigned b = e8m0_byte(am);
+            const float sc = scale_operand(b);
+            unsigned w = cvt8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
+            if (b == 0xFFu)
+                w = 0u;
+            // rows past the run fall outside the wave's ranges; lanes past the row
+            // end (and three of the four lanes of a block for s) set bit 31 of their offset
+            const int mr = (int)(mm - m0);
+            const unsigned drop_q = (unsigned)(cok ? 0 : 1) << 31;
+            const unsigned drop_s = drop_q | ((unsigned)(qp != 0) << 31);
+            __builtin_amdgcn_raw_buffer_store_b32(w, rq, (int)((unsigned)(mr * (d >> 1) + oct * 4) | drop_q), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)((unsigned)(mr * nB + (oct >> 2)) | drop_s), 0, 0);
+        }
+    }
+}
+
 template <int kMode>
 __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xin, int64_t M, int d,
                                                      const float *__restrict__ aux, int per_block,
                                                      uint8_t *__restrict__ q, uint8_t *__restrict__ s,
                                                      float *__restrict__ y, int rows_per_wave, int nCT)
 {
-    constexpr int U = 4; // rows in flight per step
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int ct = (int)(gw % nCT);
-    const int64_t m0 = (gw / nCT) * rows_per_wave;
-    if (m0 >= M)
-        return;
+    // A workgroup covers four column tiles of one row group.  All column groups
+    // of a row group run on the same XCD back to back (blockIdx % 8 picks the
+    // XCD), so the partial lines of q and s rows merge in one L2.
+    const int nCG = (nCT + 3) / 4;
+    const unsigned xcd = blockIdx.x % kXcds;
+    const unsigned slot = blockIdx.x / kXcds;
+    const int cg = (int)(slot % (unsigned)nCG);
+    const int64_t rg = (int64_t)(slot / (unsigned)nCG) * kXcds + xcd;
+    const int ct = cg * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = rg * rows_per_wave;
+    if (m0 >= M || ct >= nCT)
+        return; // wave-uniform; this kernel has no barrier
     const int64_t m1 = (m0 + rows_per_wave < M) ? m0 + rows_per_wave : M;
     const int nOct = d >> 3;
     const int nB = d >> 5;
     const int oct = ct * 64 + lane;
     const bool cok = oct < nOct;
-    const int octc = cok ? oct : 0;
+    const int octc = cok ? oct : nOct - 1; // lanes past the row end re-read a valid chunk (not stored)
     const int qp = lane & 3;
+
+    RowsIn<kMode> bufA, bufB;
+    load_rows<kMode>(bufA, xin, m0, m1, d, octc);
+    const bool quant = (kMode != kBflyT);
+    __amdgpu_buffer_rsrc_t rq = out_buffer(quant ? q + m0 * (d >> 1) : nullptr, quant ? (m1 - m0) * (d >> 1) : 0);
+    __amdgpu_buffer_rsrc_t rs = out_buffer(quant ? s + m0 * nB : nullptr, quant ? (m1 - m0) * nB : 0);
 
     float r[8];
     Bfly B;
@@ -371,101 +548,20 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
         bfly_setup(B, aux + (int64_t)set * 20, qp);
     }
 
-    for (int64_t m = m0; m < m1; m += U) {
-        float v[U][8];
-        // ---- loads for U rows
-        if constexpr (kMode == kMXF32) {
-            const float *xf = (const float *)xin;
-            f32x4 raw[U][2];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                raw[u][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                raw[u][1] = raw[u][0];
-                if (m + u < m1 && cok) {
-                    const f32x4 *p = (const f32x4 *)(xf + (m + u) * d + (int64_t)oct * 8);
-                    raw[u][0] = p[0];
-                    raw[u][1] = p[1];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[u][i] = raw[u][0][i] + 0.0f; // -0 -> +0
-                    v[u][4 + i] = raw[u][1][i] + 0.0f;
-                }
-        } else {
-            const uint16_t *xb = (const uint16_t *)xin;
-            u32x4 raw[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                raw[u] = u32x4{0u, 0u, 0u, 0u};
-                if (m + u < m1 && cok)
-                    raw[u] = *(const u32x4 *)(xb + (m + u) * d + (int64_t)oct * 8);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[u][2 * i] = bf16lo(raw[u][i]);
-                    v[u][2 * i + 1] = bf16hi(raw[u][i]);
-                }
-        }
-        // ---- transform
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (kMode == kSQ) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    v[u][i] = __builtin_fmaf(v[u][i], r[i], 0.0f); // one rounding; -0 -> +0
-            }
-            if constexpr (kMode == kBflyQ || kMode == kBflyT) {
-                // cross-lane stages first (index bits 4 and 3), then in-lane bits 2, 1, 0
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float other = dpp_xor2(v[u][i]);
-                    v[u][i] = __builtin_fmaf(B.o1, other, B.s1 * v[u][i]);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float other = dpp_xor1(v[u][i]);
-                    v[u][i] = __builtin_fmaf(B.o2, other, B.s2 * v[u][i]);
-                }
-                bfly_inlane<4, false>(v[u], B.a3);
-                bfly_inlane<2, false>(v[u], B.a4);
-                bfly_inlane<1, true>(v[u], B.a5);
-            }
-        }
-        // ---- output
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t mm = m + u;
-            if constexpr (kMode == kBflyT) {
-                if (mm < m1 && cok) {
-                    f32x4 *o = (f32x4 *)(y + mm * d + (int64_t)oct * 8);
-                    o[0] = f32x4{v[u][0], v[u][1], v[u][2], v[u][3]};
-                    o[1] = f32x4{v[u][4], v[u][5], v[u][6], v[u][7]};
-                }
-            } else {
-                float am = __builtin_fabsf(v[u][0]);
-#pragma unroll
-                for (int i = 1; i < 8; ++i)
-                    am = amax_step(am, v[u][i]);
-                am = vmax(am, dpp_xor1(am));
-                am = vmax(am, dpp_xor2(am));
-                const unsigned b = e8m0_byte(am);
-                const float sc = scale_operand(b);
-                unsigned w = cvt8(v[u][0], v[u][1], v[u][2], v[u][3], v[u][4], v[u][5], v[u][6], v[u][7], sc);
-                if (b == 0xFFu)
-                    w = 0u;
-                if (mm < m1 && cok) {
-                    *(unsigned *)(q + mm * (d >> 1) + (int64_t)oct * 4) = w;
-                    if (qp == 0)
-                        s[mm * nB + (oct >> 2)] = (uint8_t)b;
-                }
-            }
-        }
+    // two-stage pipeline; the prefetch past the run re-reads its last row (clamped) and is unused
+    int64_t m = m0;
+    for (; m + kStreamU < m1; m += 2 * kStreamU) {
+        load_rows<kMode>(bufB, xin, m + kStreamU, m1, d, octc);
+        __builtin_amdgcn_sched_barrier(0); // keep the prefetch ahead of these rows' stores
+        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
+        __builtin_amdgcn_sched_barrier(0);
+        load_rows<kMode>(bufA, xin, m + 2 * kStreamU, m1, d, octc);
+        __builtin_amdgcn_sched_barrier(0);
+        process_rows<kMode>(bufB, m + kStreamU, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (m < m1)
+        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,27 +582,32 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
                           uint8_t *s, float *y, hipStream_t stream)
 {
     const int nB = (int)(d / 32);
-    const int nP = (nB + 1) / 2;
+    const int nBG = (nB + kWavesKQ - 1) / kWavesKQ;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    int tpw = tuning().mfma_tiles_per_wave;
+    int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
     if (tpw <= 0) {
-        // enough waves to cover every SIMD about twice, each wave amortising
-        // its block build over as many tiles as that allows
-        const int64_t target_waves = (int64_t)num_cus() * 4 * 2;
-        int64_t t = (nP * nTiles) / target_waves;
-        tpw = (int)(t < 1 ? 1 : (t > 16 ? 16 : t));
+        // about two workgroups per CU over the whole launch, with the token
+        // groups a multiple of the XCD count; each wave amortises its operand
+        // build over the tiles of its group
+        const int64_t target_wgs = (int64_t)num_cus() * 2;
+        int64_t groups = target_wgs / nBG;
+        groups = (groups + kXcds - 1) / kXcds * kXcds;
+        if (groups < (int64_t)kXcds)
+            groups = kXcds;
+        int64_t t = (nTiles + groups - 1) / groups;
+        tpw = (int)(t < 1 ? 1 : (t > 256 ? 256 : t));
     }
-    const int64_t per_group = (int64_t)kWaves * tpw;
-    const int64_t nG = (nTiles + per_group - 1) / per_group;
-    const int64_t grid = nG * nP;
-    if (grid > 0x7FFFFFFF)
+    const int64_t nG = (nTiles + tpw - 1) / tpw;
+    const int64_t nGpad = (nG + kXcds - 1) / kXcds * kXcds; // token groups dealt to XCDs in turn
+    const int64_t grid = nGpad * nBG;
+    if (grid > 0x7FFFFFFF || (int64_t)tpw * kTileT * (d / 2) >= ((int64_t)1 << 31))
         return hipErrorInvalidConfiguration;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
     void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s, (void *)&y, (void *)&nP, (void *)&tpw};
+                      (void *)&s, (void *)&y, (void *)&nBG, (void *)&tpw};
     const void *fn = y ? (const void *)kq_mfma_kernel<false> : (const void *)kq_mfma_kernel<true>;
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args_q, 0, stream);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWavesKQ), args_q, 0, stream);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,
@@ -514,7 +615,7 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
 {
     const int nOct = (int)(d / 8);
     const int nCT = (nOct + 63) / 64;
-    int R = rows_knob;
+    int R = rows_knob > 256 ? 256 : rows_knob;
     if (R <= 0) {
         const int64_t target_waves = (int64_t)num_cus() * 4 * 4;
         int64_t rows = (nCT * M) / target_waves;
@@ -522,8 +623,8 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
         R = (R + 3) & ~3;
     }
     const int64_t nRG = (M + R - 1) / R;
-    const int64_t waves = nRG * nCT;
-    const int64_t grid = (waves + 3) / 4;
+    const int64_t nRGpad = (nRG + kXcds - 1) / kXcds * kXcds;
+    const int64_t grid = nRGpad * ((nCT + 3) / 4);
     if (grid > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;

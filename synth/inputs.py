@@ -25,14 +25,21 @@ import numpy as np
 
 
 def f32_to_bf16_bits(a):
-    """fp32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
+    """fp32 -> bf16 bit patterns, round to nearest even (NaN kept quiet).
+    Works in uint32 (no overflow for any non-NaN pattern) over row chunks."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32)
-    nan = (u & 0x7FFFFFFF) > 0x7F800000
-    rounded = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
-    if nan.any():
-        rounded = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), rounded)
-    return rounded
+    u = a.reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, np.uint16)
+    step = 1 << 24
+    for i in range(0, u.size, step):
+        c = u[i:i + step]
+        r = c + (np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1)))
+        r >>= np.uint32(16)
+        nan = (c & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+        if nan.any():
+            r[nan] = (c[nan] >> np.uint32(16)) | np.uint32(0x40)
+        out[i:i + step] = r
+    return out.reshape(a.shape)
 
 
 def bf16_bits_to_f32(h):

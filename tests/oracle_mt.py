@@ -1,0 +1,58 @@
+"""Run the (single-threaded) oracle over row chunks on several host threads;
+ctypes releases the GIL during each call.  Rows are independent, so the
+result is the same as one call over the whole matrix."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from oracle import oracle as O
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunks(M):
+    step = max(1, (M + THREADS * 4 - 1) // (THREADS * 4))
+    return [(r, min(M, r + step)) for r in range(0, M, step)]
+
+
+def kq_quantize(x, f):
+    M, d = x.shape
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+    y32 = np.empty((M, d), np.float32)
+
+    def job(rr):
+        a, b = rr
+        q[a:b], s[a:b], y32[a:b] = O.kq_quantize(np.ascontiguousarray(x[a:b]), f, want_y32=True)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(job, _chunks(M)))
+    return q, s, y32
+
+
+def kq_z(x, f):
+    M, d = x.shape
+    z = np.empty((M, d), np.float64)
+
+    def job(rr):
+        a, b = rr
+        z[a:b] = O.kq_transform(np.ascontiguousarray(x[a:b]), f)[1]
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(job, _chunks(M)))
+    return z
+
+
+def sq_quantize(x, scale):
+    M, d = x.shape
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+
+    def job(rr):
+        a, b = rr
+        q[a:b], s[a:b] = O.sq_quantize(np.ascontiguousarray(x[a:b]), scale)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(job, _chunks(M)))
+    return q, s

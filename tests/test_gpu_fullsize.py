@@ -1,0 +1,137 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the library's automatic launch shapes).
+
+Configurations 1-4 and the 4096-row sweep are compared against the oracle on
+every row (the oracle runs on host threads over row chunks).  The 16384- and
+65536-row sweeps compare sampled rows against the oracle, plus properties that
+hold at any size: identity factors give exactly the plain MXFP4 of the input,
+and a replicated per-block factor layout gives exactly the shared-set result.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from synth import inputs as I
+from tests import oracle_mt as OM
+from tests import parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; none is visible")
+    import mxfp4_act_quantizer_amd as K
+    return K
+
+
+def to_dev(x_bits):
+    return torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def kq_gpu(K, xd, f, variant=0):
+    q, s = K.kq_quantize(xd, torch.from_numpy(np.ascontiguousarray(f)).cuda(), variant=variant)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+FULL = [("tiny", True), ("dit_1152", False), ("dit_1152", True), ("dit_4608", False), ("dit_4608", True),
+        ("mid_2240", False), ("mid_8960", False), ("dbl_3072", False), ("dbl_12288", False),
+        ("sweep_4096", False)]
+
+
+@pytest.mark.parametrize("name,shared", FULL, ids=[f"{n}-{'shared' if s else 'perblock'}" for n, s in FULL])
+def test_kq_full_config_all_rows(K, name, shared):
+    x = I.make_activation(name)
+    f = I.make_factors(name, shared=shared)
+    M, d = x.shape
+    say(f"[full kq {name}] M={M} d={d} nT={f.shape[0]}")
+    qg, sg = kq_gpu(K, to_dev(x), f)
+    qr, sr, y32 = OM.kq_quantize(x, f)
+    z = OM.kq_z(x, f)
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(qg, sg, qr, sr, ef, bf)
+    say(f"    {res}")
+    if name.startswith("dbl"):
+        # image rows and text rows reported separately
+        m_img = (M * 8) // 9
+        for lab, sl in (("image", slice(0, m_img)), ("text", slice(m_img, M))):
+            r = P.compare(qg[sl], sg[sl], qr[sl], sr[sl], ef[sl], bf[sl])
+            say(f"    {lab} rows: {r}")
+            assert r["ok"]
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("name", ["tiny", "dit_4608", "mid_8960", "dbl_12288", "sweep_4096"])
+def test_sq_full_config_bit_exact(K, name):
+    x = I.make_activation(name)
+    scale = I.smoothquant_scale(x)
+    M, d = x.shape
+    say(f"[full sq {name}] M={M} d={d}")
+    q, s = K.sq_quantize(to_dev(x), torch.from_numpy(scale).cuda())
+    torch.cuda.synchronize()
+    qr, sr = OM.sq_quantize(x, scale)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
+    say(f"    {res}")
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0
+
+
+@pytest.mark.parametrize("name", ["sweep_4096", "sweep_16384", "sweep_65536"])
+def test_sweep_identity_hadamard(K, name):
+    M, d, _ = I.CONFIGS[name]
+    say(f"[sweep {name}] generating M={M} d={d}")
+    x, _, specials = I.act_sweep_special(M, d, I.data_seed(name))
+    xd = to_dev(x)
+    del x
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.choice(M, 112, replace=False),
+                                     specials[rng.choice(len(specials), 64, replace=False), 0]]))
+    xs = xd[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+
+    # identity: bit-exact plain MXFP4, at full size against the fp32 quantizer on the GPU
+    say(f"[sweep {name}] identity nT=1 and nT={d // 32}")
+    qi, si = kq_gpu(K, xd, I.identity_factors(1))
+    q32, s32 = K.mx_quantize_f32(xd.float())
+    torch.cuda.synchronize()
+    assert np.array_equal(qi, q32.cpu().numpy()) and np.array_equal(si, s32.cpu().numpy())
+    del q32, s32
+    qir, sir = O.kq_quantize(xs, I.identity_factors(1))
+    assert np.array_equal(qi[rows], qir) and np.array_equal(si[rows], sir)
+    qb, sb = kq_gpu(K, xd, I.identity_factors(d // 32))
+    assert np.array_equal(qb, qi) and np.array_equal(sb, si)
+    del qb, sb, qi, si
+
+    # normalised WHT-32 via five H2/sqrt(2) factors; replicated layout equals shared
+    say(f"[sweep {name}] hadamard nT=1 and nT={d // 32}")
+    h = I.hadamard_factors(1)
+    qh, sh = kq_gpu(K, xd, h)
+    qhb, shb = kq_gpu(K, xd, I.hadamard_factors(d // 32))
+    assert np.array_equal(qh, qhb) and np.array_equal(sh, shb)
+    qr, sr, y32 = O.kq_quantize(xs, h, want_y32=True)
+    _, z = O.kq_transform(xs, h)
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(qh[rows], sh[rows], qr, sr, ef, bf)
+    say(f"    sampled {len(rows)} rows: {res}")
+    assert res["ok"], res
+
+    # learned-style per-block factors, sampled rows
+    f = I.random_factors(d // 32, I.factor_seed(name))
+    say(f"[sweep {name}] random per-block factors")
+    qg, sg = kq_gpu(K, xd, f)
+    qr, sr, y32 = O.kq_quantize(xs, f, want_y32=True)
+    _, z = O.kq_transform(xs, f)
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(qg[rows], sg[rows], qr, sr, ef, bf)
+    say(f"    sampled {len(rows)} rows: {res}")
+    assert res["ok"], res
+    del xd
+    torch.cuda.empty_cache()
