@@ -10,7 +10,7 @@ Kronecker transform -> MXFP4 codes + E8M0 scales).
   value     = algorithmic bytes of the step / step time  (GB/s)
               algorithmic bytes = 2.53125 B per element (2 read, 0.5 + 1/32 written)
   roofline  = the quantizer kernel's average launch against the 8 TB/s HBM peak,
-              timed with HIP events on the launch stream
+              timed with HIP events around graphs of back-to-back launches
   cpu_baseline = the CPU oracle on a bounded sample of the same workload
 
 Inputs and outputs rotate over enough buffer sets (>= 1 GB per cycle) that
@@ -46,8 +46,7 @@ def parse():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 mfma, 2 butterfly")
     ap.add_argument("--no-extras", action="store_true", help="skip the SmoothQuant / butterfly comparison legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="rows of each matrix in the CPU sample (0 = 32 per host thread, about 15 s)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU-oracle baseline")
     return ap.parse_args()
 
 
@@ -85,9 +84,10 @@ def make_inputs():
     return mats
 
 
-def cpu_baseline(mats, rows):
-    """The oracle, as it stands, on the first `rows` rows of each matrix, spread
-    over host threads by row ranges (ctypes releases the GIL)."""
+def cpu_baseline(mats, min_seconds=10.0):
+    """The oracle, as it stands, over the whole step (every row of both
+    matrices), spread over host threads by row ranges (ctypes releases the
+    GIL), repeated until at least min_seconds of wall time."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import oracle as O
@@ -95,22 +95,27 @@ def cpu_baseline(mats, rows):
     threads = max(1, min(16, os.cpu_count() or 1))
     jobs = []
     for _, x, f, _ in mats:
-        xs = x[:rows]
-        chunk = max(1, (rows + threads - 1) // threads)
+        rows = x.shape[0]
+        chunk = max(1, (rows + 4 * threads - 1) // (4 * threads))
         for r0 in range(0, rows, chunk):
-            jobs.append((np.ascontiguousarray(xs[r0:r0 + chunk]), f))
+            jobs.append((np.ascontiguousarray(x[r0:r0 + chunk]), f))
+    passes = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(lambda a: O.kq_quantize(a[0], a[1]), jobs))
+        while True:
+            list(ex.map(lambda a: O.kq_quantize(a[0], a[1]), jobs))
+            passes += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
     dt = time.perf_counter() - t0
-    elems = sum(rows * x.shape[1] for _, x, _, _ in mats)
+    elems = sum(x.size for _, x, _, _ in mats)
     return {
-        "value": round(elems * BYTES_PER_ELEM / dt / 1e9, 4),
+        "value": round(passes * elems * BYTES_PER_ELEM / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {rows} of 8192 rows of each DiT matrix (d=1152 and d=4608, per-block factor sets); "
-                  f"{elems} elements in {dt:.1f} s, same byte formula as the GPU value",
+        "sample": f"the full step (both DiT matrices, all 8192 rows, per-block factor sets) {passes} times, "
+                  f"{passes * elems} elements in {dt:.1f} s wall on {threads} threads; same byte formula as the GPU value",
     }
 
 
@@ -145,58 +150,76 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step_kq(i, variant, evs=None):
-        for k, b in enumerate(sets[i % nsets]):
-            if evs is not None:
-                evs[k][0].record(stream)
-            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=stream, variant=variant)
-            if evs is not None:
-                evs[k][1].record(stream)
+    def step_kq(i, variant):
+        for b in sets[i % nsets]:
+            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=torch.cuda.current_stream(), variant=variant)
 
-    def step_sq(i, evs=None):
-        for k, b in enumerate(sets[i % nsets]):
-            if evs is not None:
-                evs[k][0].record(stream)
-            K.sq_quantize(b["x"], b["scale"], b["q"], b["s"], stream=stream)
-            if evs is not None:
-                evs[k][1].record(stream)
+    def step_sq(i):
+        for b in sets[i % nsets]:
+            K.sq_quantize(b["x"], b["scale"], b["q"], b["s"], stream=torch.cuda.current_stream())
 
-    def timed(step_fn, steps, warmup):
-        for i in range(warmup):
-            step_fn(i)
+    def capture(fn, count):
+        """A HIP graph of `count` calls fn(0..count-1), captured on a side stream."""
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            fn(0)  # one eager call on the capture stream first
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(count):
+                    fn(i)
         torch.cuda.synchronize()
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in mats] for _ in range(steps)]
+        return g
+
+    def timed_graph(g, replays=1):
+        """Replay a graph: wall and event time of the replays, bracketed by synchronisation."""
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for i in range(steps):
-            step_fn(i, evs[i])
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        launch_ms = [[evs[i][k][0].elapsed_time(evs[i][k][1]) for i in range(steps)] for k in range(len(mats))]
-        return wall, launch_ms
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
 
     variant = args.variant
-    wall, launch_ms = timed(lambda i, e=None: step_kq(i, variant, e), args.steps, args.warmup)
+    # the timed region: exactly K steps, launched as one graph (the launches
+    # themselves would otherwise leave the GPU idle between short kernels)
+    g_warm = capture(lambda i: step_kq(i, variant), max(1, args.warmup))
+    g_main = capture(lambda i: step_kq(i, variant), args.steps)
+    timed_graph(g_warm)
+    wall, ev = timed_graph(g_main)
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
 
-    # roofline of the quantizer kernel: all its launches in the timed region
+    # roofline of the quantizer kernel: per shape, a graph of back-to-back
+    # launches over the rotating buffers, timed with events on its stream
+    LAUNCHES = 40
     launch_bytes = [x.size * BYTES_PER_ELEM for _, x, _, _ in mats]
-    tot_dur = sum(sum(v) for v in launch_ms) / 1e3
-    n_launch = sum(len(v) for v in launch_ms)
-    achieved = sum(launch_bytes[k] * len(launch_ms[k]) for k in range(len(mats))) / tot_dur / 1e9
+    per_shape = {}
+    tot_t, tot_b = 0.0, 0.0
+    for k, (name, x, _, _) in enumerate(mats):
+        def one(i, k=k):
+            b = sets[i % nsets][k]
+            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=torch.cuda.current_stream(), variant=variant)
+        g = capture(one, LAUNCHES)
+        timed_graph(g)
+        _, t = timed_graph(g, 3)
+        avg = t / (3 * LAUNCHES)
+        tot_t += avg
+        tot_b += launch_bytes[k]
+        per_shape[name] = {"avg_us": round(avg * 1e6, 2), "GB/s": round(launch_bytes[k] / avg / 1e9, 1),
+                           "rows/s": round(x.shape[0] / avg, 1), "hbm_pct": round(100 * launch_bytes[k] / avg / 8e12, 2)}
+    achieved = tot_b / tot_t / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash)
-    per_shape = {}
-    for k, (name, x, _, _) in enumerate(mats):
-        avg = float(np.mean(launch_ms[k]))
-        per_shape[name] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(launch_ms[k])) * 1e3, 2),
-                           "GB/s": round(launch_bytes[k] / (avg / 1e3) / 1e9, 1),
-                           "rows/s": round(x.shape[0] / (avg / 1e3), 1)}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": KERNEL_SYMBOL if variant in (0, 1) else "stream_kernel<2>",
-                "avg_launch_us": round(tot_dur / n_launch * 1e6, 2), "launches": n_launch,
-                "algorithmic_bytes_per_launch": round(sum(launch_bytes) / len(launch_bytes)),
+                "avg_launch_us": round(tot_t / len(mats) * 1e6, 2), "launches_per_shape": 3 * LAUNCHES,
+                "algorithmic_bytes_per_launch": round(tot_b / len(mats)),
                 "per_shape": per_shape}
 
     out = {
@@ -216,6 +239,7 @@ def main():
                                "bf16 in, MXFP4 + E8M0 out, per-block Kronecker transforms",
                    "M": 8192, "d": [1152, 4608], "nT": [36, 144], "variant": ["auto", "mfma", "butterfly"][variant],
                    "rows_per_step": 2 * 8192, "rotating_sets": nsets, "accumulate": "fp32",
+                   "launch": "HIP graph of the K timed steps",
                    "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
                    "rows_per_s": round(2 * 8192 / (wall / args.steps), 1),
                    "kernel_source_hash": src_hash},
@@ -223,20 +247,23 @@ def main():
     }
 
     if not args.no_extras:
-        sq_wall, sq_ms = timed(lambda i, e=None: step_sq(i, e), args.steps, args.warmup)
+        g_sq = capture(step_sq, args.steps)
+        timed_graph(capture(step_sq, max(1, args.warmup)))
+        sq_wall, _ = timed_graph(g_sq)
         sq_value = step_bytes / (sq_wall / args.steps) / 1e9
         other = 2 if variant in (0, 1) else 1
-        bf_wall, _ = timed(lambda i, e=None: step_kq(i, other, e), args.steps, args.warmup)
+        g_o = capture(lambda i: step_kq(i, other), args.steps)
+        timed_graph(capture(lambda i: step_kq(i, other), max(1, args.warmup)))
+        o_wall, _ = timed_graph(g_o)
         out["comparison"] = {
             "smoothquant_GB/s": round(sq_value, 1),
             "smoothquant_hbm_pct": round(100 * sq_value / HBM_PEAK_GBS, 2),
             "kroquant_over_smoothquant_speed": round(sq_wall / wall, 4),
-            ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (bf_wall / args.steps) / 1e9, 1),
+            ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (o_wall / args.steps) / 1e9, 1),
         }
 
     if not args.no_cpu:
-        rows = args.cpu_rows or min(8192, 32 * max(1, min(16, os.cpu_count() or 1)))
-        out["cpu_baseline"] = cpu_baseline(mats, rows)
+        out["cpu_baseline"] = cpu_baseline(mats, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
 

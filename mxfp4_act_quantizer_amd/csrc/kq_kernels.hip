@@ -126,18 +126,23 @@ __device__ __forceinline__ float bf16_val(unsigned short h) { return __uint_as_f
 // keeps the next 8 significant bits, so the third remainder fits bf16).
 __device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lane)
 {
+    // the set is the same for the whole wave: scalar loads, then per-lane selects
+    float f[20];
+#pragma unroll
+    for (int i = 0; i < 20; ++i)
+        f[i] = F[i];
     const int h = lane >> 5;
     const int i = lane & 31;
     const int c = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
-    const int c4 = (c >> 4) & 1, c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
-    // F[k*4 + r*2 + col] is entry (r, col) of factor A_{k+1}
-    const float a2 = F[4 + h * 2 + c3];
-    const float a3_0 = F[8 + c2], a3_1 = F[10 + c2];
-    const float a4_0 = F[12 + c1], a4_1 = F[14 + c1];
-    const float a5_0 = F[16 + c0], a5_1 = F[18 + c0];
+    const bool c4 = (c >> 4) & 1, c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
+    // f[k*4 + r*2 + col] is entry (r, col) of factor A_{k+1}
+    const float a2 = h ? (c3 ? f[7] : f[6]) : (c3 ? f[5] : f[4]);
+    const float a3_0 = c2 ? f[9] : f[8], a3_1 = c2 ? f[11] : f[10];
+    const float a4_0 = c1 ? f[13] : f[12], a4_1 = c1 ? f[15] : f[14];
+    const float a5_0 = c0 ? f[17] : f[16], a5_1 = c0 ? f[19] : f[18];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const float p = F[0 + j * 2 + c4] * a2;
+        const float p = (j ? (c4 ? f[3] : f[2]) : (c4 ? f[1] : f[0])) * a2;
         bf16x8 hi, mid, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -205,8 +210,8 @@ __device__ __forceinline__ void stage_x(WgStage &st, int par, const XIn &in, int
 // 16j + 8h .. +7 of block `wave` of the strip (h = l/32).
 template <bool kQuant>
 __device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, int par, const bf16x8 (&A)[3][2],
-                                               int64_t t, int64_t M, int d, int jb, int h, int wave, int tl,
-                                               float *__restrict__ y)
+                                               int64_t t, int64_t M, int d, int jb, bool jb_valid, int h, int wave,
+                                               int tl, float *__restrict__ y)
 {
     bf16x8 bv[2];
 #pragma unroll
@@ -239,7 +244,8 @@ __device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, 
         if (h == 0)
             st.s[par][tl][wave] = (unsigned char)b;
     } else {
-        if (t < M) {
+        // waves past the row end computed a stand-in block: nothing to write
+        if (t < M && jb_valid) {
             f32x4 *o = (f32x4 *)(y + t * d + jb * 32 + 16 * h);
             o[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
             o[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 {
     __shared__ WgStage st;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go round-robin to the 8 XCDs (blockIdx % 8).  All strips of
     // one token group run on the same XCD, one after another, so partial
     // lines written into the same q and s rows merge in that L2.
@@ -329,7 +335,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         __syncthreads();                                                                                           \
         if (kQuant)                                                                                                \
             store_tile(st, (kk - 1) & 1, (kk - 1) * kTileT, bg, nB, d, wave, lane, rq, rs);                        \
-        transform_tile<kQuant>(st, st, kk & 1, A, t_wg + (int64_t)kk * kTileT + tl, M, d, jb, h, wave, tl, y);     \
+        transform_tile<kQuant>(st, st, kk & 1, A, t_wg + (int64_t)kk * kTileT + tl, M, d, jb, jb_raw < nB, h, wave, \
+                               tl, y);                                                                             \
     }
 
     int it = 0;
@@ -578,24 +585,50 @@ static int num_cus()
     return n;
 }
 
+// Resident workgroups of an MFMA kernel per XCD (occupancy from the runtime).
+static int mfma_wgs_per_xcd(const void *fn)
+{
+    static int cached[2] = {0, 0};
+    const int idx = fn == (const void *)kq_mfma_kernel<true> ? 1 : 0;
+    if (!cached[idx]) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kWavesKQ, 0) != hipSuccess || per_cu <= 0)
+            per_cu = 1;
+        cached[idx] = per_cu * num_cus() / (int)kXcds;
+        if (cached[idx] < 1)
+            cached[idx] = 1;
+    }
+    return cached[idx];
+}
+
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                           uint8_t *s, float *y, hipStream_t stream)
 {
     const int nB = (int)(d / 32);
     const int nBG = (nB + kWavesKQ - 1) / kWavesKQ;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
+    const void *fn = y ? (const void *)kq_mfma_kernel<false> : (const void *)kq_mfma_kernel<true>;
     int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
     if (tpw <= 0) {
-        // about two workgroups per CU over the whole launch, with the token
-        // groups a multiple of the XCD count; each wave amortises its operand
-        // build over the tiles of its group
-        const int64_t target_wgs = (int64_t)num_cus() * 2;
-        int64_t groups = target_wgs / nBG;
-        groups = (groups + kXcds - 1) / kXcds * kXcds;
-        if (groups < (int64_t)kXcds)
-            groups = kXcds;
-        int64_t t = (nTiles + groups - 1) / groups;
-        tpw = (int)(t < 1 ? 1 : (t > 256 ? 256 : t));
+        // Pick the tiles per workgroup that minimise (rounds of resident
+        // workgroups) x (tiles per workgroup + a fixed start-up cost of about
+        // 1.5 tiles): one full round beats a round and a small tail.
+        const int64_t resident = mfma_wgs_per_xcd(fn);
+        // output offsets inside a workgroup's rows are 32-bit
+        const int64_t tmax = (((int64_t)1 << 31) - 1) / (kTileT * (d / 2));
+        double best = 1e300;
+        for (int t = 1; t <= 256 && t <= tmax; ++t) {
+            const int64_t groups = (nTiles + t - 1) / t;
+            const int64_t wgs_xcd = (groups + kXcds - 1) / kXcds * nBG;
+            const int64_t rounds = (wgs_xcd + resident - 1) / resident;
+            const double cost = (double)rounds * (t + 1.5);
+            if (cost < best - 1e-9) {
+                best = cost;
+                tpw = t;
+            }
+            if (groups <= (int64_t)kXcds)
+                break; // larger t only lengthens the one round
+        }
     }
     const int64_t nG = (nTiles + tpw - 1) / tpw;
     const int64_t nGpad = (nG + kXcds - 1) / kXcds * kXcds; // token groups dealt to XCDs in turn
@@ -606,7 +639,6 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
     int per_block = nT > 1 ? 1 : 0;
     void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
                       (void *)&s, (void *)&y, (void *)&nBG, (void *)&tpw};
-    const void *fn = y ? (const void *)kq_mfma_kernel<false> : (const void *)kq_mfma_kernel<true>;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWavesKQ), args_q, 0, stream);
 }
 
@@ -616,12 +648,9 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
     const int nOct = (int)(d / 8);
     const int nCT = (nOct + 63) / 64;
     int R = rows_knob > 256 ? 256 : rows_knob;
-    if (R <= 0) {
-        const int64_t target_waves = (int64_t)num_cus() * 4 * 4;
-        int64_t rows = (nCT * M) / target_waves;
-        R = (int)(rows < 4 ? 4 : (rows > 64 ? 64 : rows));
-        R = (R + 3) & ~3;
-    }
+    if (R <= 0)
+        R = 4; // short-lived waves (one pipeline stage of rows each) keep the most loads in flight
+
     const int64_t nRG = (M + R - 1) / R;
     const int64_t nRGpad = (nRG + kXcds - 1) / kXcds * kXcds;
     const int64_t grid = nRGpad * ((nCT + 3) / 4);

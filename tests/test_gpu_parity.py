@@ -307,3 +307,41 @@ def test_mx_f32_exhaustive_bf16_patterns(K):
     qr, sr = O.mx_quantize_f32(x)
     res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr)
     assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0, res
+
+
+def test_graph_replay_matches_eager(K):
+    """The benchmark launches through HIP graphs: every replay must give the
+    eager result, with other eager work and synchronisation in between."""
+    x = I.make_activation("dit_1152", M=300)
+    f = I.make_factors("dit_1152")
+    scale = I.smoothquant_scale(x)
+    xd, fd, sd = dev_bf16(x), dev_f32(f), dev_f32(scale)
+    q_e, s_e = K.kq_quantize(xd, fd)
+    qs_e, ss_e = K.sq_quantize(xd, sd)
+    torch.cuda.synchronize()
+    q_e, s_e, qs_e, ss_e = (t.cpu().numpy() for t in (q_e, s_e, qs_e, ss_e))
+    q = torch.empty((300, 576), dtype=torch.uint8, device="cuda")
+    s = torch.empty((300, 36), dtype=torch.uint8, device="cuda")
+    qs = torch.empty_like(q)
+    ss = torch.empty_like(s)
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        K.kq_quantize(xd, fd, q, s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            K.kq_quantize(xd, fd, q, s, stream=cs)
+            K.sq_quantize(xd, sd, qs, ss, stream=cs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"[graph replay {rep}]")
+        q.fill_(0)
+        qs.fill_(0)
+        s.zero_()
+        ss.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), q_e) and np.array_equal(s.cpu().numpy(), s_e)
+        assert np.array_equal(qs.cpu().numpy(), qs_e) and np.array_equal(ss.cpu().numpy(), ss_e)
+        _ = (xd.float() * 2).sum().item()  # unrelated eager work between replays
