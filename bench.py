@@ -17,6 +17,13 @@ Inputs and outputs rotate over enough buffer sets (>= 1 GB per cycle) that
 every launch reads from HBM rather than the 256 MB last-level cache.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+HBM traffic (the roofline's "traffic" field) comes from two rocprofv3 counter
+passes over `bench.py --traffic-run` (FETCH_SIZE, then WRITE_SIZE), which
+launches a plain bf16->fp32 copy of known size as the calibration kernel and
+then the quantizer steps eagerly; `bench.py --summarize-traffic FETCH_DIR
+WRITE_DIR` turns the two runs' counter CSVs into profiles/kq_mfma_dit_traffic.md,
+which this script reads back while the kernel source hash still matches.
 """
 import argparse
 import hashlib
@@ -36,6 +43,7 @@ BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 ROTATE_BYTES = 1 << 30
 WORKLOAD = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608)]
 KERNEL_SYMBOL = "kq_mfma_kernel<true>"
+RAMP_S = 0.3  # untimed replays before the warm-up steps, for the GPU clocks to leave their idle state
 
 
 def parse():
@@ -47,6 +55,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the SmoothQuant / butterfly comparison legs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU-oracle baseline")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="eager calibration copy + quantizer steps only, for rocprofv3 counter passes")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic profile from two rocprofv3 --pmc output folders (no GPU needed)")
     return ap.parse_args()
 
 
@@ -58,18 +70,115 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kq_mfma_dit_traffic.md")
+# calibration copy of the counter runs: bf16 -> fp32, 2^27 elements
+CAL_ELEMS = 1 << 27
+CAL_READ, CAL_WRITE = 2 * CAL_ELEMS, 4 * CAL_ELEMS
+CAL_REPEAT = 4
+
+
 def load_traffic(src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic_kq_mfma_dit.json")
+    """HBM bytes per launch from the committed rocprofv3 counter runs (the json
+    block of the traffic profile), if they were taken on the current kernel
+    source; otherwise None."""
     try:
-        with open(path) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
+        with open(TRAFFIC_PROFILE) as fh:
+            text = fh.read()
+        t = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
         return None
     if t.get("kernel_source_hash") != src_hash:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def _read_counters(folder):
+    """(dispatch id, kernel name, counter, value) rows of a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), r["Counter_Name"],
+                             float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    return sorted(rows)
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    """Counter runs -> calibrated HBM bytes per quantizer launch -> the traffic profile.
+
+    The traffic run launches the shapes of WORKLOAD in turn, so the n-th
+    quantizer dispatch of a run is shape n mod len(WORKLOAD)."""
+    cal, kq = {}, {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        n = 0
+        for _, name, grid, cname, val in _read_counters(folder):
+            if cname != counter:
+                continue
+            if KERNEL_SYMBOL in name:
+                kq.setdefault((n % len(WORKLOAD), grid), {}).setdefault(counter, []).append(val * 1024.0)
+                n += 1
+            elif "copy" in name and ("BFloat16" in name or "bfloat16" in name):
+                cal.setdefault((name, grid), {}).setdefault(counter, []).append(val * 1024.0)
+    cal = [v for v in cal.values() if len(v.get("FETCH_SIZE", [])) >= CAL_REPEAT]
+    if len(cal) != 1:
+        raise SystemExit(f"expected one calibration copy kernel, found {len(cal)}")
+    cal = cal[0]
+    f_fetch = CAL_READ / float(np.median(cal["FETCH_SIZE"]))
+    f_write = CAL_WRITE / float(np.median(cal["WRITE_SIZE"]))
+    if sorted(k[0] for k in kq) != list(range(len(WORKLOAD))):
+        raise SystemExit(f"quantizer dispatches do not alternate over the {len(WORKLOAD)} shapes: {sorted(kq)}")
+    shapes = {}
+    tot = 0.0
+    for (k, grid), v in sorted(kq.items()):
+        name, M, d = WORKLOAD[k]
+        rd = float(np.mean(v["FETCH_SIZE"])) * f_fetch
+        wr = float(np.mean(v["WRITE_SIZE"])) * f_write
+        alg = M * d * BYTES_PER_ELEM
+        shapes[name] = {"grid": grid, "dispatches": len(v["FETCH_SIZE"]), "read_bytes": round(rd),
+                        "write_bytes": round(wr), "hbm_bytes": round(rd + wr), "algorithmic_bytes": round(alg),
+                        "ratio": round((rd + wr) / alg, 4)}
+        tot += rd + wr
+    blob = {"kernel": KERNEL_SYMBOL, "kernel_source_hash": kernel_source_hash(),
+            "hbm_bytes_per_launch": round(tot / len(shapes)),
+            "algorithmic_bytes_per_launch": round(sum(M * d for _, M, d in WORKLOAD) * BYTES_PER_ELEM / len(WORKLOAD)),
+            "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
+            "calibration": {"kernel": "torch bf16->fp32 copy", "elements": CAL_ELEMS,
+                            "read_bytes": CAL_READ, "write_bytes": CAL_WRITE,
+                            "fetch_kib_median": float(np.median(cal["FETCH_SIZE"])) / 1024,
+                            "write_kib_median": float(np.median(cal["WRITE_SIZE"])) / 1024},
+            "per_shape": shapes}
+    lines = [
+        "# HBM traffic of the KroQuant quantizer kernel, DiT CFG workload (8192 tokens, d=1152 and d=4608)",
+        "",
+        "Commands (from the repository root, on one MI355X; each counter pass is a run of its own):",
+        "",
+        "    timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+        "python3 bench.py --traffic-run --steps 20",
+        "    timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+        "python3 bench.py --traffic-run --steps 20",
+        "    python3 bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "",
+        f"Calibration: a plain bf16->fp32 copy of {CAL_ELEMS} elements reads {CAL_READ} B and writes {CAL_WRITE} B; "
+        f"its counters read FETCH_SIZE {blob['calibration']['fetch_kib_median']:.0f} KiB and WRITE_SIZE "
+        f"{blob['calibration']['write_kib_median']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by "
+        f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f}.",
+        "",
+        "| shape | grid | dispatches | HBM read B | HBM write B | algorithmic B | HBM / algorithmic |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for name, v in shapes.items():
+        lines.append(f"| {name} | {v['grid']} | {v['dispatches']} | {v['read_bytes']} | {v['write_bytes']} | "
+                     f"{v['algorithmic_bytes']} | {v['ratio']} |")
+    lines += ["", "Per launch (average of the two shapes, as the roofline's `achieved`): "
+              f"{blob['hbm_bytes_per_launch']} HBM bytes against {blob['algorithmic_bytes_per_launch']} algorithmic bytes.",
+              "", "```json", json.dumps(blob, indent=1), "```", ""]
+    with open(TRAFFIC_PROFILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def make_inputs():
@@ -121,6 +230,9 @@ def cpu_baseline(mats, min_seconds=10.0):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
               f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
@@ -148,7 +260,6 @@ def main():
                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
         sets.append(one)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
 
     def step_kq(i, variant):
         for b in sets[i % nsets]:
@@ -184,11 +295,33 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
 
+    def clock_ramp(g):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < RAMP_S:
+            g.replay()
+            torch.cuda.synchronize()
+        return round(time.perf_counter() - t0, 3)
+
     variant = args.variant
+    if args.traffic_run:
+        src = torch.randn(CAL_ELEMS, device=dev).to(torch.bfloat16)
+        dst = torch.empty(CAL_ELEMS, dtype=torch.float32, device=dev)
+        for _ in range(CAL_REPEAT):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        for i in range(args.warmup + args.steps):
+            step_kq(i, variant)
+        torch.cuda.synchronize()
+        print(f"traffic run: {CAL_REPEAT} calibration copies, {args.warmup + args.steps} quantizer steps", flush=True)
+        return
     # the timed region: exactly K steps, launched as one graph (the launches
     # themselves would otherwise leave the GPU idle between short kernels)
     g_warm = capture(lambda i: step_kq(i, variant), max(1, args.warmup))
     g_main = capture(lambda i: step_kq(i, variant), args.steps)
+    # the GPU idles in a low-power state: untimed replays until its clocks
+    # have ramped (about RAMP_S seconds), then the W warm-up steps, then K
+    ramp_s = clock_ramp(g_warm)
     timed_graph(g_warm)
     wall, ev = timed_graph(g_main)
     ms_per_step = wall * 1e3 / args.steps
@@ -199,7 +332,6 @@ def main():
     LAUNCHES = 40
     launch_bytes = [x.size * BYTES_PER_ELEM for _, x, _, _ in mats]
     per_shape = {}
-    tot_t, tot_b = 0.0, 0.0
     for k, (name, x, _, _) in enumerate(mats):
         def one(i, k=k):
             b = sets[i % nsets][k]
@@ -208,19 +340,20 @@ def main():
         timed_graph(g)
         _, t = timed_graph(g, 3)
         avg = t / (3 * LAUNCHES)
-        tot_t += avg
-        tot_b += launch_bytes[k]
         per_shape[name] = {"avg_us": round(avg * 1e6, 2), "GB/s": round(launch_bytes[k] / avg / 1e9, 1),
                            "rows/s": round(x.shape[0] / avg, 1), "hbm_pct": round(100 * launch_bytes[k] / avg / 8e12, 2)}
-    achieved = tot_b / tot_t / 1e9
+    # achieved: the timed region itself (its HIP events), per quantizer launch
+    n_launch = args.steps * len(mats)
+    achieved = step_bytes * args.steps / ev / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": KERNEL_SYMBOL if variant in (0, 1) else "stream_kernel<2>",
-                "avg_launch_us": round(tot_t / len(mats) * 1e6, 2), "launches_per_shape": 3 * LAUNCHES,
-                "algorithmic_bytes_per_launch": round(tot_b / len(mats)),
-                "per_shape": per_shape}
+                "avg_launch_us": round(ev / n_launch * 1e6, 2), "launches_timed": n_launch,
+                "algorithmic_bytes_per_launch": round(step_bytes / len(mats)),
+                "timing": "HIP events on the launch stream around the timed graph of K steps",
+                "per_shape": per_shape, "per_shape_timing": f"graphs of {LAUNCHES} launches of one shape, replayed 3x"}
 
     out = {
         "metric": METRIC,
@@ -239,7 +372,7 @@ def main():
                                "bf16 in, MXFP4 + E8M0 out, per-block Kronecker transforms",
                    "M": 8192, "d": [1152, 4608], "nT": [36, 144], "variant": ["auto", "mfma", "butterfly"][variant],
                    "rows_per_step": 2 * 8192, "rotating_sets": nsets, "accumulate": "fp32",
-                   "launch": "HIP graph of the K timed steps",
+                   "launch": "HIP graph of the K timed steps", "clock_ramp_s": ramp_s,
                    "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
                    "rows_per_s": round(2 * 8192 / (wall / args.steps), 1),
                    "kernel_source_hash": src_hash},

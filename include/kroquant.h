@@ -137,6 +137,12 @@ const char *kq_status_string(int status);
 /* Build description (target, variant defaults), static storage. */
 const char *kq_build_info(void);
 
+/* The hipError_t value behind the calling thread's most recent KQ_ERR_HIP
+ * return (hipSuccess = 0 if there was none), and its name (static storage,
+ * from the HIP runtime).  Neither call touches the GPU. */
+int kq_last_hip_error(void);
+const char *kq_hip_error_name(int code);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ KQ_VARIANT_BUTTERFLY = 2
 EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
-    "kq_status_string", "kq_build_info",
+    "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -55,16 +55,23 @@ _lib.kq_status_string.argtypes = [_INT]
 _lib.kq_status_string.restype = ctypes.c_char_p
 _lib.kq_build_info.argtypes = []
 _lib.kq_build_info.restype = ctypes.c_char_p
+_lib.kq_last_hip_error.argtypes = []
+_lib.kq_hip_error_name.argtypes = [_INT]
+_lib.kq_hip_error_name.restype = ctypes.c_char_p
 _lib.kq_set_tuning.argtypes = [_INT, _INT]
 for _name in EXPORTS + ("kq_set_tuning",):
-    if _name not in ("kq_status_string", "kq_build_info"):
+    if _name not in ("kq_status_string", "kq_build_info", "kq_hip_error_name"):
         getattr(_lib, _name).restype = _INT
 
 
 class KQError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {kq_status_string(status)} (status {status})")
+        msg = f"{where}: {kq_status_string(status)} (status {status})"
+        if status == KQ_ERR_HIP:
+            self.hip_error = _lib.kq_last_hip_error()
+            msg += f": {_lib.kq_hip_error_name(self.hip_error).decode()} ({self.hip_error})"
+        super().__init__(msg)
 
 
 def kq_status_string(status):

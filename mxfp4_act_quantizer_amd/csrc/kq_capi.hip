@@ -37,7 +37,16 @@ int check_sets(int64_t d, int64_t nT)
     return KQ_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
+// HIP error behind the calling thread's most recent KQ_ERR_HIP return
+thread_local hipError_t last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return KQ_OK;
+    last_hip_error = e;
+    return KQ_ERR_HIP;
+}
 
 // shared checks of the quantizing entry points (x is bf16 or fp32)
 int check_quant_io(const void *x, int64_t xbytes, const uint8_t *q, const uint8_t *s, int64_t M, int64_t d)
@@ -174,6 +183,10 @@ const char *kq_build_info(void)
            "butterfly=DPP quad stages; FP4 via v_cvt_scalef32_pk_fp4_f32";
 }
 
+int kq_last_hip_error(void) { return (int)last_hip_error; }
+
+const char *kq_hip_error_name(int code) { return hipGetErrorName((hipError_t)code); }
+
 // Tuning knobs for measurements (not part of the stable header).
 int kq_set_tuning(int key, int value)
 {
@@ -181,6 +194,7 @@ int kq_set_tuning(int key, int value)
     case 0: kq::tuning().mfma_tiles_per_wave = value; return KQ_OK;
     case 1: kq::tuning().bfly_rows_per_wave = value; return KQ_OK;
     case 2: kq::tuning().stream_rows_per_wave = value; return KQ_OK;
+    case 3: kq::tuning().mfma_interleave = value; return KQ_OK;
     default: return KQ_ERR_ARG;
     }
 }

@@ -11,6 +11,7 @@ struct Tuning {
     int mfma_tiles_per_wave;  // 0 = automatic
     int bfly_rows_per_wave;   // 0 = automatic
     int stream_rows_per_wave; // 0 = automatic
+    int mfma_interleave;      // 0 = automatic, 1 = contiguous token groups, 2 = interleaved groups
 };
 Tuning &tuning();
 

@@ -42,7 +42,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0};
+    static Tuning t{0, 0, 0, 0};
     return t;
 }
 
@@ -181,20 +181,29 @@ struct XIn {
     u32x4 v[2];
 };
 
-// Load this wave's share of a tile.  Chunks of blocks past the row end read
-// the row start instead, rows past M read row M-1: every load is in bounds,
-// and neither result is ever stored.
+// Load this wave's share of the tile at token row r0 through a buffer range
+// that holds exactly the tile's rows below M (none when `valid` is false, for
+// the look-ahead steps past a workgroup's last tile).  Rows past M and chunks
+// of blocks past the row end (bit 31 set in their offsets) fall outside the
+// range: the hardware returns zeros for them without touching memory, and no
+// such value is ever stored.  x is read exactly once, so the loads are marked
+// nontemporal (streamed past the caches rather than kept there).
+constexpr int kAuxNT = 2; // buffer instruction cache policy: nontemporal
+
 __device__ __forceinline__ void load_x(XIn &in, const uint16_t *__restrict__ x, int64_t M, int d, int bg, int nB,
-                                       int64_t t0, int wave, int lane)
+                                       int64_t r0, bool valid, int wave, int lane)
 {
     const int chunk = lane & 31;
     const int blk = bg * kWavesKQ + (chunk >> 2);
-    const int col = (blk < nB ? bg * (kStrip / 2) + chunk * 8 : 0); // element offset in the row
+    const int64_t rows = valid ? ((M - r0) < kTileT ? (M - r0) : kTileT) : 0;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(x + r0 * d), 0, (int)(rows * d * 2), kBufWord3);
+    const unsigned drop = (unsigned)(blk >= nB) << 31;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        int64_t t = t0 + 4 * wave + 2 * k + (lane >> 5);
-        t = t < M ? t : M - 1;
-        in.v[k] = *(const u32x4 *)(x + t * d + col);
+        const int row = 4 * wave + 2 * k + (lane >> 5);
+        const unsigned off = (unsigned)((row * d + bg * (kStrip / 2) + chunk * 8) * 2) | drop;
+        in.v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, kAuxNT));
     }
 }
 
@@ -255,40 +264,52 @@ __device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, 
     }
 }
 
-// Store one staged tile: waves 0-3 write the codes (eight tokens each, eight
-// lanes x 16 bytes per token row: one contiguous 128-byte segment), waves 4-7
-// the scale bytes (eight consecutive bytes per token).  Rows past M fall
-// outside the workgroup's ranges; blocks past the row end set bit 31 of
-// their offsets, which the range check drops.
-__device__ __forceinline__ void store_tile(const WgStage &st, int par, int tr0, int bg, int nB, int d, int wave,
+// Store one staged tile.  Every wave issues the same two stores, with no
+// branch (so the compiler's memory-counter waits stay exact): 8 code bytes
+// per lane, four tokens per wave (sixteen lanes x 8 bytes = one contiguous
+// 128-byte segment per token row), and one scale byte per lane for waves 0-3
+// (eight consecutive bytes per token).  rq and rs cover the tile's own rows,
+// so rows past M fall outside them; blocks past the row end, the scale lanes
+// of waves 4-7, and every lane when `valid` is false set bit 31 of their
+// offsets, which the range check drops.
+__device__ __forceinline__ void store_tile(const WgStage &st, int par, bool valid, int bg, int nB, int d, int wave,
                                            int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
 {
-    const int c = lane & 7;
-    const int blk = bg * kWavesKQ + c;
-    const unsigned drop = (unsigned)(blk >= nB || tr0 < 0) << 31;
-    if (wave < 4) {
-        const int tt = wave * 8 + (lane >> 3);
-        const u32x4 v = *(const u32x4 *)&st.q[par][tt][c * 16];
-        __builtin_amdgcn_raw_buffer_store_b128(v, rq, (int)((unsigned)((tr0 + tt) * (d >> 1) + blk * 16) | drop), 0,
-                                               0);
-    } else {
-        const int tt = (wave - 4) * 8 + (lane >> 3);
-        __builtin_amdgcn_raw_buffer_store_b8(st.s[par][tt][c], rs, (int)((unsigned)((tr0 + tt) * nB + blk) | drop), 0,
-                                             0);
-    }
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const int tq = wave * 4 + (lane >> 4);
+    const int c8 = lane & 15;
+    const unsigned drop_q = (unsigned)(bg * kWavesKQ + (c8 >> 1) >= nB || !valid) << 31;
+    const u32x2 v = *(const u32x2 *)&st.q[par][tq][c8 * 8];
+    __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * 128 + c8 * 8) | drop_q), 0, 0);
+    const int ts = (wave & 3) * 8 + (lane >> 3);
+    const int cs = lane & 7;
+    const unsigned drop_s = (unsigned)(bg * kWavesKQ + cs >= nB || !valid || wave >= 4) << 31;
+    __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs, (int)((unsigned)(ts * nB + bg * kWavesKQ + cs) | drop_s),
+                                         0, 0);
 }
 
 // One workgroup: a strip of eight blocks (one per wave for the transform) and
-// a run of 32-token tiles the eight waves walk together.  Per tile, in order:
-// stage the tile's x (loaded three tiles earlier) in LDS, issue the loads of
-// the tile three ahead, barrier, store the previous tile's staged codes,
-// transform this tile from LDS into the staging buffer.  One barrier per tile
-// orders all of it (the LDS buffers alternate by tile parity).  Loads past the
-// last tile re-read that tile (an L2 hit), so every load is unconditional.
+// a sequence of 32-token tiles the eight waves walk together: tiles
+// tile0, tile0 + stride, tile0 + 2*stride, ...  With stride 1 a workgroup owns
+// a contiguous run of rows; with stride = number of token groups the groups
+// interleave, so the workgroups resident at one time cover one compact band
+// of rows (as a grid-stride copy does).  Per tile, in order: issue the loads
+// of the tile kRing-1 ahead, stage this tile's x (loaded kRing-1 steps
+// earlier) in LDS, barrier, store the previous tile's staged codes, transform
+// this tile from LDS into the staging buffer.  One barrier per tile orders all of it
+// (the LDS buffers alternate by tile parity).  Every load instruction is
+// issued unconditionally; those of look-ahead steps past the last tile have
+// an empty range and fetch nothing.
+#ifndef KQ_RING
+#define KQ_RING 4
+#endif
+constexpr int kRing = KQ_RING; // tiles in flight per wave: kRing - 1 ahead of the one being staged
+
 template <bool kQuant>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
-    uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg)
+    uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
+    int interleave)
 {
     __shared__ WgStage st;
     const int lane = threadIdx.x & 63;
@@ -302,61 +323,71 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int64_t group = (int64_t)(slot / (unsigned)nBG) * kXcds + xcd;
     const int nB = d >> 5;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const int64_t tile0 = group * tiles_per_wg;
-    if (tile0 >= nTiles)
+    const int64_t nG = (nTiles + tiles_per_wg - 1) / tiles_per_wg;
+    if (group >= nG)
         return; // padding workgroup: uniform over the workgroup, before any barrier
+    const int64_t tile0 = interleave ? group : group * tiles_per_wg;
+    const int64_t stride = interleave ? nG : 1;
+    const int64_t left = (nTiles - tile0 + stride - 1) / stride;
+    const int n = (int)(left < tiles_per_wg ? left : tiles_per_wg);
     const int jb_raw = bg * kWavesKQ + wave;
     // waves past the row end take part in loads and barriers and transform block
     // nB-1 (their results are never stored)
     const int jb = jb_raw < nB ? jb_raw : nB - 1;
-    const int n = (int)((nTiles - tile0) < tiles_per_wg ? (nTiles - tile0) : tiles_per_wg);
     const int h = lane >> 5;
     const int tl = lane & 31;
-    const int64_t t_wg = tile0 * kTileT;
-    const int64_t rows_wg = (M - t_wg) < (int64_t)n * kTileT ? (M - t_wg) : (int64_t)n * kTileT;
-    // this workgroup's token rows [t_wg, t_wg + rows_wg) bound its output ranges
-    __amdgpu_buffer_rsrc_t rq = out_buffer(kQuant ? q + t_wg * (d >> 1) : nullptr, kQuant ? rows_wg * (d >> 1) : 0);
-    __amdgpu_buffer_rsrc_t rs = out_buffer(kQuant ? s + t_wg * nB : nullptr, kQuant ? rows_wg * nB : 0);
-    auto tbase = [&](int k) -> int64_t { return t_wg + (int64_t)(k < n ? k : n - 1) * kTileT; };
+    // first token row of step k (steps past the last tile name it again; their
+    // loads are empty)
+    auto trow = [&](int k) -> int64_t { return (tile0 + (int64_t)(k < n ? k : n - 1) * stride) * kTileT; };
 
-    XIn b0, b1, b2, b3;
-    load_x(b0, x, M, d, bg, nB, tbase(0), wave, lane);
-    load_x(b1, x, M, d, bg, nB, tbase(1), wave, lane);
-    load_x(b2, x, M, d, bg, nB, tbase(2), wave, lane);
+    // register ring of kRing tiles: tile k lives in ring[k % kRing] from its
+    // load (kRing - 1 steps ahead) until it is staged in LDS
+    XIn ring[kRing];
+    // output ranges of one tile's rows
+    auto store_prev = [&](int kp) {
+        const int64_t r0 = trow(kp < 0 ? 0 : kp);
+        const int64_t rows = (M - r0) < kTileT ? (M - r0) : kTileT;
+        store_tile(st, kp & 1, kp >= 0, bg, nB, d, wave, lane, out_buffer(q + r0 * (d >> 1), rows * (d >> 1)),
+                   out_buffer(s + r0 * nB, rows * nB));
+    };
+    // Each prologue load is followed by a store pair with every lane dropped
+    // (no memory access), so the memory counter holds the same sequence on
+    // entry to the loop as after a loop step, and the compiler's waits inside
+    // the loop stay exact rather than falling back to the prologue's shorter
+    // sequence.
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k) {
+        load_x(ring[k], x, M, d, bg, nB, trow(k), k < n, wave, lane);
+        if (kQuant)
+            store_prev(-1);
+    }
 
     bf16x8 A[3][2];
     build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * 20, lane);
 
-#define KQ_STEP(cur, ld, k)                                                                                        \
-    {                                                                                                              \
-        const int kk = it + (k);                                                                                   \
-        stage_x(st, kk & 1, cur, wave, lane);                                                                      \
-        load_x(ld, x, M, d, bg, nB, tbase(kk + 3), wave, lane);                                                    \
-        __syncthreads();                                                                                           \
-        if (kQuant)                                                                                                \
-            store_tile(st, (kk - 1) & 1, (kk - 1) * kTileT, bg, nB, d, wave, lane, rq, rs);                        \
-        transform_tile<kQuant>(st, st, kk & 1, A, t_wg + (int64_t)kk * kTileT + tl, M, d, jb, jb_raw < nB, h, wave, \
-                               tl, y);                                                                             \
-    }
+    auto step = [&](const XIn &cur, XIn &ld, int kk) {
+        load_x(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
+        stage_x(st, kk & 1, cur, wave, lane);
+        __syncthreads();
+        if (kQuant)
+            store_prev(kk - 1);
+        transform_tile<kQuant>(st, st, kk & 1, A, trow(kk) + tl, M, d, jb, jb_raw < nB, h, wave, tl, y);
+    };
 
     int it = 0;
-    for (; it + 3 < n; it += 4) {
-        KQ_STEP(b0, b3, 0)
-        KQ_STEP(b1, b0, 1)
-        KQ_STEP(b2, b1, 2)
-        KQ_STEP(b3, b2, 3)
+    for (; it + kRing - 1 < n; it += kRing) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k)
+            step(ring[k], ring[(k + kRing - 1) % kRing], it + k);
     }
-    // at most three tiles left, already loaded in b0..b2 (their prefetches re-read the last tile)
-    if (it < n)
-        KQ_STEP(b0, b3, 0)
-    if (it + 1 < n)
-        KQ_STEP(b1, b3, 1)
-    if (it + 2 < n)
-        KQ_STEP(b2, b3, 2)
-#undef KQ_STEP
+    // fewer than kRing tiles left, already in ring[0 ..]; their look-ahead loads are empty
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k)
+        if (it + k < n)
+            step(ring[k], ring[kRing - 1], it + k);
     if (kQuant) {
         __syncthreads();
-        store_tile(st, (n - 1) & 1, (n - 1) * kTileT, bg, nB, d, wave, lane, rq, rs);
+        store_prev(n - 1);
     }
 }
 
@@ -413,27 +444,27 @@ __device__ __forceinline__ void bfly_inlane(float (&v)[8], const float (&A)[4])
 
 constexpr int kStreamU = 4; // rows per pipeline stage of the streaming kernels
 
-// Raw loads of U rows of one lane's 8 channels.  Rows past the end re-read the
-// last row of the wave's run (results not stored), so every load is in bounds.
+// Raw loads of U rows of one lane's 8 channels, through a buffer range that
+// holds exactly the wave's rows [m0, m1).  Rows past m1 and lanes past the
+// row end (bit 31 of lane_off) fall outside it: the hardware returns zeros
+// without touching memory, and no such value is stored.  Nontemporal: x is
+// read once.
 template <int kMode>
 struct RowsIn {
     u32x4 v[kStreamU][kMode == kMXF32 ? 2 : 1];
 };
 
 template <int kMode>
-__device__ __forceinline__ void load_rows(RowsIn<kMode> &in, const void *__restrict__ xin, int64_t m, int64_t m1,
-                                          int d, int octc)
+__device__ __forceinline__ void load_rows(RowsIn<kMode> &in, __amdgpu_buffer_rsrc_t rx, int mr, int d,
+                                          unsigned lane_off)
 {
+    constexpr int kES = kMode == kMXF32 ? 4 : 2; // bytes per input element
 #pragma unroll
     for (int u = 0; u < kStreamU; ++u) {
-        const int64_t mm = (m + u < m1) ? m + u : m1 - 1;
-        if constexpr (kMode == kMXF32) {
-            const u32x4 *p = (const u32x4 *)((const float *)xin + mm * d + (int64_t)octc * 8);
-            in.v[u][0] = p[0];
-            in.v[u][1] = p[1];
-        } else {
-            in.v[u][0] = *(const u32x4 *)((const uint16_t *)xin + mm * d + (int64_t)octc * 8);
-        }
+        const unsigned off = (unsigned)((mr + u) * d * kES) + lane_off;
+        in.v[u][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, kAuxNT));
+        if constexpr (kMode == kMXF32)
+            in.v[u][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(off + 16), 0, kAuxNT));
     }
 }
 
@@ -534,11 +565,15 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
     const int nB = d >> 5;
     const int oct = ct * 64 + lane;
     const bool cok = oct < nOct;
-    const int octc = cok ? oct : nOct - 1; // lanes past the row end re-read a valid chunk (not stored)
+    const int octc = cok ? oct : nOct - 1; // parameter index for lanes past the row end (results not stored)
     const int qp = lane & 3;
+    constexpr int kES = kMode == kMXF32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const unsigned char *)xin + m0 * d * kES), 0, (int)((m1 - m0) * d * kES), kBufWord3);
+    const unsigned lane_off = (unsigned)(oct * 8 * kES) | ((unsigned)(cok ? 0 : 1) << 31);
 
     RowsIn<kMode> bufA, bufB;
-    load_rows<kMode>(bufA, xin, m0, m1, d, octc);
+    load_rows<kMode>(bufA, rx, 0, d, lane_off);
     const bool quant = (kMode != kBflyT);
     __amdgpu_buffer_rsrc_t rq = out_buffer(quant ? q + m0 * (d >> 1) : nullptr, quant ? (m1 - m0) * (d >> 1) : 0);
     __amdgpu_buffer_rsrc_t rs = out_buffer(quant ? s + m0 * nB : nullptr, quant ? (m1 - m0) * nB : 0);
@@ -555,14 +590,14 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
         bfly_setup(B, aux + (int64_t)set * 20, qp);
     }
 
-    // two-stage pipeline; the prefetch past the run re-reads its last row (clamped) and is unused
+    // two-stage pipeline; a prefetch past the run falls outside the range and fetches nothing
     int64_t m = m0;
     for (; m + kStreamU < m1; m += 2 * kStreamU) {
-        load_rows<kMode>(bufB, xin, m + kStreamU, m1, d, octc);
+        load_rows<kMode>(bufB, rx, (int)(m + kStreamU - m0), d, lane_off);
         __builtin_amdgcn_sched_barrier(0); // keep the prefetch ahead of these rows' stores
         process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
         __builtin_amdgcn_sched_barrier(0);
-        load_rows<kMode>(bufA, xin, m + 2 * kStreamU, m1, d, octc);
+        load_rows<kMode>(bufA, rx, (int)(m + 2 * kStreamU - m0), d, lane_off);
         __builtin_amdgcn_sched_barrier(0);
         process_rows<kMode>(bufB, m + kStreamU, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
         __builtin_amdgcn_sched_barrier(0);
@@ -608,37 +643,47 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
     const int nBG = (nB + kWavesKQ - 1) / kWavesKQ;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
     const void *fn = y ? (const void *)kq_mfma_kernel<false> : (const void *)kq_mfma_kernel<true>;
+    const int64_t resident = mfma_wgs_per_xcd(fn); // per XCD
     int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
+    int interleave = tuning().mfma_interleave == 2 ? 1 : 0;
     if (tpw <= 0) {
-        // Pick the tiles per workgroup that minimise (rounds of resident
-        // workgroups) x (tiles per workgroup + a fixed start-up cost of about
-        // 1.5 tiles): one full round beats a round and a small tail.
-        const int64_t resident = mfma_wgs_per_xcd(fn);
-        // output offsets inside a workgroup's rows are 32-bit
-        const int64_t tmax = (((int64_t)1 << 31) - 1) / (kTileT * (d / 2));
-        double best = 1e300;
-        for (int t = 1; t <= 256 && t <= tmax; ++t) {
-            const int64_t groups = (nTiles + t - 1) / t;
-            const int64_t wgs_xcd = (groups + kXcds - 1) / kXcds * nBG;
-            const int64_t rounds = (wgs_xcd + resident - 1) / resident;
-            const double cost = (double)rounds * (t + 1.5);
-            if (cost < best - 1e-9) {
-                best = cost;
-                tpw = t;
-            }
-            if (groups <= (int64_t)kXcds)
-                break; // larger t only lengthens the one round
+        // Launch shape, from measurements on MI355X (HBM time of one launch
+        // against tiles per workgroup, for M = 2048..65536 and d = 1152..12288):
+        // workgroups resident at the same time should cover one compact band
+        // of rows, and each should walk enough tiles to hide its start-up.
+        //  - If one resident round of interleaved token groups covers the rows
+        //    with 3..12 tiles per workgroup, use it.
+        //  - Fewer tiles than that: contiguous groups of 3 tiles.
+        //  - Otherwise contiguous groups of 4 tiles once that makes at least
+        //    four rounds of resident workgroups, else of 6.
+        int64_t gx = resident / nBG; // token groups per XCD in one round
+        if (gx < 1)
+            gx = 1;
+        const int64_t t1 = (nTiles + gx * kXcds - 1) / (gx * kXcds);
+        if (tuning().mfma_interleave != 1 && t1 >= 3 && t1 <= 12) {
+            tpw = (int)t1;
+            interleave = 1;
+        } else if (t1 < 3) {
+            tpw = 3;
+            interleave = 0;
+        } else {
+            const int64_t groups4 = (nTiles + 3) / 4;
+            const int64_t rounds4 = ((groups4 + kXcds - 1) / kXcds * nBG) / resident;
+            tpw = rounds4 >= 4 ? 4 : 6;
+            interleave = 0;
         }
+        if (tuning().mfma_interleave == 2)
+            interleave = 1;
     }
     const int64_t nG = (nTiles + tpw - 1) / tpw;
     const int64_t nGpad = (nG + kXcds - 1) / kXcds * kXcds; // token groups dealt to XCDs in turn
     const int64_t grid = nGpad * nBG;
-    if (grid > 0x7FFFFFFF || (int64_t)tpw * kTileT * (d / 2) >= ((int64_t)1 << 31))
+    if (grid > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
     void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s, (void *)&y, (void *)&nBG, (void *)&tpw};
+                      (void *)&s, (void *)&y, (void *)&nBG, (void *)&tpw, (void *)&interleave};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWavesKQ), args_q, 0, stream);
 }
 

@@ -58,7 +58,10 @@ def boundary_flags(z, y32, tol=TOL):
     db = delta.reshape(M, nB, 32)
     amax = ab.max(axis=2)
     dmax = db.max(axis=2)
-    E_lo = shared_exponent(np.maximum(amax - dmax, 0.0))
+    # blocks holding Inf/NaN give inf - inf here; their scale byte is 0xFF
+    # either way, so the arithmetic warning carries no information
+    with np.errstate(invalid="ignore"):
+        E_lo = shared_exponent(np.maximum(amax - dmax, 0.0))
     E_hi = shared_exponent(amax + dmax)
     blk = E_lo != E_hi
     E = shared_exponent(amax)  # the oracle's own exponent

@@ -41,6 +41,18 @@ def test_status_strings():
     assert K.kq_status_string(99) == "unknown status"
 
 
+def test_hip_error_detail_without_gpu():
+    # a thread that saw no KQ_ERR_HIP return reports hipSuccess; names come from the runtime
+    import threading
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(K.lib().kq_last_hip_error()))
+    t.start()
+    t.join()
+    assert seen == [0]
+    assert K.lib().kq_hip_error_name(0) == b"hipSuccess"
+    assert K.lib().kq_hip_error_name(98) == b"hipErrorInvalidDeviceFunction"
+
+
 # ---------------------------------------------------------------------------
 # argument checks: every one returns before any HIP call
 # ---------------------------------------------------------------------------
