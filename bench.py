@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU-oracle baseline")
     ap.add_argument("--traffic-run", action="store_true",
                     help="eager calibration copy + quantizer steps only, for rocprofv3 counter passes")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="per-configuration table: KroQuant (MFMA per-block and shared, butterfly), SmoothQuant "
+                         "and the copy ceiling, each timed alone")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic profile from two rocprofv3 --pmc output folders (no GPU needed)")
     return ap.parse_args()
@@ -228,10 +231,98 @@ def cpu_baseline(mats, min_seconds=10.0):
     }
 
 
+def all_configs(args):
+    """Every configured shape (except the tiny smoke case): the MFMA quantizer
+    with per-block and with shared factors, the butterfly variant, SmoothQuant
+    and the 4:1 copy ceiling, each as a graph of `--steps` launches over
+    rotating buffers (>= 1 GB per cycle), timed with HIP events.  Inputs are
+    N(0,1) bf16 with 1% outlier channels x50 drawn on the GPU (the kernels'
+    time does not depend on the values)."""
+    import torch
+
+    import mxfp4_act_quantizer_amd as K
+    from synth import inputs as I
+    dev = torch.device("cuda:0")
+    table = []
+    for name, (M, d, _) in I.CONFIGS.items():
+        if name == "tiny":
+            continue
+        elems = M * d
+        alg = elems * BYTES_PER_ELEM
+        nsets = max(2, int(np.ceil(ROTATE_BYTES / alg)))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(I.data_seed(name))
+        chan = torch.ones(d, device=dev)
+        chan[torch.randperm(d, generator=gen, device=dev)[:max(1, d // 100)]] = 50.0
+        bufs = []
+        for _ in range(nsets):
+            x = (torch.randn(M, d, generator=gen, device=dev) * chan).to(torch.bfloat16)
+            bufs.append(dict(x=x, q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
+                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
+        amax = bufs[0]["x"].float().abs().amax(dim=0)
+        scale = torch.sqrt(torch.clamp(amax, min=1e-5))
+        f_pb = torch.from_numpy(I.random_factors(d // 32, I.factor_seed(name))).to(dev)
+        f_sh = torch.from_numpy(I.random_factors(1, I.factor_seed(name))).to(dev)
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream
+        legs = {
+            "kq_mfma_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=1),
+            "kq_mfma_shared": lambda b: K.kq_quantize(b["x"], f_sh, b["q"], b["s"], stream=cur(), variant=1),
+            "kq_butterfly_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=2),
+            "smoothquant": lambda b: K.sq_quantize(b["x"], scale, b["q"], b["s"], stream=cur()),
+            "copy41": lambda b: K.measure_copy41(b["x"], b["q"], stream=cur()),
+        }
+        row = {"config": name, "M": M, "d": d, "algorithmic_bytes": int(alg)}
+        for leg, fn in legs.items():
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                fn(bufs[0])
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=cs):
+                    for i in range(args.steps):
+                        fn(bufs[i % nsets])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.1:  # clocks up
+                g.replay()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            nbytes = elems * 2.5 if leg == "copy41" else alg
+            row[leg] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                        "hbm_pct": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "rows/s": round(M / us * 1e6, 1)}
+        row["kq_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_perblock"]["us"], 4)
+        row["kq_over_copy41_speed"] = round(row["copy41"]["us"] / row["kq_mfma_perblock"]["us"], 4)
+        table.append(row)
+        print(json.dumps(row), flush=True)
+        del bufs
+        torch.cuda.empty_cache()
+    print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ MFMA shared us | KQ butterfly us | "
+          "SmoothQuant us (GB/s, %peak) | copy 4:1 us (GB/s) | KQ/SQ speed | KQ/copy speed |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in table:
+        a, b, c, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_butterfly_perblock",
+                                           "smoothquant", "copy41"))
+        print(f"| {r['config']} | {r['M']}x{r['d']} | {a['us']} ({a['GB/s']}, {a['hbm_pct']}%) | {b['us']} | "
+              f"{c['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | {cp['us']} ({cp['GB/s']}) | "
+              f"{r['kq_over_sq_speed']} | {r['kq_over_copy41_speed']} |", flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
+        return
+    if args.all_configs:
+        if args.gpus != 1:
+            sys.exit(2)
+        all_configs(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
@@ -388,11 +479,21 @@ def main():
         g_o = capture(lambda i: step_kq(i, other), args.steps)
         timed_graph(capture(lambda i: step_kq(i, other), max(1, args.warmup)))
         o_wall, _ = timed_graph(g_o)
+        def step_copy(i):
+            for b in sets[i % nsets]:
+                K.measure_copy41(b["x"], b["q"], stream=torch.cuda.current_stream())
+        g_c = capture(step_copy, args.steps)
+        timed_graph(capture(step_copy, max(1, args.warmup)))
+        c_wall, _ = timed_graph(g_c)
+        copy_bytes = sum(x.size * 2.5 for _, x, _, _ in mats)
         out["comparison"] = {
             "smoothquant_GB/s": round(sq_value, 1),
             "smoothquant_hbm_pct": round(100 * sq_value / HBM_PEAK_GBS, 2),
             "kroquant_over_smoothquant_speed": round(sq_wall / wall, 4),
             ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (o_wall / args.steps) / 1e9, 1),
+            "copy41_ceiling_GB/s": round(copy_bytes / (c_wall / args.steps) / 1e9, 1),
+            "kroquant_over_copy41_speed": round(c_wall / wall, 4),
+            "copy41": "plain streaming copy of the same x (2 B read) into the q buffers (0.5 B written) per element",
         }
 
     if not args.no_cpu:

@@ -59,7 +59,8 @@ _lib.kq_last_hip_error.argtypes = []
 _lib.kq_hip_error_name.argtypes = [_INT]
 _lib.kq_hip_error_name.restype = ctypes.c_char_p
 _lib.kq_set_tuning.argtypes = [_INT, _INT]
-for _name in EXPORTS + ("kq_set_tuning",):
+_lib.kq_measure_copy41.argtypes = [_P, _I64, _P, _P]
+for _name in EXPORTS + ("kq_set_tuning", "kq_measure_copy41"):
     if _name not in ("kq_status_string", "kq_build_info", "kq_hip_error_name"):
         getattr(_lib, _name).restype = _INT
 
@@ -196,9 +197,22 @@ def mx_quantize_f32(x, q=None, s=None, stream=None):
 
 
 def set_tuning(key, value):
-    """Launch-shape knobs for measurements: 0 MFMA tiles/wave, 1 butterfly rows/wave,
-    2 SmoothQuant/fp32 rows/wave (0 = automatic)."""
+    """Launch-shape knobs for measurements: 0 MFMA tiles per workgroup, 1 butterfly
+    rows/wave, 2 SmoothQuant/fp32 rows/wave (0 = automatic); 3 MFMA token-group
+    order (0 automatic, 1 contiguous, 2 interleaved)."""
     _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
+
+
+def measure_copy41(src, dst, stream=None):
+    """Measurement only: the plain 4:1 streaming copy (reads all of src, writes
+    src.nbytes / 4 bytes of dst) used as the benchmark's HBM ceiling."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes // 4:
+        raise ValueError("dst must hold src.nbytes / 4 bytes")
+    _check(_lib.kq_measure_copy41(src.data_ptr(), nbytes, dst.data_ptr(), _stream_handle(stream)),
+           "kq_measure_copy41")
 
 
 # ---------------------------------------------------------------------------

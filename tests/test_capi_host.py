@@ -41,6 +41,17 @@ def test_status_strings():
     assert K.kq_status_string(99) == "unknown status"
 
 
+def test_copy_ceiling_validation():
+    # the benchmark's measurement copy checks its arguments before any HIP call
+    L = K.lib()
+    assert L.kq_measure_copy41(FAKE, 0, FAKE + (1 << 30), None) == K.KQ_OK
+    assert L.kq_measure_copy41(None, 64, FAKE, None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE, 24, FAKE + (1 << 30), None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE + 4, 64, FAKE + (1 << 30), None) == K.KQ_ERR_ALIGN
+    assert L.kq_measure_copy41(FAKE, 64, FAKE + (1 << 30) + 1, None) == K.KQ_ERR_ALIGN
+    assert L.kq_measure_copy41(FAKE, 64, FAKE + 32, None) == K.KQ_ERR_OVERLAP
+
+
 def test_hip_error_detail_without_gpu():
     # a thread that saw no KQ_ERR_HIP return reports hipSuccess; names come from the runtime
     import threading

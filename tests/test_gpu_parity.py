@@ -345,3 +345,17 @@ def test_graph_replay_matches_eager(K):
         assert np.array_equal(q.cpu().numpy(), q_e) and np.array_equal(s.cpu().numpy(), s_e)
         assert np.array_equal(qs.cpu().numpy(), qs_e) and np.array_equal(ss.cpu().numpy(), ss_e)
         _ = (xd.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_copy_ceiling_kernel_output(K):
+    # the benchmark's 4:1 measurement copy: word i of dst = xor of the four words of src chunk i
+    for n16 in (1, 255, 256 * 2048 * 4 + 77):
+        say(f"[copy41] chunks={n16}")
+        rng = np.random.default_rng(n16)
+        src = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
+        s_dev = torch.from_numpy(src.view(np.int32)).cuda()
+        d_dev = torch.zeros(n16, dtype=torch.int32, device="cuda")
+        K.measure_copy41(s_dev, d_dev)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(src.reshape(n16, 4), axis=1)
+        assert np.array_equal(d_dev.cpu().numpy().view(np.uint32), want)
