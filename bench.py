@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 ROTATE_BYTES = 1 << 30
 WORKLOAD = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608)]
-KERNEL_SYMBOL = "kq_mfma_kernel<true>"
+KERNEL_SYMBOL = "kq_mfma_kernel<true"  # both strip-width instances: <true, 8> and <true, 16>
 RAMP_S = 0.3  # untimed replays before the warm-up steps, for the GPU clocks to leave their idle state
 
 
@@ -145,7 +145,7 @@ def summarize_traffic(fetch_dir, write_dir):
                         "write_bytes": round(wr), "hbm_bytes": round(rd + wr), "algorithmic_bytes": round(alg),
                         "ratio": round((rd + wr) / alg, 4)}
         tot += rd + wr
-    blob = {"kernel": KERNEL_SYMBOL, "kernel_source_hash": kernel_source_hash(),
+    blob = {"kernel": "kq_mfma_kernel<true, kW>", "kernel_source_hash": kernel_source_hash(),
             "hbm_bytes_per_launch": round(tot / len(shapes)),
             "algorithmic_bytes_per_launch": round(sum(M * d for _, M, d in WORKLOAD) * BYTES_PER_ELEM / len(WORKLOAD)),
             "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
@@ -440,7 +440,8 @@ def main():
     traffic = load_traffic(src_hash)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": KERNEL_SYMBOL if variant in (0, 1) else "stream_kernel<2>",
+                "kernel": ("kq_mfma_kernel<true, kW> (kW = 8 at d=1152, 16 at d=4608)" if variant in (0, 1)
+                           else "stream_kernel<2>"),
                 "avg_launch_us": round(ev / n_launch * 1e6, 2), "launches_timed": n_launch,
                 "algorithmic_bytes_per_launch": round(step_bytes / len(mats)),
                 "timing": "HIP events on the launch stream around the timed graph of K steps",

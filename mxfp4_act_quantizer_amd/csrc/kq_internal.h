@@ -12,6 +12,7 @@ struct Tuning {
     int bfly_rows_per_wave;   // 0 = automatic
     int stream_rows_per_wave; // 0 = automatic
     int mfma_interleave;      // 0 = automatic, 1 = contiguous token groups, 2 = interleaved groups
+    int mfma_strip;           // 0 = automatic, 8 or 16 blocks per workgroup
 };
 Tuning &tuning();
 

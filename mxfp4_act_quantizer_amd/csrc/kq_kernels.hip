@@ -42,7 +42,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0, 0};
+    static Tuning t{0, 0, 0, 0, 0};
     return t;
 }
 
@@ -103,7 +103,6 @@ __device__ __forceinline__ float dpp_xor2(float v)
 // ---------------------------------------------------------------------------
 // MFMA variant
 // ---------------------------------------------------------------------------
-constexpr int kWavesKQ = 8; // waves per workgroup of the MFMA kernel (one block each)
 constexpr unsigned kXcds = 8; // MI355X: 8 accelerator dies, workgroups dealt round-robin
 constexpr int kTileT = 32; // tokens per wave tile
 
@@ -162,21 +161,32 @@ __device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float 
 }
 
 // ---- workgroup tile of the MFMA variant ----------------------------------
-// A workgroup owns a strip of eight adjacent blocks (256 channels, 512 bytes
-// of a token row) and walks 32-token tiles.  x arrives with contiguous loads
-// (16 bytes per lane, two 512-byte row strips per wave instruction), goes
-// through a padded LDS tile, and is read back in the MFMA operand layout.
-constexpr int kStrip = kWavesKQ * 64;  // bytes of x per token row and workgroup
-constexpr int kXRow = kStrip + 16;     // padded LDS row: 16 consecutive tokens hit distinct banks
-constexpr int kQRow = kWavesKQ * 16 + 16; // padded LDS row of staged codes (128 bytes + pad)
-
-struct __align__(16) WgStage {
-    unsigned char x[2][kTileT][kXRow];      // x tile, double-buffered by tile parity
-    unsigned char q[2][kTileT][kQRow];      // staged codes
-    unsigned char s[2][kTileT][kWavesKQ];   // staged scale bytes
+// A workgroup of kW waves owns a strip of kW adjacent blocks (kW * 32
+// channels, kW * 64 bytes of a token row: 512 bytes for kW = 8, 1 KB for
+// kW = 16) and walks 32-token tiles.  x arrives with contiguous loads (16
+// bytes per lane; each wave instruction covers whole row strips), goes through
+// a padded LDS tile, and is read back in the MFMA operand layout.
+template <int kW>
+struct Strip {
+    static constexpr int kBytes = kW * 64;        // bytes of x per token row and workgroup
+    static constexpr int kXRow = kBytes + 16;     // padded LDS row: 16 consecutive tokens hit distinct banks
+    static constexpr int kQRow = kW * 16 + 16;    // padded LDS row of staged codes
+    static constexpr int kLanesPerRow = kW * 4;   // 16-byte chunks per row strip
+    static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+    static constexpr int kRowsPerWave = kTileT / kW;
+    static_assert(kRowsPerWave == 2 * kRowsPerLoad, "two load instructions per wave and tile");
 };
 
-// Raw x of one tile for one wave: rows 4w + 2k + (lane / 32), 16-byte chunk lane % 32.
+template <int kW>
+struct __align__(16) WgStage {
+    unsigned char x[2][kTileT][Strip<kW>::kXRow]; // x tile, double-buffered by tile parity
+    unsigned char q[2][kTileT][Strip<kW>::kQRow]; // staged codes
+    unsigned char s[2][kTileT][kW];               // staged scale bytes
+};
+
+// Raw x of one tile for one wave: two load instructions, rows
+// kRowsPerWave * wave + kRowsPerLoad * k + lane / kLanesPerRow, 16-byte chunk
+// lane % kLanesPerRow of the row strip.
 struct XIn {
     u32x4 v[2];
 };
@@ -190,35 +200,40 @@ struct XIn {
 // nontemporal (streamed past the caches rather than kept there).
 constexpr int kAuxNT = 2; // buffer instruction cache policy: nontemporal
 
+template <int kW>
 __device__ __forceinline__ void load_x(XIn &in, const uint16_t *__restrict__ x, int64_t M, int d, int bg, int nB,
                                        int64_t r0, bool valid, int wave, int lane)
 {
-    const int chunk = lane & 31;
-    const int blk = bg * kWavesKQ + (chunk >> 2);
+    using S = Strip<kW>;
+    const int chunk = lane % S::kLanesPerRow;
+    const int blk = bg * kW + (chunk >> 2);
     const int64_t rows = valid ? ((M - r0) < kTileT ? (M - r0) : kTileT) : 0;
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void *)(x + r0 * d), 0, (int)(rows * d * 2), kBufWord3);
     const unsigned drop = (unsigned)(blk >= nB) << 31;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int row = 4 * wave + 2 * k + (lane >> 5);
-        const unsigned off = (unsigned)((row * d + bg * (kStrip / 2) + chunk * 8) * 2) | drop;
+        const int row = S::kRowsPerWave * wave + S::kRowsPerLoad * k + lane / S::kLanesPerRow;
+        const unsigned off = (unsigned)((row * d + bg * (S::kBytes / 2) + chunk * 8) * 2) | drop;
         in.v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, kAuxNT));
     }
 }
 
-__device__ __forceinline__ void stage_x(WgStage &st, int par, const XIn &in, int wave, int lane)
+template <int kW>
+__device__ __forceinline__ void stage_x(WgStage<kW> &st, int par, const XIn &in, int wave, int lane)
 {
+    using S = Strip<kW>;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-        *(u32x4 *)&st.x[par][4 * wave + 2 * k + (lane >> 5)][(lane & 31) * 16] = in.v[k];
+        *(u32x4 *)&st.x[par][S::kRowsPerWave * wave + S::kRowsPerLoad * k + lane / S::kLanesPerRow]
+                         [(lane % S::kLanesPerRow) * 16] = in.v[k];
 }
 
 // Transform one tile on the matrix cores; quantize into the staging buffer
 // (or write y directly).  Lane l takes token l%32 and, for MFMA j, channels
 // 16j + 8h .. +7 of block `wave` of the strip (h = l/32).
-template <bool kQuant>
-__device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, int par, const bf16x8 (&A)[3][2],
+template <bool kQuant, int kW>
+__device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<kW> &st, int par, const bf16x8 (&A)[3][2],
                                                int64_t t, int64_t M, int d, int jb, bool jb_valid, int h, int wave,
                                                int tl, float *__restrict__ y)
 {
@@ -266,29 +281,33 @@ __device__ __forceinline__ void transform_tile(const WgStage &stc, WgStage &st, 
 
 // Store one staged tile.  Every wave issues the same two stores, with no
 // branch (so the compiler's memory-counter waits stay exact): 8 code bytes
-// per lane, four tokens per wave (sixteen lanes x 8 bytes = one contiguous
-// 128-byte segment per token row), and one scale byte per lane for waves 0-3
-// (eight consecutive bytes per token).  rq and rs cover the tile's own rows,
-// so rows past M fall outside them; blocks past the row end, the scale lanes
-// of waves 4-7, and every lane when `valid` is false set bit 31 of their
+// per lane, 2*kW lanes per token (one contiguous 16*kW-byte segment per token
+// row), and one scale byte per lane for the first 32*kW lanes of the
+// workgroup (kW consecutive bytes per token).  rq and rs cover the tile's own
+// rows, so rows past M fall outside them; blocks past the row end, the spare
+// scale lanes, and every lane when `valid` is false set bit 31 of their
 // offsets, which the range check drops.
-__device__ __forceinline__ void store_tile(const WgStage &st, int par, bool valid, int bg, int nB, int d, int wave,
+template <int kW>
+__device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool valid, int bg, int nB, int d, int wave,
                                            int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
 {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const int tq = wave * 4 + (lane >> 4);
-    const int c8 = lane & 15;
-    const unsigned drop_q = (unsigned)(bg * kWavesKQ + (c8 >> 1) >= nB || !valid) << 31;
+    constexpr int kLQ = 2 * kW; // lanes per token for the codes
+    const int tq = wave * (64 / kLQ) + lane / kLQ;
+    const int c8 = lane % kLQ;
+    const unsigned drop_q = (unsigned)(bg * kW + (c8 >> 1) >= nB || !valid) << 31;
     const u32x2 v = *(const u32x2 *)&st.q[par][tq][c8 * 8];
-    __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * 128 + c8 * 8) | drop_q), 0, 0);
-    const int ts = (wave & 3) * 8 + (lane >> 3);
-    const int cs = lane & 7;
-    const unsigned drop_s = (unsigned)(bg * kWavesKQ + cs >= nB || !valid || wave >= 4) << 31;
-    __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs, (int)((unsigned)(ts * nB + bg * kWavesKQ + cs) | drop_s),
-                                         0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * kW * 16 + c8 * 8) | drop_q), 0,
+                                          0);
+    const int f = wave * 64 + lane; // flat lane of the workgroup
+    const int ts = (f / kW) % kTileT;
+    const int cs = f % kW;
+    const unsigned drop_s = (unsigned)(bg * kW + cs >= nB || !valid || f >= kTileT * kW) << 31;
+    __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs, (int)((unsigned)(ts * nB + bg * kW + cs) | drop_s), 0,
+                                         0);
 }
 
-// One workgroup: a strip of eight blocks (one per wave for the transform) and
+// One workgroup: a strip of kW blocks (one per wave for the transform) and
 // a sequence of 32-token tiles the eight waves walk together: tiles
 // tile0, tile0 + stride, tile0 + 2*stride, ...  With stride 1 a workgroup owns
 // a contiguous run of rows; with stride = number of token groups the groups
@@ -305,13 +324,13 @@ __device__ __forceinline__ void store_tile(const WgStage &st, int par, bool vali
 #endif
 constexpr int kRing = KQ_RING; // tiles in flight per wave: kRing - 1 ahead of the one being staged
 
-template <bool kQuant>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
+template <bool kQuant, int kW>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
     int interleave)
 {
-    __shared__ WgStage st;
+    __shared__ WgStage<kW> st;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Workgroups go round-robin to the 8 XCDs (blockIdx % 8).  All strips of
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     const int64_t stride = interleave ? nG : 1;
     const int64_t left = (nTiles - tile0 + stride - 1) / stride;
     const int n = (int)(left < tiles_per_wg ? left : tiles_per_wg);
-    const int jb_raw = bg * kWavesKQ + wave;
+    const int jb_raw = bg * kW + wave;
     // waves past the row end take part in loads and barriers and transform block
     // nB-1 (their results are never stored)
     const int jb = jb_raw < nB ? jb_raw : nB - 1;
@@ -357,7 +376,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     // sequence.
 #pragma unroll
     for (int k = 0; k < kRing - 1; ++k) {
-        load_x(ring[k], x, M, d, bg, nB, trow(k), k < n, wave, lane);
+        load_x<kW>(ring[k], x, M, d, bg, nB, trow(k), k < n, wave, lane);
         if (kQuant)
             store_prev(-1);
     }
@@ -366,12 +385,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * 20, lane);
 
     auto step = [&](const XIn &cur, XIn &ld, int kk) {
-        load_x(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
+        load_x<kW>(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
         stage_x(st, kk & 1, cur, wave, lane);
         __syncthreads();
         if (kQuant)
             store_prev(kk - 1);
-        transform_tile<kQuant>(st, st, kk & 1, A, trow(kk) + tl, M, d, jb, jb_raw < nB, h, wave, tl, y);
+        transform_tile<kQuant, kW>(st, st, kk & 1, A, trow(kk) + tl, M, d, jb, jb_raw < nB, h, wave, tl, y);
     };
 
     int it = 0;
@@ -620,30 +639,39 @@ static int num_cus()
     return n;
 }
 
-// Resident workgroups of an MFMA kernel per XCD (occupancy from the runtime).
-static int mfma_wgs_per_xcd(const void *fn)
+// Resident workgroups of an MFMA kernel per XCD (occupancy from the runtime),
+// cached per kernel instance.
+static int mfma_wgs_per_xcd(const void *fn, int threads)
 {
-    static int cached[2] = {0, 0};
-    const int idx = fn == (const void *)kq_mfma_kernel<true> ? 1 : 0;
-    if (!cached[idx]) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * kWavesKQ, 0) != hipSuccess || per_cu <= 0)
-            per_cu = 1;
-        cached[idx] = per_cu * num_cus() / (int)kXcds;
-        if (cached[idx] < 1)
-            cached[idx] = 1;
-    }
-    return cached[idx];
+    static const void *keys[4] = {nullptr, nullptr, nullptr, nullptr};
+    static int vals[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 4; ++i)
+        if (keys[i] == fn)
+            return vals[i];
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    int v = per_cu * num_cus() / (int)kXcds;
+    if (v < 1)
+        v = 1;
+    for (int i = 0; i < 4; ++i)
+        if (!keys[i]) {
+            keys[i] = fn;
+            vals[i] = v;
+            break;
+        }
+    return v;
 }
 
-hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                          uint8_t *s, float *y, hipStream_t stream)
+template <int kW>
+static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                                   uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
 {
     const int nB = (int)(d / 32);
-    const int nBG = (nB + kWavesKQ - 1) / kWavesKQ;
+    const int nBG = (nB + kW - 1) / kW;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const void *fn = y ? (const void *)kq_mfma_kernel<false> : (const void *)kq_mfma_kernel<true>;
-    const int64_t resident = mfma_wgs_per_xcd(fn); // per XCD
+    const void *fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW>;
+    const int64_t resident = mfma_wgs_per_xcd(fn, 64 * kW); // per XCD
     int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
     int interleave = tuning().mfma_interleave == 2 ? 1 : 0;
     if (tpw <= 0) {
@@ -682,9 +710,40 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
         return hipErrorInvalidConfiguration;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
+    int nbg = nBG;
     void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s, (void *)&y, (void *)&nBG, (void *)&tpw, (void *)&interleave};
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kWavesKQ), args_q, 0, stream);
+                      (void *)&s, (void *)&y, (void *)&nbg, (void *)&tpw, (void *)&interleave};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kW), args_q, 0, stream);
+}
+
+hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                          uint8_t *s, float *y, hipStream_t stream)
+{
+    // Strips of 16 blocks (16 waves, 1 KB of each row per workgroup, 85 KB of
+    // LDS, one workgroup per CU) read and write HBM in longer runs than strips
+    // of 8, which pays when the whole launch is one resident round of
+    // interleaved token groups (measured: 8192 x 4608, 18.3 us against 19.8).
+    // Over several rounds the lone workgroup per CU leaves its CU idle
+    // between workgroups, and strips of 8 (two per CU) win.  They are used
+    // only when they divide the row exactly, so no wave idles.
+    const int64_t nB = d / 32;
+    int w = tuning().mfma_strip;
+    if (w != 8 && w != 16) {
+        w = 8;
+        if (nB % 16 == 0 && tuning().mfma_tiles_per_wave <= 0 && tuning().mfma_interleave != 1) {
+            const void *fn16 = y ? (const void *)kq_mfma_kernel<false, 16> : (const void *)kq_mfma_kernel<true, 16>;
+            int64_t gx = mfma_wgs_per_xcd(fn16, 64 * 16) / (nB / 16);
+            if (gx < 1)
+                gx = 1;
+            const int64_t nTiles = (M + kTileT - 1) / kTileT;
+            const int64_t t1 = (nTiles + gx * kXcds - 1) / (gx * kXcds);
+            if (t1 >= 3 && t1 <= 12)
+                w = 16;
+        }
+    }
+    if (w == 16)
+        return launch_kq_mfma_w<16>(x, M, d, factors, nT, q, s, y, stream);
+    return launch_kq_mfma_w<8>(x, M, d, factors, nT, q, s, y, stream);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,

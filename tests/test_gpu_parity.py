@@ -359,3 +359,22 @@ def test_copy_ceiling_kernel_output(K):
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(src.reshape(n16, 4), axis=1)
         assert np.array_equal(d_dev.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("strip", [8, 16])
+@pytest.mark.parametrize("M,d,shared", [(67, 1152, False), (33, 160, True), (130, 4608, False), (5, 544, False)])
+def test_kq_mfma_strip_widths(K, strip, M, d, shared):
+    # both workgroup strip widths of the MFMA quantizer, forced, on ragged shapes
+    # (blocks past the row end inside a strip, rows past M inside a tile)
+    x, _ = I.act_gaussian_outliers(M, d, 7000 + M + d, max(1, d // 100), 50.0)
+    f = I.random_factors(1 if shared else d // 32, 7100 + d)
+    K.set_tuning(4, strip)
+    try:
+        check_kq(K, f"strip={strip} shared={shared}", x, f, VARIANTS["mfma"])
+        y = K.kq_transform_f32(dev_bf16(x), dev_f32(f), variant=VARIANTS["mfma"])
+        torch.cuda.synchronize()
+    finally:
+        K.set_tuning(4, 0)
+    yr, z = O.kq_transform(x, f)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - yr)
+    assert np.all(err <= P.TOL * z + P.TOL_ABS), float((err / (z + 1e-300)).max())
