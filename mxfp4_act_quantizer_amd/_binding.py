@@ -197,9 +197,10 @@ def mx_quantize_f32(x, q=None, s=None, stream=None):
 
 
 def set_tuning(key, value):
-    """Launch-shape knobs for measurements: 0 MFMA tiles per workgroup, 1 butterfly
-    rows/wave, 2 SmoothQuant/fp32 rows/wave (0 = automatic); 3 MFMA token-group
-    order (0 automatic, 1 contiguous, 2 interleaved)."""
+    """Launch-shape knobs for measurements (0 = automatic everywhere): 0 MFMA tiles
+    per workgroup, 1 butterfly rows/wave, 2 SmoothQuant/fp32 rows/wave, 3 MFMA
+    token groups (1 contiguous, 2 interleaved), 4 MFMA strip width (8 or 16
+    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat)."""
     _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
 
 

@@ -196,6 +196,7 @@ int kq_set_tuning(int key, int value)
     case 2: kq::tuning().stream_rows_per_wave = value; return KQ_OK;
     case 3: kq::tuning().mfma_interleave = value; return KQ_OK;
     case 4: kq::tuning().mfma_strip = value; return KQ_OK;
+    case 5: kq::tuning().mfma_order = value; return KQ_OK;
     default: return KQ_ERR_ARG;
     }
 }

@@ -13,6 +13,7 @@ struct Tuning {
     int stream_rows_per_wave; // 0 = automatic
     int mfma_interleave;      // 0 = automatic, 1 = contiguous token groups, 2 = interleaved groups
     int mfma_strip;           // 0 = automatic, 8 or 16 blocks per workgroup
+    int mfma_order;           // 0 = automatic, 1 = XCD-grouped workgroups, 2 = flat order
 };
 Tuning &tuning();
 

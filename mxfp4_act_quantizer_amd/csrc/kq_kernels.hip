@@ -42,7 +42,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0, 0, 0};
+    static Tuning t{0, 0, 0, 0, 0, 0};
     return t;
 }
 
@@ -328,18 +328,28 @@ template <bool kQuant, int kW>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
-    int interleave)
+    int order)
 {
     __shared__ WgStage<kW> st;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Workgroups go round-robin to the 8 XCDs (blockIdx % 8).  All strips of
-    // one token group run on the same XCD, one after another, so partial
-    // lines written into the same q and s rows merge in that L2.
-    const unsigned xcd = blockIdx.x % kXcds;
-    const unsigned slot = blockIdx.x / kXcds;
-    const int bg = (int)(slot % (unsigned)nBG);
-    const int64_t group = (int64_t)(slot / (unsigned)nBG) * kXcds + xcd;
+    // order bit 0: interleaved token groups (else contiguous runs of tiles).
+    // order bit 1: flat workgroup order, strips fastest.  Otherwise XCD-grouped:
+    // workgroups go round-robin to the 8 XCDs (blockIdx % 8) and all strips of
+    // one token group run on the same XCD, one after another, so partial lines
+    // written into the same q and s rows merge in that L2.
+    const bool interleave = order & 1;
+    int bg;
+    int64_t group;
+    if (order & 2) {
+        bg = (int)(blockIdx.x % (unsigned)nBG);
+        group = blockIdx.x / (unsigned)nBG;
+    } else {
+        const unsigned xcd = blockIdx.x % kXcds;
+        const unsigned slot = blockIdx.x / kXcds;
+        bg = (int)(slot % (unsigned)nBG);
+        group = (int64_t)(slot / (unsigned)nBG) * kXcds + xcd;
+    }
     const int nB = d >> 5;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
     const int64_t nG = (nTiles + tiles_per_wg - 1) / tiles_per_wg;
@@ -674,6 +684,25 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
     const int64_t resident = mfma_wgs_per_xcd(fn, 64 * kW); // per XCD
     int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
     int interleave = tuning().mfma_interleave == 2 ? 1 : 0;
+    bool flat = tuning().mfma_order == 2;
+    if (tpw <= 0 && tuning().mfma_order == 0 && tuning().mfma_interleave != 1) {
+        // When XCD-grouped token groups would fill under 80% of the resident
+        // workgroup slots (strips per row not a good divisor of the slots per
+        // XCD: e.g. 35 strips against 64 slots), deal (group, strip) pairs in
+        // flat order instead and cover the rows in one interleaved round
+        // (measured: 2048 x 8960 from 14.6 to 13.0 us, 4608 x 12288 from 30.1
+        // to 28.1 us).
+        const int64_t gx = resident / nBG;
+        const int64_t groups_f = resident * kXcds / nBG;
+        if (groups_f >= 1 && 5 * (gx < 1 ? 1 : gx) * nBG < 4 * resident) {
+            const int64_t t1f = (nTiles + groups_f - 1) / groups_f;
+            if (t1f >= 3 && t1f <= 16) {
+                tpw = (int)t1f;
+                interleave = 1;
+                flat = true;
+            }
+        }
+    }
     if (tpw <= 0) {
         // Launch shape, from measurements on MI355X (HBM time of one launch
         // against tiles per workgroup, for M = 2048..65536 and d = 1152..12288):
@@ -704,15 +733,17 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
             interleave = 1;
     }
     const int64_t nG = (nTiles + tpw - 1) / tpw;
-    const int64_t nGpad = (nG + kXcds - 1) / kXcds * kXcds; // token groups dealt to XCDs in turn
+    // XCD-grouped: token groups dealt to the XCDs in turn, padded to a multiple of 8
+    const int64_t nGpad = flat ? nG : (nG + kXcds - 1) / kXcds * kXcds;
     const int64_t grid = nGpad * nBG;
     if (grid > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
     int nbg = nBG;
+    int order = (interleave ? 1 : 0) | (flat ? 2 : 0);
     void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s, (void *)&y, (void *)&nbg, (void *)&tpw, (void *)&interleave};
+                      (void *)&s, (void *)&y, (void *)&nbg, (void *)&tpw, (void *)&order};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kW), args_q, 0, stream);
 }
 
