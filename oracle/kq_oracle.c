@@ -23,6 +23,14 @@
  *   [LBA]  same record, skeptic_critique.load_bearing_attack (paper Section 3.2,
  *          Eq. 4): T is block diagonal with 32x32 blocks aligned to the
  *          quantizer's 32-element blocks.
+ *   [LU]   same record, referee_report.minor_comments (section 3): each factor
+ *          is G = L U with U = [[a, b], [0, -1/a]], so det G = -1; with
+ *          key_machinery and core_discovery: three scalars per factor, 15 per
+ *          block, Hadamard initialisation, and the K2 kernel that rebuilds
+ *          the block from those 15 scalars on the fly.
+ *   [FWD]  same record, pith_extraction.forward_implications: K2 is compared
+ *          with a fast Walsh-Hadamard transform of the same 32-element
+ *          blocks.
  *   [OCP]  the element (FP4 E2M1) and shared-scale (E8M0) encodings are not
  *          spelled out on the pages, which only name MXFP4; they follow the
  *          public OCP Microscaling Formats (MX) v1.0 specification:
@@ -44,6 +52,11 @@
  *   - SmoothQuant: y = fl32(x * fl32(1/s_c)), one rounding per step.
  *   - The transformed value is rounded once, from its exact (double) value,
  *     to fp32 before quantization; it is never rounded to bf16.
+ *   - LU factor: L = [[1, 0], [c, 1]] (unit lower triangular; the pages give
+ *     only U and "three scalars"), so G = L U = [[a, b], [c a, c b - 1/a]],
+ *     scalars stored as (a, b, c) per factor, factors A1..A5 in order.
+ *   - FWHT comparison: the normalised Sylvester-order Walsh-Hadamard matrix,
+ *     y_c = 2^-2.5 * sum_r x_r (-1)^popcount(r & c), then the same MXFP4.
  */
 #include <math.h>
 #include <stdint.h>
@@ -126,6 +139,56 @@ int oracle_kron_block_inverse(const float *f, double *Kinv)
         }
     }
     return OR_OK;
+}
+
+/* One LU factor [LU]: G = L U with L = [[1, 0], [c, 1]] and
+ * U = [[a, b], [0, -1/a]], in double from the given fp32 scalars. */
+void oracle_lu_factor(const float *abc, double *G)
+{
+    double a = abc[0], b = abc[1], c = abc[2];
+    double u11 = -1.0 / a;
+    /* row 0 of L is (1, 0): row 0 of U; row 1 of L is (c, 1): c * row 0 + row 1 */
+    G[0] = a;
+    G[1] = b;
+    G[2] = c * a;
+    G[3] = c * b + u11;
+}
+
+/* The 32x32 block of an LU-parameterised factor set (15 scalars) [LU], [KM]:
+ * the Kronecker product of the five factors, same index order as
+ * oracle_kron_block. */
+void oracle_lu_kron_block(const float *lu, double *K)
+{
+    double G[20];
+    for (int k = 0; k < 5; ++k)
+        oracle_lu_factor(lu + 3 * k, G + 4 * k);
+    for (int r = 0; r < 32; ++r) {
+        for (int c = 0; c < 32; ++c) {
+            double p = 1.0;
+            for (int k = 0; k < 5; ++k) {
+                int rk = (r >> (4 - k)) & 1;
+                int ck = (c >> (4 - k)) & 1;
+                p *= G[k * 4 + rk * 2 + ck];
+            }
+            K[r * 32 + c] = p;
+        }
+    }
+}
+
+/* Normalised Walsh-Hadamard block [FWD]: H[r][c] = (-1)^popcount(r & c) / sqrt(32). */
+void oracle_wht_block(double *K)
+{
+    double scale = 1.0 / sqrt(32.0);
+    for (int r = 0; r < 32; ++r) {
+        for (int c = 0; c < 32; ++c) {
+            int bits = r & c, par = 0;
+            while (bits) {
+                par ^= bits & 1;
+                bits >>= 1;
+            }
+            K[r * 32 + c] = par ? -scale : scale;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------ */
@@ -233,26 +296,16 @@ static int check_sets(int64_t d, int64_t nT)
 /* z is the magnitude scale the comparison tolerance is relative to.    */
 /* y or z may be NULL.                                                   */
 /* ------------------------------------------------------------------ */
-int oracle_kq_transform(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                        double *y, double *z)
+/* y = x_blk . K_j for every block (row vector times block, [ABS], [KM]),
+ * summed in double; z = |x_blk| . |K_j| (the absolute-value transform that
+ * the tolerance is relative to).  Kall holds nT 32x32 blocks. */
+static void transform_with_blocks(const uint16_t *x, int64_t M, int64_t d, const double *Kall, int64_t nT, double *y,
+                                  double *z)
 {
-    int st = check_shape(M, d);
-    if (st)
-        return st;
-    st = check_sets(d, nT);
-    if (st)
-        return st;
-    if (!x || !factors)
-        return OR_ERR_ARG;
     int64_t nB = d / 32;
-    double *K = (double *)malloc((size_t)nT * 1024 * sizeof(double));
-    if (!K)
-        return OR_ERR_ARG;
-    for (int64_t t = 0; t < nT; ++t)
-        oracle_kron_block(factors + t * 20, K + t * 1024);
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t j = 0; j < nB; ++j) {
-            const double *Kj = K + (nT == 1 ? 0 : j) * 1024;
+            const double *Kj = Kall + (nT == 1 ? 0 : j) * 1024;
             double xb[32];
             for (int r = 0; r < 32; ++r)
                 xb[r] = oracle_bf16_to_double(x[m * d + j * 32 + r]);
@@ -269,32 +322,16 @@ int oracle_kq_transform(const uint16_t *x, int64_t M, int64_t d, const float *fa
             }
         }
     }
-    free(K);
-    return OR_OK;
 }
 
-/* KroQuant quantizer: transform, round once to fp32, MX-quantize each
- * block.  y32 (the fp32 pre-quantization values) may be NULL. */
-int oracle_kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                       uint8_t *q, uint8_t *s, float *y32)
+/* The transformed block rounded once to fp32, then the MX encoding. */
+static void quantize_with_blocks(const uint16_t *x, int64_t M, int64_t d, const double *Kall, int64_t nT, uint8_t *q,
+                                 uint8_t *s, float *y32)
 {
-    int st = check_shape(M, d);
-    if (st)
-        return st;
-    st = check_sets(d, nT);
-    if (st)
-        return st;
-    if (!x || !factors || !q || !s)
-        return OR_ERR_ARG;
     int64_t nB = d / 32;
-    double *K = (double *)malloc((size_t)nT * 1024 * sizeof(double));
-    if (!K)
-        return OR_ERR_ARG;
-    for (int64_t t = 0; t < nT; ++t)
-        oracle_kron_block(factors + t * 20, K + t * 1024);
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t j = 0; j < nB; ++j) {
-            const double *Kj = K + (nT == 1 ? 0 : j) * 1024;
+            const double *Kj = Kall + (nT == 1 ? 0 : j) * 1024;
             double xb[32];
             float yb[32];
             for (int r = 0; r < 32; ++r)
@@ -311,12 +348,101 @@ int oracle_kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *fac
                 memcpy(y32 + m * d + j * 32, yb, sizeof yb);
         }
     }
+}
+
+/* Block matrices of a parameter set: kind 0 = 2x2 factors [nT,5,2,2],
+ * kind 1 = LU scalars [nT,5,3], kind 2 = the Walsh-Hadamard block (nT = 1,
+ * params unused).  Returns NULL when out of memory. */
+static double *make_blocks(const float *params, int64_t nT, int kind)
+{
+    double *K = (double *)malloc((size_t)nT * 1024 * sizeof(double));
+    if (!K)
+        return NULL;
+    for (int64_t t = 0; t < nT; ++t) {
+        if (kind == 0)
+            oracle_kron_block(params + t * 20, K + t * 1024);
+        else if (kind == 1)
+            oracle_lu_kron_block(params + t * 15, K + t * 1024);
+        else
+            oracle_wht_block(K + t * 1024);
+    }
+    return K;
+}
+
+static int transform_entry(const uint16_t *x, int64_t M, int64_t d, const float *params, int64_t nT, int kind,
+                           double *y, double *z)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    st = check_sets(d, nT);
+    if (st)
+        return st;
+    if (!x || (kind != 2 && !params))
+        return OR_ERR_ARG;
+    double *K = make_blocks(params, nT, kind);
+    if (!K)
+        return OR_ERR_ARG;
+    transform_with_blocks(x, M, d, K, nT, y, z);
     free(K);
     return OR_OK;
 }
 
-/* SmoothQuant-style per-channel scaling [ABS]: x_c / s_c, taken as a
- * multiply by the fp32 reciprocal, then the same MX quantizer. */
+static int quantize_entry(const uint16_t *x, int64_t M, int64_t d, const float *params, int64_t nT, int kind,
+                          uint8_t *q, uint8_t *s, float *y32)
+{
+    int st = check_shape(M, d);
+    if (st)
+        return st;
+    st = check_sets(d, nT);
+    if (st)
+        return st;
+    if (!x || (kind != 2 && !params) || !q || !s)
+        return OR_ERR_ARG;
+    double *K = make_blocks(params, nT, kind);
+    if (!K)
+        return OR_ERR_ARG;
+    quantize_with_blocks(x, M, d, K, nT, q, s, y32);
+    free(K);
+    return OR_OK;
+}
+
+int oracle_kq_transform(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                        double *y, double *z)
+{
+    return transform_entry(x, M, d, factors, nT, 0, y, z);
+}
+
+int oracle_kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                       uint8_t *q, uint8_t *s, float *y32)
+{
+    return quantize_entry(x, M, d, factors, nT, 0, q, s, y32);
+}
+
+/* K2 form [LU]: the same quantizer with each factor set given as 15 LU scalars. */
+int oracle_kq_transform_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, double *y,
+                           double *z)
+{
+    return transform_entry(x, M, d, lu, nT, 1, y, z);
+}
+
+int oracle_kq_quantize_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, uint8_t *q,
+                          uint8_t *s, float *y32)
+{
+    return quantize_entry(x, M, d, lu, nT, 1, q, s, y32);
+}
+
+/* FWHT comparison [FWD]: normalised Walsh-Hadamard of every block, then MXFP4. */
+int oracle_fwht_transform(const uint16_t *x, int64_t M, int64_t d, double *y, double *z)
+{
+    return transform_entry(x, M, d, NULL, 1, 2, y, z);
+}
+
+int oracle_fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y32)
+{
+    return quantize_entry(x, M, d, NULL, 1, 2, q, s, y32);
+}
+
 int oracle_sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale,
                        uint8_t *q, uint8_t *s, float *y32)
 {

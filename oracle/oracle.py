@@ -55,6 +55,20 @@ def bind(L):
     L.oracle_sq_quantize.restype = ctypes.c_int
     L.oracle_mx_quantize_f32.argtypes = [P, I64, I64, P, P]
     L.oracle_mx_quantize_f32.restype = ctypes.c_int
+    L.oracle_lu_factor.argtypes = [P, P]
+    L.oracle_lu_factor.restype = None
+    L.oracle_lu_kron_block.argtypes = [P, P]
+    L.oracle_lu_kron_block.restype = None
+    L.oracle_wht_block.argtypes = [P]
+    L.oracle_wht_block.restype = None
+    L.oracle_kq_transform_lu.argtypes = [P, I64, I64, P, I64, P, P]
+    L.oracle_kq_transform_lu.restype = ctypes.c_int
+    L.oracle_kq_quantize_lu.argtypes = [P, I64, I64, P, I64, P, P, P]
+    L.oracle_kq_quantize_lu.restype = ctypes.c_int
+    L.oracle_fwht_transform.argtypes = [P, I64, I64, P, P]
+    L.oracle_fwht_transform.restype = ctypes.c_int
+    L.oracle_fwht_quantize.argtypes = [P, I64, I64, P, P, P]
+    L.oracle_fwht_quantize.restype = ctypes.c_int
     return L
 
 
@@ -169,6 +183,70 @@ def mx_quantize_f32(x_f32):
     s = np.empty((M, d // 32), np.uint8)
     _check(lib().oracle_mx_quantize_f32(_ptr(x), M, d, _ptr(q), _ptr(s)))
     return q, s
+
+
+def lu_factor(abc):
+    """One LU-form factor G = L U (2x2, float64) from its scalars (a, b, c)."""
+    a = _f32(abc).reshape(3)
+    G = np.empty((2, 2), np.float64)
+    lib().oracle_lu_factor(_ptr(a), _ptr(G))
+    return G
+
+
+def lu_kron_block(lu5):
+    """The 32x32 block (float64) of one LU-parameterised factor set [5, 3]."""
+    f = _f32(lu5).reshape(15)
+    K = np.empty((32, 32), np.float64)
+    lib().oracle_lu_kron_block(_ptr(f), _ptr(K))
+    return K
+
+
+def wht_block():
+    K = np.empty((32, 32), np.float64)
+    lib().oracle_wht_block(_ptr(K))
+    return K
+
+
+def kq_transform_lu(x_u16, lu, want_z=True):
+    x = _u16(x_u16)
+    M, d = x.shape
+    f = _f32(lu)
+    nT = f.reshape(-1, 15).shape[0]
+    y = np.empty((M, d), np.float64)
+    z = np.empty((M, d), np.float64) if want_z else None
+    _check(lib().oracle_kq_transform_lu(_ptr(x), M, d, _ptr(f), nT, _ptr(y), _ptr(z)))
+    return (y, z) if want_z else y
+
+
+def kq_quantize_lu(x_u16, lu, want_y32=False):
+    x = _u16(x_u16)
+    M, d = x.shape
+    f = _f32(lu)
+    nT = f.reshape(-1, 15).shape[0]
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+    y32 = np.empty((M, d), np.float32) if want_y32 else None
+    _check(lib().oracle_kq_quantize_lu(_ptr(x), M, d, _ptr(f), nT, _ptr(q), _ptr(s), _ptr(y32)))
+    return (q, s, y32) if want_y32 else (q, s)
+
+
+def fwht_transform(x_u16, want_z=True):
+    x = _u16(x_u16)
+    M, d = x.shape
+    y = np.empty((M, d), np.float64)
+    z = np.empty((M, d), np.float64) if want_z else None
+    _check(lib().oracle_fwht_transform(_ptr(x), M, d, _ptr(y), _ptr(z)))
+    return (y, z) if want_z else y
+
+
+def fwht_quantize(x_u16, want_y32=False):
+    x = _u16(x_u16)
+    M, d = x.shape
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+    y32 = np.empty((M, d), np.float32) if want_y32 else None
+    _check(lib().oracle_fwht_quantize(_ptr(x), M, d, _ptr(q), _ptr(s), _ptr(y32)))
+    return (q, s, y32) if want_y32 else (q, s)
 
 
 def raw_status(fn_name, *args):

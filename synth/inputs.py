@@ -95,6 +95,28 @@ def hadamard_factors(nT=1):
     return np.tile(g, (nT, 5, 1, 1))
 
 
+def hadamard_lu(nT=1):
+    """LU scalars (a, b, c) per factor, [nT, 5, 3] fp32, at the Hadamard
+    initialisation: a = b = fl32(1/sqrt(2)), c = 1 for all five factors."""
+    h = np.float32(1.0 / math.sqrt(2.0))
+    return np.tile(np.array([h, h, 1.0], np.float32), (nT, 5, 1))
+
+
+def random_lu(nT, seed, spread=0.3):
+    """LU scalars (a, b, c) per factor, [nT, 5, 3] fp32: bounded perturbations
+    of the Hadamard initialisation, a = (1/sqrt 2)(1 + spread*U(-1,1)),
+    b = 1/sqrt 2 + spread*U(-1,1), c = 1 + spread*U(-1,1).  |a| stays at or
+    above 0.49, so every factor is well conditioned without any test here."""
+    rng = _rng(seed)
+    h = 1.0 / math.sqrt(2.0)
+    u = rng.uniform(-1.0, 1.0, size=(nT, 5, 3))
+    out = np.empty((nT, 5, 3), np.float32)
+    out[..., 0] = h * (1.0 + spread * u[..., 0])
+    out[..., 1] = h + spread * u[..., 1]
+    out[..., 2] = 1.0 + spread * u[..., 2]
+    return out
+
+
 def integer_unimodular_factors(nT, seed):
     """Integer factors with determinant +-1 (so every inverse is integer too);
     used for exact invariance checks."""

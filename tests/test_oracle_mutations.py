@@ -46,6 +46,22 @@ MUTATIONS = {
         "float recip = 1.0f / scale[j * 32 + c];\n                float xf = (float)oracle_bf16_to_double(x[m * d + j * 32 + c]);\n                yb[c] = xf * recip;",
         "float recip = 1.0f / scale[j * 32 + c];\n                float xf = (float)oracle_bf16_to_double(x[m * d + j * 32 + c]);\n                yb[c] = (float)((double)xf / (double)scale[j * 32 + c]); (void)recip;",
         "test_sq_rounds_once_per_step", {}),
+    "lu_upper_diagonal_sign": (
+        "double u11 = -1.0 / a;",
+        "double u11 = 1.0 / a;",
+        "test_lu_factor_closed_forms", {}),
+    "lu_product_order_u_times_l": (
+        "G[0] = a;\n    G[1] = b;\n    G[2] = c * a;\n    G[3] = c * b + u11;",
+        "G[0] = a + b * c;\n    G[1] = b;\n    G[2] = c * u11;\n    G[3] = u11;",
+        "test_lu_factor_closed_forms", {}),
+    "lu_block_factors_transposed": (
+        "p *= G[k * 4 + rk * 2 + ck];",
+        "p *= G[k * 4 + ck * 2 + rk];",
+        "test_lu_block_is_kron_of_its_factors", {}),
+    "wht_sign_flipped": (
+        "K[r * 32 + c] = par ? -scale : scale;",
+        "K[r * 32 + c] = par ? scale : -scale;",
+        "test_wht_block_is_sylvester_hadamard", {}),
 }
 
 

@@ -275,3 +275,103 @@ def test_shape_rules(oracle_lib):
     assert L.oracle_kq_quantize(P(x), 2, 64, P(f), 3, P(q), P(s), None) == 2  # nT not in {1, d/32}
     assert L.oracle_kq_quantize(P(x), -1, 64, P(f), 1, P(q), P(s), None) == 1
     assert L.oracle_kq_quantize(P(x), 0, 64, P(f), 1, P(q), P(s), None) == 0  # empty is fine
+
+
+# ---------------------------------------------------------------------------
+# K2 form: factors given as LU scalars (pith.science verdict record:
+# referee_report.minor_comments, section 3, U = [[a, b], [0, -1/a]] and
+# det G = -1; key_machinery / core_discovery: three scalars per factor,
+# Hadamard initialisation).  L = [[1, 0], [c, 1]] is this build's reading.
+# ---------------------------------------------------------------------------
+def test_lu_factor_closed_forms(oracle_lib):
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        a, b, c = (rng.uniform(0.3, 2.0) * rng.choice([-1, 1]), rng.normal(), rng.normal())
+        abc = np.array([a, b, c], np.float32)
+        a, b, c = (float(v) for v in abc)
+        G = oracle_lib.lu_factor(abc)
+        # row 0 of L U is row 0 of U
+        assert G[0, 0] == a and G[0, 1] == b
+        # unit-triangular L and det U = a * (-1/a): det G = -1
+        assert abs(np.linalg.det(G) + 1.0) <= 1e-13 * max(1.0, np.abs(G).max() ** 2)
+        # inverse from the closed forms U^-1 = [[1/a, b], [0, -a]], L^-1 = [[1, 0], [-c, 1]]
+        Uinv = np.array([[1.0 / a, b], [0.0, -a]])
+        Linv = np.array([[1.0, 0.0], [-c, 1.0]])
+        assert np.allclose(G @ (Uinv @ Linv), np.eye(2), rtol=0, atol=1e-12 * max(1.0, np.abs(G).max() ** 2))
+
+
+def test_lu_block_is_kron_of_its_factors(oracle_lib):
+    lu = I.random_lu(3, 17)
+    for t in range(3):
+        K = oracle_lib.lu_kron_block(lu[t])
+        ref = np.array([[1.0]])
+        for k in range(5):
+            ref = np.kron(ref, oracle_lib.lu_factor(lu[t, k]))
+        assert np.allclose(K, ref, rtol=1e-15, atol=0)
+        # det(A (x) B) = det(A)^n det(B)^m: five factors of det -1 give det K = +1
+        assert abs(np.linalg.det(K) - 1.0) < 1e-9
+
+
+def test_lu_hadamard_initialisation_gives_wht32(oracle_lib):
+    K = oracle_lib.lu_kron_block(I.hadamard_lu(1)[0])
+    H = scipy.linalg.hadamard(32).astype(np.float64) / math.sqrt(32.0)
+    # exact up to the fp32 rounding of 1/sqrt(2) in a, b (and -1/a)
+    assert np.abs(K - H).max() <= 8 * 2.0 ** -24
+
+
+def test_wht_block_is_sylvester_hadamard(oracle_lib):
+    H = scipy.linalg.hadamard(32).astype(np.float64) / math.sqrt(32.0)
+    assert np.abs(oracle_lib.wht_block() - H).max() <= 1e-16
+
+
+def _fwht_inplace(v):
+    """Iterative fast Walsh-Hadamard transform along the last axis (natural
+    order), unnormalised: the butterfly algorithm, independent of the dense
+    definition the oracle uses."""
+    v = v.copy()
+    n = v.shape[-1]
+    h = 1
+    while h < n:
+        v = v.reshape(v.shape[:-1] + (n // (2 * h), 2, h))
+        a, b = v[..., 0, :].copy(), v[..., 1, :].copy()
+        v[..., 0, :], v[..., 1, :] = a + b, a - b
+        v = v.reshape(v.shape[:-3] + (n,))
+        h *= 2
+    return v
+
+
+def test_fwht_transform_matches_fast_butterfly(oracle_lib):
+    M, d = 13, 96
+    x = I.act_gaussian_outliers(M, d, 41, 2, 50.0)[0]
+    y, z = oracle_lib.fwht_transform(x)
+    X = I.bf16_bits_to_f32(x).astype(np.float64).reshape(M, d // 32, 32)
+    ref = _fwht_inplace(X).reshape(M, d) / math.sqrt(32.0)
+    assert np.all(np.abs(y - ref) <= 1e-14 * z)
+    assert np.allclose(z, np.abs(X).sum(axis=2).repeat(32, axis=1).reshape(M, d) / math.sqrt(32.0), rtol=1e-14)
+
+
+def test_fwht_quantize_is_mx_of_its_transform(oracle_lib):
+    M, d = 7, 64
+    x = I.act_gaussian_outliers(M, d, 43, 2, 50.0)[0]
+    q, s, y32 = oracle_lib.fwht_quantize(x, want_y32=True)
+    y = oracle_lib.fwht_transform(x, want_z=False)
+    assert np.array_equal(y32, y.astype(np.float32))
+    qm, sm = oracle_lib.mx_quantize_f32(y32)
+    assert np.array_equal(q, qm) and np.array_equal(s, sm)
+
+
+def test_kq_lu_matches_factor_path_on_the_same_block(oracle_lib):
+    # the LU path and the 2x2-factor path share the per-block machinery: with
+    # integer scalars every factor entry is exact in fp32, so both paths see the
+    # identical block and must agree bit for bit
+    lu = np.array([[[1, 2, -1], [-1, 0, 1], [1, 1, 1], [1, -1, 2], [-1, 1, 0]]], np.float32)
+    f = np.array([[oracle_lib.lu_factor(lu[0, k]) for k in range(5)]], np.float32)
+    assert np.array_equal(f.astype(np.float64), np.array([[oracle_lib.lu_factor(lu[0, k]) for k in range(5)]]))
+    M, d = 5, 96
+    x = I.act_gaussian_outliers(M, d, 47, 2, 20.0)[0]
+    q1, s1 = oracle_lib.kq_quantize_lu(x, lu)
+    q2, s2 = oracle_lib.kq_quantize(x, f)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    for shape_lu in (np.zeros((2, 5, 3), np.float32), np.zeros((d // 32 + 1, 5, 3), np.float32)):
+        with pytest.raises(Exception):
+            oracle_lib.kq_quantize_lu(x, shape_lu)
