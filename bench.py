@@ -263,12 +263,15 @@ def all_configs(args):
         scale = torch.sqrt(torch.clamp(amax, min=1e-5))
         f_pb = torch.from_numpy(I.random_factors(d // 32, I.factor_seed(name))).to(dev)
         f_sh = torch.from_numpy(I.random_factors(1, I.factor_seed(name))).to(dev)
+        lu_pb = torch.from_numpy(I.random_lu(d // 32, I.factor_seed(name) + 77)).to(dev)
         torch.cuda.synchronize()
         cur = torch.cuda.current_stream
         legs = {
             "kq_mfma_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=1),
             "kq_mfma_shared": lambda b: K.kq_quantize(b["x"], f_sh, b["q"], b["s"], stream=cur(), variant=1),
             "kq_butterfly_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=2),
+            "kq_lu_perblock": lambda b: K.kq_quantize_lu(b["x"], lu_pb, b["q"], b["s"], stream=cur()),
+            "fwht": lambda b: K.fwht_quantize(b["x"], b["q"], b["s"], stream=cur()),
             "smoothquant": lambda b: K.sq_quantize(b["x"], scale, b["q"], b["s"], stream=cur()),
             "copy41": lambda b: K.measure_copy41(b["x"], b["q"], stream=cur()),
         }
@@ -299,19 +302,22 @@ def all_configs(args):
                         "hbm_pct": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "rows/s": round(M / us * 1e6, 1)}
         row["kq_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_perblock"]["us"], 4)
         row["kq_over_copy41_speed"] = round(row["copy41"]["us"] / row["kq_mfma_perblock"]["us"], 4)
+        row["k2_lu_over_fwht_speed"] = round(row["fwht"]["us"] / row["kq_lu_perblock"]["us"], 4)
         table.append(row)
         print(json.dumps(row), flush=True)
         del bufs
         torch.cuda.empty_cache()
     print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ MFMA shared us | KQ butterfly us | "
-          "SmoothQuant us (GB/s, %peak) | copy 4:1 us (GB/s) | KQ/SQ speed | KQ/copy speed |")
-    print("|---|---|---|---|---|---|---|---|---|")
+          "K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | copy 4:1 us (GB/s) | KQ/SQ speed | "
+          "KQ/copy speed | K2/FWHT speed |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in table:
-        a, b, c, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_butterfly_perblock",
-                                           "smoothquant", "copy41"))
+        a, b, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_butterfly_perblock",
+                                                   "kq_lu_perblock", "fwht", "smoothquant", "copy41"))
         print(f"| {r['config']} | {r['M']}x{r['d']} | {a['us']} ({a['GB/s']}, {a['hbm_pct']}%) | {b['us']} | "
-              f"{c['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | {cp['us']} ({cp['GB/s']}) | "
-              f"{r['kq_over_sq_speed']} | {r['kq_over_copy41_speed']} |", flush=True)
+              f"{c['us']} | {l2['us']} | {fw['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | "
+              f"{cp['us']} ({cp['GB/s']}) | {r['kq_over_sq_speed']} | {r['kq_over_copy41_speed']} | "
+              f"{r['k2_lu_over_fwht_speed']} |", flush=True)
 
 
 def main():
@@ -336,6 +342,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     mats = make_inputs()
+    from synth import inputs as I
 
     # ---- device buffers, rotated so one cycle touches >= 1 GB
     step_bytes = sum(x.size * BYTES_PER_ELEM for _, x, _, _ in mats)
@@ -346,7 +353,9 @@ def main():
         for name, x, f, scale in mats:
             M, d = x.shape
             xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            lu = I.random_lu(d // 32, I.factor_seed(name) + 77)
             one.append(dict(x=xd, f=torch.from_numpy(f).to(dev), scale=torch.from_numpy(scale).to(dev),
+                            lu=torch.from_numpy(lu).to(dev),
                             q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
         sets.append(one)
@@ -480,6 +489,20 @@ def main():
         g_o = capture(lambda i: step_kq(i, other), args.steps)
         timed_graph(capture(lambda i: step_kq(i, other), max(1, args.warmup)))
         o_wall, _ = timed_graph(g_o)
+        def step_lu(i):
+            for b in sets[i % nsets]:
+                K.kq_quantize_lu(b["x"], b["lu"], b["q"], b["s"], stream=torch.cuda.current_stream())
+
+        def step_fwht(i):
+            for b in sets[i % nsets]:
+                K.fwht_quantize(b["x"], b["q"], b["s"], stream=torch.cuda.current_stream())
+
+        walls = {}
+        for nm, fn in (("lu", step_lu), ("fwht", step_fwht)):
+            g = capture(fn, args.steps)
+            timed_graph(capture(fn, max(1, args.warmup)))
+            walls[nm], _ = timed_graph(g)
+
         def step_copy(i):
             for b in sets[i % nsets]:
                 K.measure_copy41(b["x"], b["q"], stream=torch.cuda.current_stream())
@@ -492,6 +515,11 @@ def main():
             "smoothquant_hbm_pct": round(100 * sq_value / HBM_PEAK_GBS, 2),
             "kroquant_over_smoothquant_speed": round(sq_wall / wall, 4),
             ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (o_wall / args.steps) / 1e9, 1),
+            "k2_lu_GB/s": round(step_bytes / (walls["lu"] / args.steps) / 1e9, 1),
+            "fwht_GB/s": round(step_bytes / (walls["fwht"] / args.steps) / 1e9, 1),
+            "k2_lu_over_fwht_speed": round(walls["fwht"] / walls["lu"], 4),
+            "k2": "factor sets as 15 LU scalars per block, rebuilt in the kernel (kq_quantize_lu); "
+                  "fwht: fixed normalised Walsh-Hadamard-32 + MXFP4 (fwht_quantize)",
             "copy41_ceiling_GB/s": round(copy_bytes / (c_wall / args.steps) / 1e9, 1),
             "kroquant_over_copy41_speed": round(c_wall / wall, 4),
             "copy41": "plain streaming copy of the same x (2 B read) into the q buffers (0.5 B written) per element",

@@ -110,6 +110,46 @@ int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uin
  */
 int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream);
 
+/*
+ * K2 form: each factor set given as 15 LU scalars and rebuilt inside the
+ * kernel (pith.science record: key_machinery and core_discovery - three
+ * scalars per factor through a unit-determinant LU form, 15 per block, and a
+ * kernel that rebuilds the block from them on the fly; referee_report.
+ * minor_comments on section 3 - U = [[a, b], [0, -1/a]], det G = -1).
+ * Reading of the unstated L: L = [[1, 0], [c, 1]], so
+ * G = L U = [[a, b], [c a, c b - 1/a]] (a = b = 1/sqrt(2), c = 1 gives the
+ * normalised 2x2 Hadamard factor).
+ *   lu  dev, float32 [nT, 5, 3]: lu[t][k] = (a, b, c) of factor A_{k+1} of set t,
+ *       nT = 1 or d/32, 4-byte aligned
+ * In the kernel each factor is formed in fp32 exactly as kq_lu_factors forms
+ * it on the host, then the block is transformed on the matrix cores as in
+ * kq_quantize (KQ_VARIANT_MFMA).  a = 0 or non-finite scalars make the
+ * block's values non-finite: such blocks encode as scale 0xFF, codes 0.
+ * Otherwise the same contract as kq_quantize.
+ */
+int kq_quantize_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, uint8_t *q, uint8_t *s,
+                   void *stream);
+
+/* The transformed values of kq_quantize_lu (fp32), for inspection.
+ *   y  dev, float32 [M, d], 16-byte aligned */
+int kq_transform_lu_f32(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, float *y,
+                        void *stream);
+
+/*
+ * fwht_quantize: the fixed-transform comparison kernel (pith.science record,
+ * pith_extraction.forward_implications: the K2 kernel is compared with a fast
+ * Walsh-Hadamard transform of the same 32-element blocks).  For every block,
+ * y_c = (1/sqrt 32) sum_r x_r (-1)^popcount(r & c) (Sylvester order, five
+ * butterfly stages of +-1 in fp32, then one multiply by fl32(1/sqrt 32)),
+ * then the same MXFP4 quantization.  Same contract as sq_quantize without a
+ * parameter array.
+ */
+int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream);
+
+/* The transformed values of fwht_quantize (fp32), for inspection.
+ *   y  dev, float32 [M, d], 16-byte aligned */
+int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *stream);
+
 /* ---------------- host helpers for the offline weight side --------------- */
 /* All pointers are host memory; the calls are synchronous and touch no GPU.  */
 
@@ -130,6 +170,13 @@ int kq_block_inverse(const float *factors, int64_t nT, float *Kinv);
  * row n and block j, W_out[n, 32j:32j+32] = W[n, 32j:32j+32] . (K_j^-1)^T.
  * Accumulates in double, rounds once to float32.  W_out may equal W. */
 int kq_fold_weight(const float *W, int64_t N, int64_t d, const float *factors, int64_t nT, float *W_out);
+
+/* The 2x2 factors [nT, 5, 2, 2] of LU-parameterised sets [nT, 5, 3], formed
+ * in fp32 exactly as kq_quantize_lu forms them in the kernel: g00 = a,
+ * g01 = b, g10 = fl32(c a), g11 = fma(c, b, -fl32(1/a)).  The result can be
+ * passed to kq_fold_weight, kq_factor_inverse or kq_quantize.  Returns
+ * KQ_ERR_SINGULAR if some a is 0 or a scalar or result is not finite. */
+int kq_lu_factors(const float *lu, int64_t nT, float *factors);
 
 /* Text for a status code (static storage). */
 const char *kq_status_string(int status);

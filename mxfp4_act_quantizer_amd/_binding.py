@@ -30,6 +30,7 @@ KQ_VARIANT_BUTTERFLY = 2
 EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
+    "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors",
     "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
 )
 
@@ -47,6 +48,11 @@ _lib.kq_quantize_ex.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _INT, _P]
 _lib.kq_transform_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _INT, _P]
 _lib.sq_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
 _lib.mx_quantize_f32.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.kq_quantize_lu.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
+_lib.kq_transform_lu_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+_lib.fwht_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.fwht_transform_f32.argtypes = [_P, _I64, _I64, _P, _P]
+_lib.kq_lu_factors.argtypes = [_P, _I64, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
 _lib.kq_block_matrix.argtypes = [_P, _I64, _P]
 _lib.kq_block_inverse.argtypes = [_P, _I64, _P]
@@ -174,6 +180,57 @@ def kq_transform_f32(x, factors, y=None, stream=None, variant=KQ_VARIANT_AUTO):
     return y
 
 
+def _nT_lu(lu):
+    n = lu.numel()
+    if n % 15:
+        raise ValueError("lu must hold [nT, 5, 3] float32 values")
+    return n // 15
+
+
+def kq_quantize_lu(x, lu, q=None, s=None, stream=None):
+    """K2 form of the KroQuant quantizer: factor sets as LU scalars [nT, 5, 3]."""
+    torch = _torch()
+    M, d = _md(x)
+    q, s = _outputs(x, M, d, q, s)
+    st = _lib.kq_quantize_lu(_dev(x, _bf16_types(), "x"), M, d, _dev(lu, (torch.float32,), "lu"), _nT_lu(lu),
+                             _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    _check(st, "kq_quantize_lu")
+    return q, s
+
+
+def kq_transform_lu_f32(x, lu, y=None, stream=None):
+    torch = _torch()
+    M, d = _md(x)
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    st = _lib.kq_transform_lu_f32(_dev(x, _bf16_types(), "x"), M, d, _dev(lu, (torch.float32,), "lu"), _nT_lu(lu),
+                                  _dev(y, (torch.float32,), "y"), _stream_handle(stream))
+    _check(st, "kq_transform_lu_f32")
+    return y
+
+
+def fwht_quantize(x, q=None, s=None, stream=None):
+    """Walsh-Hadamard-32 comparison quantizer (fixed transform, then MXFP4)."""
+    torch = _torch()
+    M, d = _md(x)
+    q, s = _outputs(x, M, d, q, s)
+    st = _lib.fwht_quantize(_dev(x, _bf16_types(), "x"), M, d, _dev(q, (torch.uint8,), "q"),
+                            _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    _check(st, "fwht_quantize")
+    return q, s
+
+
+def fwht_transform_f32(x, y=None, stream=None):
+    torch = _torch()
+    M, d = _md(x)
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    st = _lib.fwht_transform_f32(_dev(x, _bf16_types(), "x"), M, d, _dev(y, (torch.float32,), "y"),
+                                 _stream_handle(stream))
+    _check(st, "fwht_transform_f32")
+    return y
+
+
 def sq_quantize(x, scale, q=None, s=None, stream=None):
     """SmoothQuant comparison quantizer: y = x * fl32(1/scale_c), then MXFP4."""
     torch = _torch()
@@ -222,6 +279,17 @@ def measure_copy41(src, dst, stream=None):
 def _host_f32(a, name):
     a = np.ascontiguousarray(a, dtype=np.float32)
     return a
+
+
+def kq_lu_factors(lu):
+    """2x2 factors [nT, 5, 2, 2] of LU scalars [nT, 5, 3], in the kernel's fp32 arithmetic."""
+    f = _host_f32(lu, "lu")
+    if f.size % 15:
+        raise ValueError("lu must hold [nT, 5, 3] float32 values")
+    nT = f.size // 15
+    out = np.empty((nT, 5, 2, 2), np.float32)
+    _check(_lib.kq_lu_factors(f.ctypes.data, nT, out.ctypes.data), "kq_lu_factors")
+    return out
 
 
 def kq_factor_inverse(factors):

@@ -100,7 +100,7 @@ int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors
     hipStream_t hs = (hipStream_t)stream;
     if (variant == KQ_VARIANT_BUTTERFLY)
         return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, q, s, nullptr, hs));
-    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, q, s, nullptr, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, q, s, nullptr, 0, hs));
 }
 
 int kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
@@ -133,7 +133,75 @@ int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *facto
     hipStream_t hs = (hipStream_t)stream;
     if (variant == KQ_VARIANT_BUTTERFLY)
         return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, nullptr, nullptr, y, hs));
-    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, nullptr, nullptr, y, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, nullptr, nullptr, y, 0, hs));
+}
+
+int kq_quantize_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, uint8_t *q, uint8_t *s,
+                   void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if ((st = check_sets(d, nT)))
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    const int64_t xb = M * d * 2;
+    if ((st = check_quant_io(x, xb, q, s, M, d)))
+        return st;
+    if ((st = check_param(lu, nT * 15, x, xb, q, M * (d / 2), s, M * (d / 32))))
+        return st;
+    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, q, s, nullptr, 1, (hipStream_t)stream));
+}
+
+int kq_transform_lu_f32(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, float *y,
+                        void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if ((st = check_sets(d, nT)))
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if (!x || !y)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t xb = M * d * 2, yb = M * d * 4;
+    if (overlap(x, xb, y, yb))
+        return KQ_ERR_OVERLAP;
+    if ((st = check_param(lu, nT * 15, x, xb, y, yb, nullptr, 0)))
+        return st;
+    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, nullptr, nullptr, y, 1, (hipStream_t)stream));
+}
+
+int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if ((st = check_quant_io(x, M * d * 2, q, s, M, d)))
+        return st;
+    return hip_status(kq::launch_fwht(x, M, d, q, s, nullptr, (hipStream_t)stream));
+}
+
+int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if (!x || !y)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return KQ_ERR_ALIGN;
+    if (overlap(x, M * d * 2, y, M * d * 4))
+        return KQ_ERR_OVERLAP;
+    return hip_status(kq::launch_fwht(x, M, d, nullptr, nullptr, y, (hipStream_t)stream));
 }
 
 int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s, void *stream)

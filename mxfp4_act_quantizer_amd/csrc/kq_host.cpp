@@ -80,6 +80,31 @@ int kq_factor_inverse(const float *factors, int64_t nT, float *inv)
     return KQ_OK;
 }
 
+int kq_lu_factors(const float *lu, int64_t nT, float *factors)
+{
+    if (!lu || !factors || nT <= 0)
+        return KQ_ERR_ARG;
+    for (int64_t t = 0; t < nT; ++t) {
+        for (int k = 0; k < 5; ++k) {
+            const float a = lu[t * 15 + 3 * k], b = lu[t * 15 + 3 * k + 1], c = lu[t * 15 + 3 * k + 2];
+            if (!(a != 0.0f) || !std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+                return KQ_ERR_SINGULAR;
+            // the kernel's fp32 sequence: correctly rounded 1/a, c*a, fma(c, b, -1/a)
+            const float r = 1.0f / a;
+            const float g10 = c * a;
+            const float g11 = std::fmaf(c, b, -r);
+            if (!std::isfinite(r) || !std::isfinite(g10) || !std::isfinite(g11))
+                return KQ_ERR_SINGULAR;
+            float *g = factors + t * 20 + 4 * k;
+            g[0] = a;
+            g[1] = b;
+            g[2] = g10;
+            g[3] = g11;
+        }
+    }
+    return KQ_OK;
+}
+
 int kq_block_matrix(const float *factors, int64_t nT, float *K)
 {
     if (!factors || !K || nT <= 0)

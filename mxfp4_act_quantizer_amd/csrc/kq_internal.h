@@ -17,13 +17,16 @@ struct Tuning {
 };
 Tuning &tuning();
 
+// factors: [nT,5,2,2] 2x2 factors (lu = 0) or [nT,5,3] LU scalars (lu = 1)
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                          uint8_t *s, float *y, hipStream_t stream);
+                          uint8_t *s, float *y, int lu, hipStream_t stream);
 hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
                                uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
 hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
                      hipStream_t stream);
 hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream);
+// normalised Walsh-Hadamard-32 comparison: quantize (y null) or export y
+hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
 
 // Largest row count / width the launchers accept (grid and 32-bit lane math).
 constexpr int64_t kMaxD = (int64_t)1 << 20;

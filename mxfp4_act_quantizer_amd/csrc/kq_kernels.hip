@@ -123,13 +123,30 @@ __device__ __forceinline__ float bf16_val(unsigned short h) { return __uint_as_f
 // Each entry K = A1[r4][c4] A2[r3][c3] A3[r2][c2] A4[r1][c1] A5[r0][c0] is
 // formed in fp32 and split exactly into hi + mid + lo bf16 terms (each step
 // keeps the next 8 significant bits, so the third remainder fits bf16).
-__device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lane)
+//
+// With lu set, F holds the set as 15 LU scalars (a, b, c) per factor and each
+// factor is rebuilt first as G = [[1, 0], [c, 1]] [[a, b], [0, -1/a]] =
+// [[a, b], [c a, c b - 1/a]], in fp32 with the operations kq_lu_factors
+// performs on the host (correctly rounded 1/a, c*a, fma(c, b, -1/a)).
+__device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lu, int lane)
 {
     // the set is the same for the whole wave: scalar loads, then per-lane selects
     float f[20];
+    if (lu) {
 #pragma unroll
-    for (int i = 0; i < 20; ++i)
-        f[i] = F[i];
+        for (int k = 0; k < 5; ++k) {
+            const float a = F[3 * k], b = F[3 * k + 1], c = F[3 * k + 2];
+            const float r = __fdiv_rn(1.0f, a);
+            f[4 * k] = a;
+            f[4 * k + 1] = b;
+            f[4 * k + 2] = c * a;
+            f[4 * k + 3] = __builtin_fmaf(c, b, -r);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 20; ++i)
+            f[i] = F[i];
+    }
     const int h = lane >> 5;
     const int i = lane & 31;
     const int c = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
@@ -328,7 +345,7 @@ template <bool kQuant, int kW>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
-    int order)
+    int order, int lu)
 {
     __shared__ WgStage<kW> st;
     const int lane = threadIdx.x & 63;
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
     }
 
     bf16x8 A[3][2];
-    build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * 20, lane);
+    build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * (lu ? 15 : 20), lu, lane);
 
     auto step = [&](const XIn &cur, XIn &ld, int kk) {
         load_x<kW>(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
@@ -424,7 +441,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
 // Streaming variants: one lane per 8 channels, a wave covers 512 channels
 // (16 blocks) of U rows at a time and walks a run of rows.
 // ---------------------------------------------------------------------------
-enum StreamMode { kSQ = 0, kMXF32 = 1, kBflyQ = 2, kBflyT = 3 };
+enum StreamMode { kSQ = 0, kMXF32 = 1, kBflyQ = 2, kBflyT = 3, kFwhtQ = 4, kFwhtT = 5 };
 
 // Per-lane constants of the butterfly for its block's factor set.
 // The lane's channels are 8*qp + e of the block (qp = lane%4): index bits 4
@@ -470,6 +487,23 @@ __device__ __forceinline__ void bfly_inlane(float (&v)[8], const float (&A)[4])
         }
     }
 }
+
+// Unnormalised Walsh-Hadamard stage on an in-lane index bit (stride ST):
+// pairs (u at bit 0, w at bit 1) become (u + w, u - w).
+template <int ST>
+__device__ __forceinline__ void wht_inlane(float (&v)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i & ST)
+            continue;
+        const float u = v[i], w = v[i + ST];
+        v[i] = u + w;
+        v[i + ST] = u - w;
+    }
+}
+
+constexpr float kInvSqrt32 = 0.17677669529663688f; // fl32(1 / sqrt(32))
 
 constexpr int kStreamU = 4; // rows per pipeline stage of the streaming kernels
 
@@ -540,8 +574,28 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
             bfly_inlane<2, false>(v, B.a4);
             bfly_inlane<1, true>(v, B.a5);
         }
+        if constexpr (kMode == kFwhtQ || kMode == kFwhtT) {
+            // Walsh-Hadamard comparison transform: the same five stages with
+            // fixed +-1 coefficients.  Cross-lane bits 4 and 3: a lane at bit
+            // value b keeps own + other (b = 0) or other - own (b = 1); then the
+            // in-lane bits 2, 1, 0; then one multiply by fl32(1/sqrt 32),
+            // started from +0 so no result is -0.
+            const float s4 = (qp & 2) ? -1.0f : 1.0f, s3 = (qp & 1) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_fmaf(s4, v[i], dpp_xor2(v[i]));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_fmaf(s3, v[i], dpp_xor1(v[i]));
+            wht_inlane<4>(v);
+            wht_inlane<2>(v);
+            wht_inlane<1>(v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_fmaf(v[i], kInvSqrt32, 0.0f);
+        }
         const int64_t mm = m + u;
-        if constexpr (kMode == kBflyT) {
+        if constexpr (kMode == kBflyT || kMode == kFwhtT) {
             if (mm < m1 && cok) {
                 f32x4 *o = (f32x4 *)(y + mm * d + (int64_t)oct * 8);
                 o[0] = f32x4{v[0], v[1], v[2], v[3]};
@@ -603,7 +657,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
 
     RowsIn<kMode> bufA, bufB;
     load_rows<kMode>(bufA, rx, 0, d, lane_off);
-    const bool quant = (kMode != kBflyT);
+    const bool quant = (kMode != kBflyT && kMode != kFwhtT);
     __amdgpu_buffer_rsrc_t rq = out_buffer(quant ? q + m0 * (d >> 1) : nullptr, quant ? (m1 - m0) * (d >> 1) : 0);
     __amdgpu_buffer_rsrc_t rs = out_buffer(quant ? s + m0 * nB : nullptr, quant ? (m1 - m0) * nB : 0);
 
@@ -675,7 +729,7 @@ static int mfma_wgs_per_xcd(const void *fn, int threads)
 
 template <int kW>
 static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                                   uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
+                                   uint8_t *q, uint8_t *s, float *y, int lu, hipStream_t stream)
 {
     const int nB = (int)(d / 32);
     const int nBG = (nB + kW - 1) / kW;
@@ -742,13 +796,13 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
     int per_block = nT > 1 ? 1 : 0;
     int nbg = nBG;
     int order = (interleave ? 1 : 0) | (flat ? 2 : 0);
-    void *args_q[] = {(void *)&x, (void *)&M, (void *)&di, (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s, (void *)&y, (void *)&nbg, (void *)&tpw, (void *)&order};
+    void *args_q[] = {(void *)&x,   (void *)&M,   (void *)&di,  (void *)&factors, (void *)&per_block, (void *)&q,
+                      (void *)&s,   (void *)&y,   (void *)&nbg, (void *)&tpw,     (void *)&order,     (void *)&lu};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kW), args_q, 0, stream);
 }
 
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                          uint8_t *s, float *y, hipStream_t stream)
+                          uint8_t *s, float *y, int lu, hipStream_t stream)
 {
     // Strips of 16 blocks (16 waves, 1 KB of each row per workgroup, 85 KB of
     // LDS, one workgroup per CU) read and write HBM in longer runs than strips
@@ -773,8 +827,8 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
         }
     }
     if (w == 16)
-        return launch_kq_mfma_w<16>(x, M, d, factors, nT, q, s, y, stream);
-    return launch_kq_mfma_w<8>(x, M, d, factors, nT, q, s, y, stream);
+        return launch_kq_mfma_w<16>(x, M, d, factors, nT, q, s, y, lu, stream);
+    return launch_kq_mfma_w<8>(x, M, d, factors, nT, q, s, y, lu, stream);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,
@@ -799,7 +853,9 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
     case kSQ: fn = (const void *)stream_kernel<kSQ>; break;
     case kMXF32: fn = (const void *)stream_kernel<kMXF32>; break;
     case kBflyQ: fn = (const void *)stream_kernel<kBflyQ>; break;
-    default: fn = (const void *)stream_kernel<kBflyT>; break;
+    case kBflyT: fn = (const void *)stream_kernel<kBflyT>; break;
+    case kFwhtQ: fn = (const void *)stream_kernel<kFwhtQ>; break;
+    default: fn = (const void *)stream_kernel<kFwhtT>; break;
     }
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, stream);
 }
@@ -820,6 +876,11 @@ hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale
 hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream)
 {
     return launch_stream(kMXF32, x, M, d, nullptr, 0, q, s, nullptr, tuning().stream_rows_per_wave, stream);
+}
+
+hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
+{
+    return launch_stream(y ? kFwhtT : kFwhtQ, x, M, d, nullptr, 0, q, s, y, tuning().stream_rows_per_wave, stream);
 }
 
 } // namespace kq

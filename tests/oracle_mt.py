@@ -56,3 +56,60 @@ def sq_quantize(x, scale):
     with ThreadPoolExecutor(THREADS) as ex:
         list(ex.map(job, _chunks(M)))
     return q, s
+
+
+def _run(M, fn):
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(fn, _chunks(M)))
+
+
+def kq_quantize_lu(x, lu):
+    M, d = x.shape
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+    y32 = np.empty((M, d), np.float32)
+
+    def job(rr):
+        a, b = rr
+        q[a:b], s[a:b], y32[a:b] = O.kq_quantize_lu(np.ascontiguousarray(x[a:b]), lu, want_y32=True)
+
+    _run(M, job)
+    return q, s, y32
+
+
+def kq_z_lu(x, lu):
+    M, d = x.shape
+    z = np.empty((M, d), np.float64)
+
+    def job(rr):
+        a, b = rr
+        z[a:b] = O.kq_transform_lu(np.ascontiguousarray(x[a:b]), lu)[1]
+
+    _run(M, job)
+    return z
+
+
+def fwht_quantize(x):
+    M, d = x.shape
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 32), np.uint8)
+    y32 = np.empty((M, d), np.float32)
+
+    def job(rr):
+        a, b = rr
+        q[a:b], s[a:b], y32[a:b] = O.fwht_quantize(np.ascontiguousarray(x[a:b]), want_y32=True)
+
+    _run(M, job)
+    return q, s, y32
+
+
+def fwht_z(x):
+    M, d = x.shape
+    z = np.empty((M, d), np.float64)
+
+    def job(rr):
+        a, b = rr
+        z[a:b] = O.fwht_transform(np.ascontiguousarray(x[a:b]))[1]
+
+    _run(M, job)
+    return z

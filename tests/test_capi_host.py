@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "kroquant.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kq_\w+|sq_\w+|mx_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kq_\w+|sq_\w+|mx_\w+|fwht_\w+)\s*\(", src, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -202,3 +202,76 @@ def test_fold_weight_shape_errors():
     assert L.kq_fold_weight(W.ctypes.data, 2, 64, f.ctypes.data, 3, W.ctypes.data) == K.KQ_ERR_SHAPE
     assert L.kq_fold_weight(W.ctypes.data, 2, 60, f.ctypes.data, 1, W.ctypes.data) == K.KQ_ERR_SHAPE
     assert L.kq_fold_weight(None, 2, 64, f.ctypes.data, 1, W.ctypes.data) == K.KQ_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# K2 (LU scalars) and Walsh-Hadamard comparison entry points
+# ---------------------------------------------------------------------------
+def test_lu_and_fwht_validation():
+    q, s, f, x = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    y = FAKE + (4 << 30)
+    assert raw("kq_quantize_lu", x, 4, 48, f, 1, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_quantize_lu", x, 4, 64, f, 3, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_quantize_lu", x, 4, 64, None, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize_lu", x, 4, 64, f + 2, 1, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize_lu", x, 4, 64, q + 32, 1, q, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_quantize_lu", x, 0, 64, None, 1, None, None, None) == K.KQ_OK
+    assert raw("kq_transform_lu_f32", x, 4, 64, f, 2, None, None) == K.KQ_ERR_ARG
+    assert raw("kq_transform_lu_f32", x, 4, 64, f, 2, y + 4, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_transform_lu_f32", x, 4, 64, f, 2, x + 64, None) == K.KQ_ERR_OVERLAP
+    assert raw("fwht_quantize", x, 4, 40, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("fwht_quantize", None, 4, 64, q, s, None) == K.KQ_ERR_ARG
+    assert raw("fwht_quantize", x + 2, 4, 64, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("fwht_quantize", x, 4, 64, x + 32, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("fwht_quantize", x, 0, 64, None, None, None) == K.KQ_OK
+    assert raw("fwht_transform_f32", x, 4, 64, None, None) == K.KQ_ERR_ARG
+    assert raw("fwht_transform_f32", x, 4, 64, y + 8, None) == K.KQ_ERR_ALIGN
+
+
+def test_lu_factors_match_oracle_factor(oracle_lib):
+    lu = np.concatenate([I.random_lu(6, 23), I.hadamard_lu(1),
+                         np.array([[[1, 2, -1], [-1, 0, 1], [1, 1, 1], [1, -1, 2], [-1, 1, 0]]], np.float32)])
+    g = K.kq_lu_factors(lu)
+    assert g.shape == (lu.shape[0], 5, 2, 2) and g.dtype == np.float32
+    for t in range(lu.shape[0]):
+        for k in range(5):
+            a, b, c = (np.float32(v) for v in lu[t, k])
+            G = oracle_lib.lu_factor(lu[t, k])
+            # entries the fp32 sequence forms exactly: a, b and fl32(c a)
+            assert g[t, k, 0, 0] == a and g[t, k, 0, 1] == b
+            assert g[t, k, 1, 0] == np.float32(G[1, 0])
+            # c b - fl32(1/a), rounded once: within half an fp32 ulp of the double value
+            r = np.float32(1.0) / a
+            exact = float(c) * float(b) - float(r)
+            assert abs(float(g[t, k, 1, 1]) - exact) <= 0.5 * float(np.spacing(np.float32(abs(exact)))) + 1e-300
+            # and close to the oracle's double-precision factor (differs only by fl32(1/a))
+            assert abs(float(g[t, k, 1, 1]) - G[1, 1]) <= 2 ** -22 * max(1.0, abs(G[1, 1]))
+    # the Hadamard initialisation gives the fp32 Hadamard factor up to one ulp of -1/sqrt 2
+    h = K.kq_lu_factors(I.hadamard_lu(1))[0]
+    assert np.abs(h - I.hadamard_factors(1)[0]).max() <= np.spacing(np.float32(0.70710677))
+
+
+def test_lu_factors_singular():
+    bad = I.hadamard_lu(2)
+    bad[1, 3, 0] = 0.0
+    with pytest.raises(K.KQError) as e:
+        K.kq_lu_factors(bad)
+    assert e.value.status == K.KQ_ERR_SINGULAR
+    bad[1, 3, 0] = np.inf
+    with pytest.raises(K.KQError):
+        K.kq_lu_factors(bad)
+
+
+def test_fold_weight_through_lu_factors(oracle_lib):
+    # K2 users fold their weights with the factors kq_lu_factors forms
+    rng = np.random.default_rng(29)
+    M, d, N = 4, 96, 5
+    lu = I.random_lu(d // 32, 31)
+    f = K.kq_lu_factors(lu)
+    x = I.act_gaussian_outliers(M, d, 37, 1, 10.0)[0]
+    W = rng.standard_normal((N, d)).astype(np.float32)
+    Wf = K.kq_fold_weight(W, f)
+    y = oracle_lib.kq_transform(x, f, want_z=False)
+    ref = I.bf16_bits_to_f32(x).astype(np.float64) @ W.astype(np.float64).T
+    got = y @ Wf.astype(np.float64).T
+    assert np.allclose(got, ref, rtol=0, atol=1e-4 * np.abs(ref).max())

@@ -135,3 +135,27 @@ def test_sweep_identity_hadamard(K, name):
     assert res["ok"], res
     del xd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["dit_4608", "mid_8960", "dbl_12288"])
+def test_kq_lu_and_fwht_full_config_all_rows(K, name):
+    # K2 form with per-block LU scalars, and the Walsh-Hadamard comparison, on every row
+    x = I.make_activation(name)
+    M, d = x.shape
+    lu = I.random_lu(d // 32, I.factor_seed(name) + 77)
+    xd = to_dev(x)
+    say(f"[full kq_lu {name}] M={M} d={d}")
+    q, s = K.kq_quantize_lu(xd, torch.from_numpy(lu).cuda())
+    qf, sf = K.fwht_quantize(xd)
+    torch.cuda.synchronize()
+    qr, sr, y32 = OM.kq_quantize_lu(x, lu)
+    ef, bf = P.boundary_flags(OM.kq_z_lu(x, lu), y32)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)
+    say(f"    {res}")
+    assert res["ok"], res
+    say(f"[full fwht {name}] M={M} d={d}")
+    qr, sr, y32 = OM.fwht_quantize(x)
+    ef, bf = P.boundary_flags(OM.fwht_z(x), y32)
+    res = P.compare(qf.cpu().numpy(), sf.cpu().numpy(), qr, sr, ef, bf)
+    say(f"    {res}")
+    assert res["ok"], res

@@ -378,3 +378,133 @@ def test_kq_mfma_strip_widths(K, strip, M, d, shared):
     yr, z = O.kq_transform(x, f)
     err = np.abs(y.cpu().numpy().astype(np.float64) - yr)
     assert np.all(err <= P.TOL * z + P.TOL_ABS), float((err / (z + 1e-300)).max())
+
+
+# ---------------------------------------------------------------------------
+# K2 form: factor sets as 15 LU scalars, rebuilt in the kernel
+# ---------------------------------------------------------------------------
+def _check_values(y_gpu, yr, z, what):
+    err = np.abs(y_gpu.astype(np.float64) - yr)
+    bad = err > P.TOL * z + P.TOL_ABS
+    assert not bad.any(), f"{what}: {int(bad.sum())} values outside 2e-6*z, worst {float((err / (z + 1e-300)).max())}"
+
+
+LU_CASES = [(256, 1152, True), (130, 4608, False), (67, 2240, False), (33, 160, True), (1, 32, False),
+            (5, 12288, False)]
+
+
+@pytest.mark.parametrize("M,d,shared", LU_CASES, ids=[f"{m}x{d}-{'shared' if s else 'perblock'}"
+                                                       for m, d, s in LU_CASES])
+def test_kq_lu_against_oracle(K, M, d, shared):
+    x, _ = I.act_gaussian_outliers(M, d, 8000 + M + d, max(1, d // 100), 50.0)
+    lu = I.random_lu(1 if shared else d // 32, 8100 + d)
+    say(f"[kq_lu] M={M} d={d} nT={lu.shape[0]}")
+    xd, ld = dev_bf16(x), dev_f32(lu)
+    q, s = K.kq_quantize_lu(xd, ld)
+    y = K.kq_transform_lu_f32(xd, ld)
+    torch.cuda.synchronize()
+    qr, sr, y32 = O.kq_quantize_lu(x, lu, want_y32=True)
+    yr, z = O.kq_transform_lu(x, lu)
+    _check_values(y.cpu().numpy(), yr, z, "kq_transform_lu_f32")
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)
+    say(f"    {res}")
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("M,d", [(200, 1152), (96, 4608)])
+def test_kq_lu_equals_factor_path_bit_exact(K, M, d):
+    # the kernel forms each factor from its LU scalars with the same fp32
+    # operations as kq_lu_factors on the host, so both paths see identical
+    # blocks: codes, scales and transformed values agree bit for bit
+    x, _ = I.act_gaussian_outliers(M, d, 8200 + d, max(1, d // 100), 50.0)
+    for shared in (True, False):
+        lu = I.random_lu(1 if shared else d // 32, 8300 + d + shared)
+        f = K.kq_lu_factors(lu)
+        say(f"[kq_lu == kq(kq_lu_factors)] M={M} d={d} nT={lu.shape[0]}")
+        xd = dev_bf16(x)
+        q1, s1 = K.kq_quantize_lu(xd, dev_f32(lu))
+        q2, s2 = K.kq_quantize(xd, dev_f32(f), variant=VARIANTS["mfma"])
+        y1 = K.kq_transform_lu_f32(xd, dev_f32(lu))
+        y2 = K.kq_transform_f32(xd, dev_f32(f), variant=VARIANTS["mfma"])
+        torch.cuda.synchronize()
+        assert torch.equal(q1, q2) and torch.equal(s1, s2)
+        assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_kq_lu_hadamard_init_and_nonfinite(K):
+    # Hadamard initialisation: within tolerance of the oracle's K2 path;
+    # a = 0 makes the set's blocks non-finite (scale 0xFF, codes 0)
+    M, d = 40, 256
+    x, _ = I.act_gaussian_outliers(M, d, 8400, 3, 30.0)
+    check_lu = I.hadamard_lu(d // 32)
+    say(f"[kq_lu hadamard] M={M} d={d}")
+    q, s = K.kq_quantize_lu(dev_bf16(x), dev_f32(check_lu))
+    torch.cuda.synchronize()
+    qr, sr, y32 = O.kq_quantize_lu(x, check_lu, want_y32=True)
+    _, z = O.kq_transform_lu(x, check_lu)
+    ef, bf = P.boundary_flags(z, y32)
+    assert P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)["ok"]
+    bad = check_lu.copy()
+    bad[3, 2, 0] = 0.0  # a = 0 in factor A3 of set 3
+    say(f"[kq_lu a=0] M={M} d={d}")
+    q, s = K.kq_quantize_lu(dev_bf16(x), dev_f32(bad))
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    q = q.cpu().numpy()
+    assert np.all(s[:, 3] == 0xFF) and np.all(q[:, 48:64] == 0)
+    # every other block as the oracle gives it for the same scalars (same flags:
+    # their blocks are unchanged)
+    qb, sb = O.kq_quantize_lu(x, bad)
+    assert np.all(sb[:, 3] == 0xFF) and np.all(qb[:, 48:64] == 0)
+    assert P.compare(q, s, qb, sb, ef, bf)["ok"]
+
+
+# ---------------------------------------------------------------------------
+# Walsh-Hadamard-32 comparison kernel
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d", [(256, 1152), (67, 2240), (33, 160), (1, 32), (130, 4608), (3, 12288)])
+def test_fwht_against_oracle(K, M, d):
+    x, _ = I.act_gaussian_outliers(M, d, 8500 + M + d, max(1, d // 100), 50.0)
+    say(f"[fwht] M={M} d={d}")
+    xd = dev_bf16(x)
+    q, s = K.fwht_quantize(xd)
+    y = K.fwht_transform_f32(xd)
+    torch.cuda.synchronize()
+    qr, sr, y32 = O.fwht_quantize(x, want_y32=True)
+    yr, z = O.fwht_transform(x)
+    _check_values(y.cpu().numpy(), yr, z, "fwht_transform_f32")
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)
+    say(f"    {res}")
+    assert res["ok"], res
+
+
+def test_fwht_special_blocks(K):
+    # all-zero, all -0, subnormal, NaN and Inf blocks; -0 must never give code 8
+    M, d = 6, 192
+    xf = np.zeros((M, d), np.float32)
+    xf[1] = -0.0
+    xf[2, :32] = np.float32(2.0 ** -130) * np.arange(1, 33, dtype=np.float32)
+    xf[3, 40] = np.nan
+    xf[4, 70] = np.inf
+    xf[5] = np.linspace(-3, 3, d, dtype=np.float32)
+    x = I.f32_to_bf16_bits(xf)
+    say(f"[fwht special] M={M} d={d}")
+    q, s = K.fwht_quantize(dev_bf16(x))
+    torch.cuda.synchronize()
+    qr, sr, y32 = O.fwht_quantize(x, want_y32=True)
+    _, z = O.fwht_transform(x)
+    assert sr[3, 1] == 0xFF and sr[4, 2] == 0xFF
+    ef, bf = P.boundary_flags(z, y32)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)
+    assert res["ok"], res
+    assert np.all(q.cpu().numpy()[:2] == 0) and np.all(s.cpu().numpy()[:2] == 0)
+
+
+def test_lu_fwht_empty(K):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s = K.kq_quantize_lu(x, dev_f32(I.hadamard_lu(1)))
+    q2, s2 = K.fwht_quantize(x)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 32) and s2.shape == (0, 2)
