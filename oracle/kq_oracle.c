@@ -31,6 +31,8 @@
  *   [FWD]  same record, pith_extraction.forward_implications: K2 is compared
  *          with a fast Walsh-Hadamard transform of the same 32-element
  *          blocks.
+ *   [W4A4] the abstract: the quantized activations feed a W4A4 MXFP4 product
+ *          with weights that carry the folded inverse transform.
  *   [OCP]  the element (FP4 E2M1) and shared-scale (E8M0) encodings are not
  *          spelled out on the pages, which only name MXFP4; they follow the
  *          public OCP Microscaling Formats (MX) v1.0 specification:
@@ -480,5 +482,74 @@ int oracle_mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uin
     int64_t nblk = M * (d / 32);
     for (int64_t b = 0; b < nblk; ++b)
         oracle_mx_block(x + b * 32, q + b * 16, s + b);
+    return OR_OK;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 consumer [W4A4], [OCP]: dequantization and the W4A4 product.   */
+/* ------------------------------------------------------------------ */
+
+/* Value of one element: E2M1 code (sign bit 3, magnitude code bits 0-2 on
+ * the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6) times 2^(s - 127); scale byte 0xFF is
+ * the E8M0 NaN encoding and gives NaN. */
+double oracle_mx_value(int code, int sbyte)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (sbyte == 0xFF)
+        return NAN;
+    double v = ldexp(grid[code & 7], sbyte - 127);
+    return (code & 8) ? -v : v;
+}
+
+/* x[m, k] of an MXFP4 matrix q [M, K/2] (element 2i in the low nibble),
+ * s [M, K/32]. */
+int oracle_mx_dequant(const uint8_t *q, const uint8_t *s, int64_t M, int64_t K, double *out)
+{
+    if (!q || !s || !out || M < 0 || K <= 0)
+        return OR_ERR_ARG;
+    if (K % 32)
+        return OR_ERR_SHAPE;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = q[m * (K / 2) + k / 2];
+            int code = (k & 1) ? (byte >> 4) : (byte & 15);
+            out[m * K + k] = oracle_mx_value(code, s[m * (K / 32) + k / 32]);
+        }
+    return OR_OK;
+}
+
+/* out[m, n] = sum_k A[m, k] B[n, k] of two MXFP4 matrices (A [M, K], B [N, K],
+ * both in the quantizer's layout), in double; mag[m, n] = sum_k |A[m,k] B[n,k]|. */
+int oracle_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+                   int64_t K, double *out, double *mag)
+{
+    if (!qa || !sa || !qb || !sb || !out || M < 0 || N < 0 || K <= 0)
+        return OR_ERR_ARG;
+    if (K % 32)
+        return OR_ERR_SHAPE;
+    double *A = (double *)malloc((size_t)(M > 0 ? M : 1) * K * sizeof(double));
+    double *B = (double *)malloc((size_t)(N > 0 ? N : 1) * K * sizeof(double));
+    if (!A || !B) {
+        free(A);
+        free(B);
+        return OR_ERR_ARG;
+    }
+    oracle_mx_dequant(qa, sa, M, K, A);
+    oracle_mx_dequant(qb, sb, N, K, B);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, ab = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = A[m * K + k] * B[n * K + k];
+                acc += p;
+                ab += fabs(p);
+            }
+            out[m * N + n] = acc;
+            if (mag)
+                mag[m * N + n] = ab;
+        }
+    free(A);
+    free(B);
     return OR_OK;
 }

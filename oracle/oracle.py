@@ -69,6 +69,12 @@ def bind(L):
     L.oracle_fwht_transform.restype = ctypes.c_int
     L.oracle_fwht_quantize.argtypes = [P, I64, I64, P, P, P]
     L.oracle_fwht_quantize.restype = ctypes.c_int
+    L.oracle_mx_value.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.oracle_mx_value.restype = ctypes.c_double
+    L.oracle_mx_dequant.argtypes = [P, P, I64, I64, P]
+    L.oracle_mx_dequant.restype = ctypes.c_int
+    L.oracle_mx_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
+    L.oracle_mx_gemm.restype = ctypes.c_int
     return L
 
 
@@ -247,6 +253,33 @@ def fwht_quantize(x_u16, want_y32=False):
     y32 = np.empty((M, d), np.float32) if want_y32 else None
     _check(lib().oracle_fwht_quantize(_ptr(x), M, d, _ptr(q), _ptr(s), _ptr(y32)))
     return (q, s, y32) if want_y32 else (q, s)
+
+
+def mx_value(code, sbyte):
+    return lib().oracle_mx_value(int(code), int(sbyte))
+
+
+def mx_dequant(q, s):
+    """float64 values [M, K] of an MXFP4 matrix (q [M, K/2], s [M, K/32])."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    M, K = q.shape[0], q.shape[1] * 2
+    out = np.empty((M, K), np.float64)
+    _check(lib().oracle_mx_dequant(_ptr(q), _ptr(s), M, K, _ptr(out)))
+    return out
+
+
+def mx_gemm(qa, sa, qb, sb, want_mag=True):
+    """A [M, K] times B [N, K]^T of two MXFP4 matrices, float64 (and sum |a b|)."""
+    qa, sa = np.ascontiguousarray(qa, np.uint8), np.ascontiguousarray(sa, np.uint8)
+    qb, sb = np.ascontiguousarray(qb, np.uint8), np.ascontiguousarray(sb, np.uint8)
+    M, K = qa.shape[0], qa.shape[1] * 2
+    N = qb.shape[0]
+    assert qb.shape[1] * 2 == K
+    out = np.empty((M, N), np.float64)
+    mag = np.empty((M, N), np.float64) if want_mag else None
+    _check(lib().oracle_mx_gemm(_ptr(qa), _ptr(sa), M, _ptr(qb), _ptr(sb), N, K, _ptr(out), _ptr(mag)))
+    return (out, mag) if want_mag else out
 
 
 def raw_status(fn_name, *args):

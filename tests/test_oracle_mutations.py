@@ -58,6 +58,14 @@ MUTATIONS = {
         "p *= G[k * 4 + rk * 2 + ck];",
         "p *= G[k * 4 + ck * 2 + rk];",
         "test_lu_block_is_kron_of_its_factors", {}),
+    "dequant_nibble_order_swapped": (
+        "int code = (k & 1) ? (byte >> 4) : (byte & 15);",
+        "int code = (k & 1) ? (byte & 15) : (byte >> 4);",
+        "test_mx_dequant_requantizes_to_itself", {}),
+    "dequant_grid_value_wrong": (
+        "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}",
+        "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}",
+        "test_mx_value_inverts_the_element_encoding", {}),
     "wht_sign_flipped": (
         "K[r * 32 + c] = par ? -scale : scale;",
         "K[r * 32 + c] = par ? scale : -scale;",

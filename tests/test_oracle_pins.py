@@ -375,3 +375,64 @@ def test_kq_lu_matches_factor_path_on_the_same_block(oracle_lib):
     for shape_lu in (np.zeros((2, 5, 3), np.float32), np.zeros((d // 32 + 1, 5, 3), np.float32)):
         with pytest.raises(Exception):
             oracle_lib.kq_quantize_lu(x, shape_lu)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 consumer (the abstract's W4A4 product): dequantization and GEMM
+# ---------------------------------------------------------------------------
+def test_mx_value_inverts_the_element_encoding(oracle_lib):
+    # every code at every normal scale: encoding the value again gives the code
+    # back (-0, code 8, comes back as +0: the sign bit is set only for values < 0)
+    for sbyte in range(1, 255, 3):
+        E = sbyte - 127
+        for code in range(16):
+            v = oracle_lib.mx_value(code, sbyte)
+            if abs(v) > float(np.finfo(np.float32).max):
+                continue  # 4 or 6 times 2^126 is past fp32: not an fp32 input to encode
+            back = oracle_lib.fp4_code(np.float32(v), E)
+            assert back == (0 if code == 8 else code), (code, sbyte, v, back)
+    assert math.isnan(oracle_lib.mx_value(3, 0xFF))
+
+
+def test_mx_dequant_requantizes_to_itself(oracle_lib):
+    rng = np.random.default_rng(53)
+    y = (rng.standard_normal((24, 256)) * np.exp(rng.uniform(-8, 8, (24, 1)))).astype(np.float32)
+    y[3, 32:64] = 0.0
+    q, s = oracle_lib.mx_quantize_f32(y)
+    v = oracle_lib.mx_dequant(q, s)
+    # each value is within 2^(E+1) of its input: half the widest grid step
+    # (2 * 2^E, between 4 and 6), or the saturation of (6, 8) * 2^E to 6 * 2^E
+    E = s.astype(np.int64).repeat(32, axis=1) - 127
+    assert np.all(np.abs(v - y) <= np.ldexp(2.0, E))
+    q2, s2 = oracle_lib.mx_quantize_f32(v.astype(np.float32))
+    lo, hi = q & 0x0F, q >> 4
+    q_pos0 = np.where(lo == 8, 0, lo) | (np.where(hi == 8, 0, hi) << 4)
+    assert np.array_equal(s2, s) and np.array_equal(q2, q_pos0.astype(np.uint8))
+
+
+def test_mx_gemm_matches_numpy_matmul(oracle_lib):
+    rng = np.random.default_rng(59)
+    M, N, K = 9, 7, 160
+    ya = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+    yb = (rng.standard_normal((N, K)) * 0.1).astype(np.float32)
+    qa, sa = oracle_lib.mx_quantize_f32(ya)
+    qb, sb = oracle_lib.mx_quantize_f32(yb)
+    out, mag = oracle_lib.mx_gemm(qa, sa, qb, sb)
+    A, B = oracle_lib.mx_dequant(qa, sa), oracle_lib.mx_dequant(qb, sb)
+    assert np.all(np.abs(out - A @ B.T) <= 1e-14 * mag)
+    assert np.allclose(mag, np.abs(A) @ np.abs(B).T, rtol=1e-14, atol=0)
+
+
+def test_mx_gemm_hand_case(oracle_lib):
+    # one block each: A = 1.5 * 2^1 at k = 0 and -6 * 2^1 at k = 31; B = 4 * 2^-2 at
+    # k = 0 and 0.5 * 2^-2 at k = 31:  3 * 1 + (-12) * 0.125 = 1.5
+    qa = np.zeros((1, 16), np.uint8)
+    qa[0, 0] = 0x03          # k = 0: code 3 (1.5), low nibble
+    qa[0, 15] = 0xF0         # k = 31: code 15 (-6), high nibble
+    qb = np.zeros((1, 16), np.uint8)
+    qb[0, 0] = 0x06          # k = 0: code 6 (4)
+    qb[0, 15] = 0x10         # k = 31: code 1 (0.5)
+    sa = np.array([[128]], np.uint8)
+    sb = np.array([[125]], np.uint8)
+    out, mag = oracle_lib.mx_gemm(qa, sa, qb, sb)
+    assert out[0, 0] == 1.5 and mag[0, 0] == 4.5
