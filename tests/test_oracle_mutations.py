@@ -63,8 +63,8 @@ MUTATIONS = {
         "int code = (k & 1) ? (byte & 15) : (byte >> 4);",
         "test_mx_dequant_requantizes_to_itself", {}),
     "dequant_grid_value_wrong": (
-        "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}",
-        "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}",
+        "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};\n    if (sbyte == 0xFF)",
+        "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0};\n    if (sbyte == 0xFF)",
         "test_mx_value_inverts_the_element_encoding", {}),
     "wht_sign_flipped": (
         "K[r * 32 + c] = par ? -scale : scale;",
