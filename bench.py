@@ -28,6 +28,7 @@ which this script reads back while the kernel source hash still matches.
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--all-configs", action="store_true",
                     help="per-configuration table: KroQuant (MFMA per-block and shared, butterfly), SmoothQuant "
                          "and the copy ceiling, each timed alone")
+    ap.add_argument("--gemm", action="store_true",
+                    help="W4A4 consumer (mx_gemm) on the DiT layer shapes, against its roofline")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic profile from two rocprofv3 --pmc output folders (no GPU needed)")
     return ap.parse_args()
@@ -320,15 +323,86 @@ def all_configs(args):
               f"{r['k2_lu_over_fwht_speed']} |", flush=True)
 
 
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak (TFLOP/s)
+# DiT (d = 1152, MLP 4608) linear layers on the CFG batch of 8192 tokens: (name, M, N, K)
+GEMM_SHAPES = [("qkv", 8192, 3456, 1152), ("proj", 8192, 1152, 1152), ("mlp_up", 8192, 4608, 1152),
+               ("mlp_down", 8192, 1152, 4608)]
+
+
+def gemm_bench(args):
+    """mx_gemm (bf16 out) on the DiT layer shapes; operands from the quantizer's
+    own kernels on synthetic data; each shape a graph of --steps launches over
+    rotating operand sets, timed with HIP events.  Roofline per shape:
+    max(2MNK / FP4 peak, bytes / HBM peak) with bytes = A, B codes and scales
+    plus the bf16 output."""
+    import torch
+
+    import mxfp4_act_quantizer_amd as K
+    from synth import inputs as I
+    dev = torch.device("cuda:0")
+    rows = []
+    for name, M, N, Kd in GEMM_SHAPES:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(M + N + Kd)
+        nbytes = M * Kd // 2 + M * Kd // 32 + N * Kd // 2 + N * Kd // 32 + M * N * 2
+        nsets = max(2, int(np.ceil(ROTATE_BYTES / nbytes)))
+        f = torch.from_numpy(I.hadamard_factors(Kd // 32)).to(dev)
+        sets = []
+        for _ in range(nsets):
+            x = torch.randn(M, Kd, generator=gen, device=dev).to(torch.bfloat16)
+            qa, sa = K.kq_quantize(x, f)
+            w = torch.randn(N, Kd, generator=gen, device=dev) / math.sqrt(Kd)
+            qb, sb = K.mx_quantize_f32(w)
+            sets.append((qa, sa, qb, sb, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+            del x, w
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            K.mx_gemm(*sets[0][:4], out=sets[0][4], stream=cs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(args.steps):
+                    b = sets[i % nsets]
+                    K.mx_gemm(*b[:4], out=b[4], stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            g.replay()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        flops = 2.0 * M * N * Kd
+        t_mfma = flops / (FP4_PEAK_TFLOPS * 1e12) * 1e6
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        row = {"layer": name, "M": M, "N": N, "K": Kd, "us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
+               "GB/s": round(nbytes / us / 1e3, 1), "bound": bound,
+               "roofline_us": round(max(t_mfma, t_hbm), 2), "frac": round(max(t_mfma, t_hbm) / us, 4)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    tot_us = sum(r["us"] for r in rows)
+    tot_roof = sum(r["roofline_us"] for r in rows)
+    print(json.dumps({"gemm_block_us": round(tot_us, 2), "roofline_us": round(tot_roof, 2),
+                      "frac": round(tot_roof / tot_us, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
-    if args.all_configs:
+    if args.all_configs or args.gemm:
         if args.gpus != 1:
             sys.exit(2)
-        all_configs(args)
+        all_configs(args) if args.all_configs else gemm_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "

@@ -150,6 +150,25 @@ int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *
  *   y  dev, float32 [M, d], 16-byte aligned */
 int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *stream);
 
+/*
+ * mx_gemm: the W4A4 consumer of the quantizer's output (abstract: MXFP4 W4A4,
+ * with the inverse transform folded into the weights).  out = A . B^T, where
+ * A [M, K] and B [N, K] are MXFP4 matrices in the layout above: codes
+ * qa [M, K/2], qb [N, K/2] and E8M0 scales sa [M, K/32], sb [N, K/32].  Every
+ * element is (E2M1 value) x 2^(s - 127); a scale byte 0xFF is NaN.  Products
+ * are formed on the gfx950 block-scaled FP4 matrix cores and accumulated in
+ * fp32; out is float32 [M, N] (out_bf16 = 0) or bf16 [M, N] rounded to
+ * nearest even from that fp32 sum (out_bf16 = 1).
+ *   qa, qb     dev, 16-byte aligned        sa, sb  dev, any alignment
+ *   out        dev, 4-byte (float32) or 2-byte (bf16) aligned, not overlapping
+ *   K % 32 == 0, K <= 2^20, N <= 2^21 (per-tile offsets stay 32-bit).
+ *   M == 0 or N == 0 is a no-op.
+ * Typical use: qa, sa from kq_quantize of the activations; qb, sb from
+ * mx_quantize_f32 of kq_fold_weight(W).
+ */
+int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+            int64_t K, void *out, int out_bf16, void *stream);
+
 /* ---------------- host helpers for the offline weight side --------------- */
 /* All pointers are host memory; the calls are synchronous and touch no GPU.  */
 

@@ -30,7 +30,7 @@ KQ_VARIANT_BUTTERFLY = 2
 EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
-    "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors",
+    "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors", "mx_gemm",
     "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
 )
 
@@ -53,6 +53,7 @@ _lib.kq_transform_lu_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
 _lib.fwht_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.fwht_transform_f32.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.kq_lu_factors.argtypes = [_P, _I64, _P]
+_lib.mx_gemm.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
 _lib.kq_block_matrix.argtypes = [_P, _I64, _P]
 _lib.kq_block_inverse.argtypes = [_P, _I64, _P]
@@ -229,6 +230,26 @@ def fwht_transform_f32(x, y=None, stream=None):
                                  _stream_handle(stream))
     _check(st, "fwht_transform_f32")
     return y
+
+
+def mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
+    """W4A4 product out = A . B^T of two MXFP4 matrices (codes [rows, K/2] u8,
+    scales [rows, K/32] u8), accumulated in fp32; out float32 or bfloat16."""
+    torch = _torch()
+    M, K = int(qa.shape[0]), int(qa.shape[1]) * 2
+    N = int(qb.shape[0])
+    if int(qb.shape[1]) * 2 != K or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+        raise ValueError("operand shapes do not match")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=qa.device)
+    bf = 1 if out.dtype == torch.bfloat16 else 0
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (M, N):
+        raise ValueError("out must be float32 or bfloat16 [M, N]")
+    u8 = (torch.uint8,)
+    st = _lib.mx_gemm(_dev(qa, u8, "qa"), _dev(sa, u8, "sa"), M, _dev(qb, u8, "qb"), _dev(sb, u8, "sb"), N, K,
+                      _dev(out, (torch.float32, torch.bfloat16), "out"), bf, _stream_handle(stream))
+    _check(st, "mx_gemm")
+    return out
 
 
 def sq_quantize(x, scale, q=None, s=None, stream=None):

@@ -231,6 +231,26 @@ int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s
     return hip_status(kq::launch_mx_f32(x, M, d, q, s, (hipStream_t)stream));
 }
 
+int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+            int64_t K, void *out, int out_bf16, void *stream)
+{
+    if (M < 0 || N < 0 || K <= 0 || (out_bf16 != 0 && out_bf16 != 1))
+        return KQ_ERR_ARG;
+    if (K % 32 != 0 || K > kq::kMaxD || N > ((int64_t)1 << 21) || (M > 0 && N > 0 && M * N > ((int64_t)1 << 40)))
+        return KQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return KQ_OK;
+    if (!qa || !sa || !qb || !sb || !out)
+        return KQ_ERR_ARG;
+    if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(out, out_bf16 ? 2 : 4))
+        return KQ_ERR_ALIGN;
+    const int64_t ob = M * N * (out_bf16 ? 2 : 4);
+    if (overlap(out, ob, qa, M * (K / 2)) || overlap(out, ob, sa, M * (K / 32)) || overlap(out, ob, qb, N * (K / 2)) ||
+        overlap(out, ob, sb, N * (K / 32)))
+        return KQ_ERR_OVERLAP;
+    return hip_status(kq::launch_mx_gemm(qa, sa, M, qb, sb, N, K, out, out_bf16, (hipStream_t)stream));
+}
+
 const char *kq_status_string(int status)
 {
     switch (status) {

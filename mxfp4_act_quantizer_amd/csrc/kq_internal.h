@@ -25,6 +25,10 @@ hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const fl
 hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
                      hipStream_t stream);
 hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream);
+// W4A4 product of two MXFP4 matrices in the quantizer's layout: out[M, N]
+// (float32, or bf16 when bf16 != 0) = A[M, K] . B[N, K]^T
+hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
+                          int64_t N, int64_t K, void *out, int bf16, hipStream_t stream);
 // normalised Walsh-Hadamard-32 comparison: quantize (y null) or export y
 hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
 

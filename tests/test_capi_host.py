@@ -275,3 +275,18 @@ def test_fold_weight_through_lu_factors(oracle_lib):
     ref = I.bf16_bits_to_f32(x).astype(np.float64) @ W.astype(np.float64).T
     got = y @ Wf.astype(np.float64).T
     assert np.allclose(got, ref, rtol=0, atol=1e-4 * np.abs(ref).max())
+
+
+def test_mx_gemm_validation():
+    qa, sa, qb, sb, out = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 48, out, 0, None) == K.KQ_ERR_SHAPE  # K % 32
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 0, out, 0, None) == K.KQ_ERR_ARG
+    assert raw("mx_gemm", qa, sa, -1, qb, sb, 4, 64, out, 0, None) == K.KQ_ERR_ARG
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 64, out, 2, None) == K.KQ_ERR_ARG  # out type
+    assert raw("mx_gemm", None, sa, 4, qb, sb, 4, 64, out, 0, None) == K.KQ_ERR_ARG
+    assert raw("mx_gemm", qa + 8, sa, 4, qb, sb, 4, 64, out, 0, None) == K.KQ_ERR_ALIGN
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 64, out + 2, 0, None) == K.KQ_ERR_ALIGN
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 64, qa + 2, 1, None) == K.KQ_ERR_OVERLAP  # 2-byte ok for bf16
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 64, qa + 16, 0, None) == K.KQ_ERR_OVERLAP
+    assert raw("mx_gemm", None, None, 0, None, None, 4, 64, None, 0, None) == K.KQ_OK
+    assert raw("mx_gemm", qa, sa, 4, qb, sb, (1 << 21) + 1, 64, out, 0, None) == K.KQ_ERR_SHAPE

@@ -7,6 +7,7 @@ Bars (see tests/parity.py for the exact rules):
   - sq_quantize, mx_quantize_f32 and kq_quantize with identity factors fully
     bit-exact.
 """
+import math
 import sys
 
 import numpy as np
@@ -31,6 +32,11 @@ def _need_gpu():
 def K():
     _need_gpu()
     import mxfp4_act_quantizer_amd as K
+    return K
+
+
+@pytest.fixture(scope="module")
+def K_lib(K):
     return K
 
 
@@ -508,3 +514,89 @@ def test_lu_fwht_empty(K):
     q2, s2 = K.fwht_quantize(x)
     torch.cuda.synchronize()
     assert q.shape == (0, 32) and s2.shape == (0, 2)
+
+
+# ---------------------------------------------------------------------------
+# W4A4 consumer: MXFP4 x MXFP4 on the block-scaled matrix cores
+# ---------------------------------------------------------------------------
+def _mx_operand(rows, K, seed, scale_spread=6.0):
+    rng = np.random.default_rng(seed)
+    y = (rng.standard_normal((rows, K)) * np.exp(rng.uniform(-scale_spread, scale_spread, (rows, 1)))).astype(np.float32)
+    q, s = O.mx_quantize_f32(y)
+    return q, s
+
+
+def _gemm_tol(K, mag):
+    # fp32 accumulation: one rounding per 64-wide k step, plus the last; a
+    # factor 2 of margin for the order inside a step
+    return (K // 64 + 2) * 2.0 ** -23 * mag
+
+
+GEMM_CASES = [(128, 128, 256), (200, 72, 160), (1, 1, 32), (257, 130, 1152), (64, 300, 4608), (33, 129, 96)]
+
+
+@pytest.mark.parametrize("M,N,Kd", GEMM_CASES, ids=[f"{m}x{n}x{k}" for m, n, k in GEMM_CASES])
+def test_mx_gemm_against_oracle(K_lib, M, N, Kd):
+    qa, sa = _mx_operand(M, Kd, 9000 + M)
+    qb, sb = _mx_operand(N, Kd, 9100 + N)
+    say(f"[mx_gemm] M={M} N={N} K={Kd}")
+    d = [torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)]
+    out = K_lib.mx_gemm(*d)
+    outb = K_lib.mx_gemm(*d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, mag = O.mx_gemm(qa, sa, qb, sb)
+    o = out.cpu().numpy().astype(np.float64)
+    err = np.abs(o - ref)
+    assert np.all(err <= _gemm_tol(Kd, mag) + 1e-300), float((err / (mag + 1e-300)).max())
+    # bf16 output: round to nearest even of the same fp32 sums
+    rne = torch.from_numpy(out.cpu().numpy()).to(torch.bfloat16)
+    assert torch.equal(outb.cpu().view(torch.int16), rne.view(torch.int16))
+
+
+def test_mx_gemm_nan_scale_and_zero_blocks(K_lib):
+    M, N, Kd = 64, 64, 128
+    qa, sa = _mx_operand(M, Kd, 9200)
+    qb, sb = _mx_operand(N, Kd, 9201)
+    sa[5, 2] = 0xFF            # NaN block in row 5
+    qb[7, :] = 0               # column 7 all +0 codes
+    say(f"[mx_gemm special] M={M} N={N} K={Kd}")
+    out = K_lib.mx_gemm(*[torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)])
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    ref, mag = O.mx_gemm(qa, sa, qb, sb)
+    assert np.all(np.isnan(o[5])) and np.all(np.isnan(ref[5]))
+    keep = np.ones(M, bool)
+    keep[5] = False
+    assert np.all(o[keep, 7] == 0.0)
+    assert np.all(np.abs(o[keep] - ref[keep]) <= _gemm_tol(Kd, mag[keep]) + 1e-300)
+
+
+def test_w4a4_end_to_end_invariance(K_lib):
+    # Y = X W^T through the quantized path: activations transformed and
+    # quantized by kq_quantize, weights folded (kq_fold_weight) and quantized
+    # (mx_quantize_f32), product on the matrix cores.  With outlier channels in
+    # X, the Hadamard-initialised transform must beat plain MXFP4 (identity
+    # factors) on output error, and every GPU product must match the oracle's
+    # product of the same codes.
+    M, d, N = 256, 1152, 384
+    x = I.make_activation("dit_1152", M=M)
+    rng = np.random.default_rng(9300)
+    W = (rng.standard_normal((N, d)) / math.sqrt(d)).astype(np.float32)
+    Xf = I.bf16_bits_to_f32(x).astype(np.float64)
+    Y_ref = Xf @ W.astype(np.float64).T
+    errs = {}
+    for label, f in (("identity", I.identity_factors(1)), ("hadamard", I.hadamard_factors(d // 32)),
+                     ("lu_random", K_lib.kq_lu_factors(I.random_lu(d // 32, 9301)))):
+        say(f"[w4a4] {label} M={M} d={d} N={N}")
+        qa, sa = K_lib.kq_quantize(dev_bf16(x), dev_f32(f))
+        Wf = K_lib.kq_fold_weight(W, f)
+        qb, sb = K_lib.mx_quantize_f32(torch.from_numpy(Wf).cuda())
+        Y = K_lib.mx_gemm(qa, sa, qb, sb)
+        torch.cuda.synchronize()
+        Yn = Y.cpu().numpy().astype(np.float64)
+        ref, mag = O.mx_gemm(qa.cpu().numpy(), sa.cpu().numpy(), qb.cpu().numpy(), sb.cpu().numpy())
+        assert np.all(np.abs(Yn - ref) <= _gemm_tol(d, mag) + 1e-300)
+        errs[label] = float(np.linalg.norm(Yn - Y_ref) / np.linalg.norm(Y_ref))
+    say(f"    relative output error {errs}")
+    assert all(np.isfinite(v) for v in errs.values())
+    assert errs["hadamard"] < errs["identity"]
