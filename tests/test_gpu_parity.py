@@ -553,6 +553,28 @@ def test_mx_gemm_against_oracle(K_lib, M, N, Kd):
     assert torch.equal(outb.cpu().view(torch.int16), rne.view(torch.int16))
 
 
+def test_mx_gemm_output_alignment_and_guards(K_lib):
+    # The product written into caller buffers that start 4 or 2 bytes past a
+    # 16-byte boundary (element-wise stores) must equal the one written into
+    # an aligned buffer (16-byte row pieces), and nothing outside [M, N] is
+    # touched in either case.
+    M, N, Kd = 96, 136, 320
+    qa, sa = _mx_operand(M, Kd, 9400)
+    qb, sb = _mx_operand(N, Kd, 9401)
+    d = [torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)]
+    for dt, off in ((torch.float32, 4), (torch.float32, 1), (torch.bfloat16, 8), (torch.bfloat16, 2),
+                    (torch.bfloat16, 1)):
+        say(f"[mx_gemm out] dtype={dt} element offset={off}")
+        buf = torch.full((M * N + off + 16,), float("nan"), dtype=dt, device="cuda")
+        out = buf[off:off + M * N].view(M, N)
+        K_lib.mx_gemm(*d, out=out)
+        ref = K_lib.mx_gemm(*d, out_dtype=dt)
+        torch.cuda.synchronize()
+        iv = torch.int32 if dt == torch.float32 else torch.int16
+        assert torch.equal(out.cpu().view(iv), ref.cpu().view(iv))
+        assert torch.isnan(buf[:off].float()).all() and torch.isnan(buf[off + M * N:].float()).all()
+
+
 def test_mx_gemm_nan_scale_and_zero_blocks(K_lib):
     M, N, Kd = 64, 64, 128
     qa, sa = _mx_operand(M, Kd, 9200)
