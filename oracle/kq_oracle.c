@@ -33,6 +33,12 @@
  *          blocks.
  *   [W4A4] the abstract: the quantized activations feed a W4A4 MXFP4 product
  *          with weights that carry the folded inverse transform.
+ *   [ADALN] the abstract: normalization layers between the blocks force the
+ *          transform to run online at every denoising step; the verdict
+ *          record's referee_report.summary: AdaLN is what prevents absorbing
+ *          it offline.  The normalisation in front of the quantizer is
+ *          therefore AdaLN, and fusing the two keeps the normalised
+ *          activation from a round trip through memory.
  *   [OCP]  the element (FP4 E2M1) and shared-scale (E8M0) encodings are not
  *          spelled out on the pages, which only name MXFP4; they follow the
  *          public OCP Microscaling Formats (MX) v1.0 specification:
@@ -59,6 +65,13 @@
  *     scalars stored as (a, b, c) per factor, factors A1..A5 in order.
  *   - FWHT comparison: the normalised Sylvester-order Walsh-Hadamard matrix,
  *     y_c = 2^-2.5 * sum_r x_r (-1)^popcount(r & c), then the same MXFP4.
+ *   - AdaLN front-end (the pages name AdaLN but print no formula): per token
+ *     row, LayerNorm without a learned affine (mean and biased variance over
+ *     the row's d channels, 1/sqrt(var + eps)), then the per-sample
+ *     modulation x_c = n_c * (1 + scale[b][c]) + shift[b][c], sample
+ *     b = m / T for token row m and T tokens per sample.  The quantizer
+ *     receives x rounded to bf16 (nearest, ties to even): the value the
+ *     unfused pipeline would store and read back.
  */
 #include <math.h>
 #include <stdint.h>
@@ -551,5 +564,93 @@ int oracle_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_
         }
     free(A);
     free(B);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* AdaLN front-end [ADALN]: the normalisation in front of the quantizer. */
+/* ------------------------------------------------------------------ */
+
+/* bf16 bits of v rounded to the nearest bf16 value, ties to the even
+ * fraction, written out from the format: 8 significant bits for normal
+ * values (exponent -126..127), a fixed spacing of 2^-133 below 2^-126. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e = ilogb(a); /* a in [2^e, 2^(e+1)) */
+    if (e < -126)
+        e = -126;
+    double ulp = ldexp(1.0, e - 7);
+    double m = floor(a / ulp); /* exact: ulp is a power of two */
+    double rem = a - m * ulp;  /* exact */
+    double half = 0.5 * ulp;
+    if (rem > half || (rem == half && fmod(m, 2.0) == 1.0))
+        m += 1.0;
+    double r = m * ulp; /* the rounded magnitude */
+    if (r >= ldexp(1.0, 128))
+        return sign | 0x7F80; /* past the largest bf16 */
+    int er = ilogb(r);
+    if (er < -126)
+        return sign | (uint16_t)(r / ldexp(1.0, -133)); /* subnormal: fraction only */
+    return sign | (uint16_t)((er + 127) << 7) | (uint16_t)(r / ldexp(1.0, er - 7) - 128.0);
+}
+
+/* x[m, c] = (h[m, c] - mu_m) / sqrt(var_m + eps) * (1 + scale[b][c]) + shift[b][c],
+ * b = m / T, in double (mean, then the variance about it: two passes).
+ * Outputs: x (double), xb = x rounded to bf16, xflag[m, c] = 1 where x lies
+ * within a margin of a bf16 rounding midpoint, so that a computation of the
+ * same value in other (double) arithmetic may round to the other neighbour.
+ * The margin bounds the error of any double evaluation of the statistics by
+ * sums of at most a few hundred terms, with a factor 32 to spare:
+ *   2^-40 [ mean|h| r |g| + |h - mu| r |g| (1 + (var + mu^2) / (var + eps)) + |x| + |shift| ],
+ * r = 1/sqrt(var + eps), g = 1 + scale.  shift and scale are [ceil(M/T), d]. */
+int oracle_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
+                 float eps, double *x, uint16_t *xb, uint8_t *xflag)
+{
+    if (!h || !shift || !scale || !x || !xb || !xflag || M < 0 || d <= 0 || T <= 0 || !(eps > 0.0f))
+        return OR_ERR_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *hr = h + m * d;
+        double sum = 0.0, sabs = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            double v = oracle_bf16_to_double(hr[c]);
+            sum += v;
+            sabs += fabs(v);
+        }
+        double mu = sum / (double)d;
+        double ss = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            double dv = oracle_bf16_to_double(hr[c]) - mu;
+            ss += dv * dv;
+        }
+        double var = ss / (double)d;
+        double r = 1.0 / sqrt(var + (double)eps);
+        double cancel = 1.0 + (var + mu * mu) / (var + (double)eps);
+        int64_t b = m / T;
+        for (int64_t c = 0; c < d; ++c) {
+            double g = 1.0 + (double)scale[b * d + c];
+            double t = (double)shift[b * d + c];
+            double dv = oracle_bf16_to_double(hr[c]) - mu;
+            double v = dv * r * g + t;
+            x[m * d + c] = v;
+            xb[m * d + c] = oracle_double_to_bf16(v);
+            /* the bf16 rounding midpoint next to v */
+            double a = fabs(v);
+            int e = a > 0.0 ? ilogb(a) : -126;
+            if (e < -126)
+                e = -126;
+            double ulp = ldexp(1.0, e - 7);
+            double mid = (floor(a / ulp) + 0.5) * ulp;
+            double margin = ldexp((sabs / (double)d) * r * fabs(g) + fabs(dv) * r * fabs(g) * cancel + a + fabs(t), -40);
+            xflag[m * d + c] = fabs(a - mid) <= margin;
+        }
+    }
     return OR_OK;
 }

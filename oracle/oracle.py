@@ -75,6 +75,10 @@ def bind(L):
     L.oracle_mx_dequant.restype = ctypes.c_int
     L.oracle_mx_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
     L.oracle_mx_gemm.restype = ctypes.c_int
+    L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    L.oracle_double_to_bf16.restype = ctypes.c_uint16
+    L.oracle_adaln.argtypes = [P, I64, I64, P, P, I64, ctypes.c_float, P, P, P]
+    L.oracle_adaln.restype = ctypes.c_int
     return L
 
 
@@ -280,6 +284,28 @@ def mx_gemm(qa, sa, qb, sb, want_mag=True):
     mag = np.empty((M, N), np.float64) if want_mag else None
     _check(lib().oracle_mx_gemm(_ptr(qa), _ptr(sa), M, _ptr(qb), _ptr(sb), N, K, _ptr(out), _ptr(mag)))
     return (out, mag) if want_mag else out
+
+
+def double_to_bf16(v):
+    """bf16 bit pattern of a double, rounded to nearest, ties to even."""
+    return int(lib().oracle_double_to_bf16(float(v)))
+
+
+def adaln(h_u16, shift, scale, T, eps):
+    """AdaLN front-end: x = LN(h) * (1 + scale[b]) + shift[b], b = m // T.
+    Returns x (float64 [M, d]), x rounded to bf16 (uint16 bits) and the
+    near-midpoint flags (bool [M, d])."""
+    h = _u16(h_u16)
+    M, d = h.shape
+    sh = _f32(shift)
+    sc = _f32(scale)
+    nS = (M + T - 1) // T
+    assert sh.shape == (max(nS, 0), d) and sc.shape == sh.shape
+    x = np.empty((M, d), np.float64)
+    xb = np.empty((M, d), np.uint16)
+    fl = np.empty((M, d), np.uint8)
+    _check(lib().oracle_adaln(_ptr(h), M, d, _ptr(sh), _ptr(sc), int(T), float(eps), _ptr(x), _ptr(xb), _ptr(fl)))
+    return x, xb, fl.astype(bool)
 
 
 def raw_status(fn_name, *args):

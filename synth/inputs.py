@@ -303,3 +303,28 @@ def make_factors(name, d=None, shared=None, seed=None):
         shared = (_CFG_ID[name] == 1)
     nT = 1 if shared else d // 32
     return random_factors(nT, seed)
+
+
+def adaln_modulation(n_samples, d, seed, sigma=0.5):
+    """Per-sample AdaLN modulation vectors (shift, scale), fp32 [n_samples, d]
+    each, drawn N(0, sigma^2) per entry (standing in for the conditioning
+    projection of a diffusion transformer block)."""
+    rng = _rng(seed)
+    shift = (sigma * _normal(rng, (n_samples, d))).astype(np.float32)
+    scale = (sigma * _normal(rng, (n_samples, d))).astype(np.float32)
+    return shift, scale
+
+
+def adaln_seed(name):
+    return 1000 * _CFG_ID[name] + 700 + _VARIANT[name]
+
+
+def tokens_per_sample(name, M=None):
+    """Tokens per sample of a named workload: the CFG-doubled batches hold two
+    samples (conditional and unconditional) of M / 2 tokens each; the tiny
+    workload is one sample."""
+    M0, _, _ = CONFIGS[name]
+    M = M0 if M is None else M
+    if _CFG_ID[name] == 1:
+        return max(M, 1)
+    return max((M + 1) // 2, 1)

@@ -66,6 +66,26 @@ MUTATIONS = {
         "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};\n    if (sbyte == 0xFF)",
         "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0};\n    if (sbyte == 0xFF)",
         "test_mx_value_inverts_the_element_encoding", {}),
+    "adaln_eps_dropped": (
+        "double r = 1.0 / sqrt(var + (double)eps);",
+        "double r = 1.0 / sqrt(var);",
+        "test_adaln_matches_torch_layer_norm", {"M": 5, "d": 64, "T": 2}),
+    "adaln_unbiased_variance": (
+        "double var = ss / (double)d;",
+        "double var = ss / (double)(d - 1);",
+        "test_adaln_matches_torch_layer_norm", {"M": 5, "d": 64, "T": 2}),
+    "adaln_modulation_without_one": (
+        "double g = 1.0 + (double)scale[b * d + c];",
+        "double g = (double)scale[b * d + c];",
+        "test_adaln_hand_case", {}),
+    "adaln_sample_index_modulo": (
+        "int64_t b = m / T;",
+        "int64_t b = m % T;",
+        "test_adaln_matches_torch_layer_norm", {"M": 7, "d": 1152, "T": 3}),
+    "bf16_rounding_ties_away": (
+        "if (rem > half || (rem == half && fmod(m, 2.0) == 1.0))\n        m += 1.0;\n    double r = m * ulp;",
+        "if (rem >= half)\n        m += 1.0;\n    double r = m * ulp;",
+        "test_double_to_bf16_nearest_even", {}),
     "wht_sign_flipped": (
         "K[r * 32 + c] = par ? -scale : scale;",
         "K[r * 32 + c] = par ? scale : -scale;",
