@@ -70,7 +70,7 @@ def parse():
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("kq_kernels.hip", "kq_capi.hip", "kq_internal.h"):
+    for f in ("kq_kernels.hip", "kq_device.h", "kq_capi.hip", "kq_internal.h"):
         with open(os.path.join(ROOT, "mxfp4_act_quantizer_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

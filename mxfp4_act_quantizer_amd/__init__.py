@@ -16,7 +16,7 @@ _BINDING_NAMES = (
     "kq_block_inverse", "kq_block_matrix", "kq_build_info", "kq_factor_inverse", "kq_fold_weight", "kq_quantize",
     "kq_quantize_ex", "kq_status_string", "kq_transform_f32", "lib", "mx_quantize_f32", "set_tuning",
     "sq_quantize", "measure_copy41", "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize",
-    "fwht_transform_f32", "kq_lu_factors", "mx_gemm",
+    "fwht_transform_f32", "kq_lu_factors", "mx_gemm", "kq_adaln_quantize", "adaln_modulate",
 )
 __all__ = list(_BINDING_NAMES)
 

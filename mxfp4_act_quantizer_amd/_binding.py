@@ -31,7 +31,7 @@ EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
     "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors", "mx_gemm",
-    "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
+    "kq_adaln_quantize", "adaln_modulate", "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -54,6 +54,8 @@ _lib.fwht_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.fwht_transform_f32.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.kq_lu_factors.argtypes = [_P, _I64, _P]
 _lib.mx_gemm.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]
+_lib.kq_adaln_quantize.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P]
+_lib.adaln_modulate.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
 _lib.kq_block_matrix.argtypes = [_P, _I64, _P]
 _lib.kq_block_inverse.argtypes = [_P, _I64, _P]
@@ -274,11 +276,40 @@ def mx_quantize_f32(x, q=None, s=None, stream=None):
     return q, s
 
 
+def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, s=None, stream=None):
+    """AdaLN front-end fused with the quantizer: x = LN(h) (1 + scale[b]) +
+    shift[b] (b = row // tokens_per_sample) rounded to bf16, then the
+    butterfly transform and MXFP4.  Returns (q, s)."""
+    torch = _torch()
+    M, d = _md(h)
+    q, s = _outputs(h, M, d, q, s)
+    st = _lib.kq_adaln_quantize(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
+                                _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
+                                _dev(factors, (torch.float32,), "factors"), _nT(factors), _dev(q, (torch.uint8,), "q"),
+                                _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    _check(st, "kq_adaln_quantize")
+    return q, s
+
+
+def adaln_modulate(h, shift, scale, tokens_per_sample, eps, x=None, stream=None):
+    """The AdaLN front-end alone: x (bf16 [M, d]) as kq_adaln_quantize computes it."""
+    torch = _torch()
+    M, d = _md(h)
+    if x is None:
+        x = torch.empty((M, d), dtype=torch.bfloat16, device=h.device)
+    st = _lib.adaln_modulate(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
+                             _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
+                             _dev(x, _bf16_types(), "x"), _stream_handle(stream))
+    _check(st, "adaln_modulate")
+    return x
+
+
 def set_tuning(key, value):
     """Launch-shape knobs for measurements (0 = automatic everywhere): 0 MFMA tiles
     per workgroup, 1 butterfly rows/wave, 2 SmoothQuant/fp32 rows/wave, 3 MFMA
     token groups (1 contiguous, 2 interleaved), 4 MFMA strip width (8 or 16
-    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat)."""
+    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat), 6 AdaLN rows per
+    workgroup."""
     _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
 
 

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkroquant.so")
-SOURCES = ["kq_kernels.hip", "kq_capi.hip", "kq_host.cpp", "kq_measure.hip", "kq_gemm.hip"]
+SOURCES = ["kq_kernels.hip", "kq_capi.hip", "kq_host.cpp", "kq_measure.hip", "kq_gemm.hip", "kq_adaln.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

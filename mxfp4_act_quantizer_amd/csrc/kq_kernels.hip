@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kq_device.h"
 #include "kq_internal.h"
 
 namespace kq {
@@ -42,62 +43,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0, 0, 0, 0};
+    static Tuning t{0, 0, 0, 0, 0, 0, 0};
     return t;
-}
-
-// ---------------------------------------------------------------------------
-// MX step pieces
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float amax_step(float m, float a) { return vmax(m, __builtin_fabsf(a)); }
-
-// E8M0 byte of a block whose |max| is amax (amax >= 0 or NaN):
-// E = floor(log2 amax) - 2 = expfield - 129, clamped below at -127 (byte 0);
-// amax = 0 and fp32 subnormals land on byte 0; NaN / Inf give 0xFF.
-__device__ __forceinline__ unsigned e8m0_byte(float amax)
-{
-    unsigned e = (__float_as_uint(amax) >> 23) & 0xFFu;
-    unsigned b = (e < 2u ? 2u : e) - 2u;
-    return e == 0xFFu ? 0xFFu : b;
-}
-
-// The convert instruction takes 2^E from the exponent field of a float.
-__device__ __forceinline__ float scale_operand(unsigned byte) { return __uint_as_float(byte << 23); }
-
-// Eight values -> one dword of packed FP4 (value 2k in bits 8k..8k+3).
-__device__ __forceinline__ unsigned cvt8(float v0, float v1, float v2, float v3, float v4, float v5, float v6,
-                                         float v7, float sc)
-{
-    unsigned w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, v1, sc, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v2, v3, sc, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v4, v5, sc, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v6, v7, sc, 3);
-    return w;
-}
-
-// Raw buffer resources for the outputs.  Stores whose offset is at or past
-// num_records are dropped by the hardware range check, which masks lanes
-// (tail rows, a missing block) without a branch in the hot loop.
-constexpr unsigned kBufWord3 = 0x00020000u; // gfx9-family raw buffer descriptor flags
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_buffer(void *base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, kBufWord3);
-}
-
-__device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// DPP quad permutes: partner lane^1 and lane^2.
-__device__ __forceinline__ float dpp_xor1(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
 // ---------------------------------------------------------------------------
@@ -443,51 +390,6 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
 // ---------------------------------------------------------------------------
 enum StreamMode { kSQ = 0, kMXF32 = 1, kBflyQ = 2, kBflyT = 3, kFwhtQ = 4, kFwhtT = 5 };
 
-// Per-lane constants of the butterfly for its block's factor set.
-// The lane's channels are 8*qp + e of the block (qp = lane%4): index bits 4
-// and 3 are the lane's quad position, bits 2..0 are e.
-struct Bfly {
-    float a3[4], a4[4], a5[4]; // full 2x2 factors for the in-lane stages
-    float s1, o1, s2, o2;      // cross-lane stages: coefficient on own / partner value
-};
-
-__device__ __forceinline__ void bfly_setup(Bfly &B, const float *__restrict__ F, int qp)
-{
-    const int b4 = (qp >> 1) & 1, b3 = qp & 1;
-    // stage on index bit 4 (A1) and bit 3 (A2): new(self) = A[b][b] self + A[1-b][b] other
-    B.s1 = F[0 + b4 * 2 + b4];
-    B.o1 = F[0 + (1 - b4) * 2 + b4];
-    B.s2 = F[4 + b3 * 2 + b3];
-    B.o2 = F[4 + (1 - b3) * 2 + b3];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        B.a3[k] = F[8 + k];
-        B.a4[k] = F[12 + k];
-        B.a5[k] = F[16 + k];
-    }
-}
-
-// In-lane stage on index bit (stride st): pairs (u at bit 0, w at bit 1):
-// u' = A00 u + A10 w, w' = A01 u + A11 w.  The last stage starts each sum
-// from +0 so no result is -0.
-template <int ST, bool kLast>
-__device__ __forceinline__ void bfly_inlane(float (&v)[8], const float (&A)[4])
-{
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (i & ST)
-            continue;
-        const float u = v[i], w = v[i + ST];
-        if (kLast) {
-            v[i] = __builtin_fmaf(A[0], u, __builtin_fmaf(A[2], w, 0.0f));
-            v[i + ST] = __builtin_fmaf(A[1], u, __builtin_fmaf(A[3], w, 0.0f));
-        } else {
-            v[i] = __builtin_fmaf(A[0], u, A[2] * w);
-            v[i + ST] = __builtin_fmaf(A[1], u, A[3] * w);
-        }
-    }
-}
-
 // Unnormalised Walsh-Hadamard stage on an in-lane index bit (stride ST):
 // pairs (u at bit 0, w at bit 1) become (u + w, u - w).
 template <int ST>
@@ -558,22 +460,8 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
             for (int i = 0; i < 8; ++i)
                 v[i] = __builtin_fmaf(v[i], r[i], 0.0f); // one rounding; -0 -> +0
         }
-        if constexpr (kMode == kBflyQ || kMode == kBflyT) {
-            // cross-lane stages first (index bits 4 and 3), then in-lane bits 2, 1, 0
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float other = dpp_xor2(v[i]);
-                v[i] = __builtin_fmaf(B.o1, other, B.s1 * v[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float other = dpp_xor1(v[i]);
-                v[i] = __builtin_fmaf(B.o2, other, B.s2 * v[i]);
-            }
-            bfly_inlane<4, false>(v, B.a3);
-            bfly_inlane<2, false>(v, B.a4);
-            bfly_inlane<1, true>(v, B.a5);
-        }
+        if constexpr (kMode == kBflyQ || kMode == kBflyT)
+            bfly_stages(v, B);
         if constexpr (kMode == kFwhtQ || kMode == kFwhtT) {
             // Walsh-Hadamard comparison transform: the same five stages with
             // fixed +-1 coefficients.  Cross-lane bits 4 and 3: a lane at bit
@@ -602,17 +490,8 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
                 o[1] = f32x4{v[4], v[5], v[6], v[7]};
             }
         } else {
-            float am = __builtin_fabsf(v[0]);
-#pragma unroll
-            for (int i = 1; i < 8; ++i)
-                am = amax_step(am, v[i]);
-            am = vmax(am, dpp_xor1(am));
-            am = vmax(am, dpp_xor2(am));
-            const unsigned b = e8m0_byte(am);
-            const float sc = scale_operand(b);
-            unsigned w = cvt8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
-            if (b == 0xFFu)
-                w = 0u;
+            unsigned b;
+            const unsigned w = mx_encode_quad(v, b);
             // rows past the run fall outside the wave's ranges; lanes past the row
             // end (and three of the four lanes of a block for s) set bit 31 of their offset
             const int mr = (int)(mm - m0);

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "kroquant.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kq_\w+|sq_\w+|mx_\w+|fwht_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kq_\w+|sq_\w+|mx_\w+|fwht_\w+|adaln_\w+)\s*\(", src, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -290,3 +290,40 @@ def test_mx_gemm_validation():
     assert raw("mx_gemm", qa, sa, 4, qb, sb, 4, 64, qa + 16, 0, None) == K.KQ_ERR_OVERLAP
     assert raw("mx_gemm", None, None, 0, None, None, 4, 64, None, 0, None) == K.KQ_OK
     assert raw("mx_gemm", qa, sa, 4, qb, sb, (1 << 21) + 1, 64, out, 0, None) == K.KQ_ERR_SHAPE
+
+
+def test_adaln_validation():
+    h, sh, sc, f, q, s, x = (FAKE + (k << 30) for k in range(7))
+    ok = dict(T=2, eps=1e-6)
+
+    def fused(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], f=f, nT=1, q=q, s=s):
+        return raw("kq_adaln_quantize", h, M, d, sh, sc, T, eps, f, nT, q, s, None)
+
+    def alone(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], x=x):
+        return raw("adaln_modulate", h, M, d, sh, sc, T, eps, x, None)
+
+    assert fused(d=48) == K.KQ_ERR_SHAPE
+    assert fused(d=8192 + 32) == K.KQ_ERR_SHAPE  # a workgroup holds whole rows
+    assert fused(nT=3) == K.KQ_ERR_SHAPE
+    assert fused(T=0) == K.KQ_ERR_ARG
+    for e in (0.0, -1.0, float("inf"), float("nan")):
+        assert fused(eps=e) == K.KQ_ERR_ARG
+    assert fused(M=-1) == K.KQ_ERR_ARG
+    assert fused(h=None) == K.KQ_ERR_ARG
+    assert fused(sc=None) == K.KQ_ERR_ARG
+    assert fused(f=None) == K.KQ_ERR_ARG
+    assert fused(h=h + 2) == K.KQ_ERR_ALIGN
+    assert fused(q=q + 8) == K.KQ_ERR_ALIGN
+    assert fused(sh=sh + 2) == K.KQ_ERR_ALIGN
+    assert fused(q=h + 16) == K.KQ_ERR_OVERLAP
+    assert fused(s=sh + 4) == K.KQ_ERR_OVERLAP
+    assert fused(s=q + 8) == K.KQ_ERR_OVERLAP
+    assert fused(f=q + 16) == K.KQ_ERR_OVERLAP
+    assert fused(M=0, h=None, q=None) == K.KQ_OK
+    assert alone(d=8192 + 32) == K.KQ_ERR_SHAPE
+    assert alone(x=None) == K.KQ_ERR_ARG
+    assert alone(x=x + 8) == K.KQ_ERR_ALIGN
+    assert alone(x=sc) == K.KQ_ERR_OVERLAP
+    assert alone(x=h + 64) == K.KQ_ERR_OVERLAP
+    assert alone(T=-3) == K.KQ_ERR_ARG
+    assert alone(M=0, x=None) == K.KQ_OK
