@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--all-configs", action="store_true",
                     help="per-configuration table: KroQuant (MFMA per-block and shared, butterfly), SmoothQuant "
                          "and the copy ceiling, each timed alone")
+    ap.add_argument("--adaln", action="store_true",
+                    help="AdaLN front-end fused with the quantizer against the unfused pipeline, hidden widths")
     ap.add_argument("--gemm", action="store_true",
                     help="W4A4 consumer (mx_gemm) on the DiT layer shapes, against its roofline")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -394,15 +396,139 @@ def gemm_bench(args):
                       "frac": round(tot_roof / tot_us, 4)}), flush=True)
 
 
+def _time_leg(fn, nsets, steps):
+    """Average time of one call of fn(set index): a graph of `steps` calls over
+    the rotating sets, captured on a side stream, replayed after the clocks
+    are up, timed with HIP events on that stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        fn(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(steps):
+                fn(i % nsets)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:  # clocks up
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        e0.record(cs)
+        g.replay()
+        e1.record(cs)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+ADALN_WORKLOADS = ("dit_1152", "mid_2240", "dbl_3072")  # the hidden widths AdaLN normalises
+ADALN_EPS = 1e-6
+
+
+def adaln_bench(args):
+    """The AdaLN front-end fused with the quantizer (kq_adaln_quantize) against
+    the unfused pipeline (adaln_modulate writing bf16 x, then kq_quantize with
+    the MFMA or the butterfly transform) and against torch's layer_norm and
+    modulation (bf16 out) followed by kq_quantize, at the hidden widths, two samples
+    (CFG) per batch.  Fused algorithmic bytes: 2.53125 B per element (h read,
+    codes and scales written) plus the modulation; unfused: 6.53125 (x
+    written and read back).  Per-block factor sets; h drawn on the GPU as
+    N(0,1) with 1% outlier channels x50 (the time does not depend on the
+    values)."""
+    import torch
+
+    import mxfp4_act_quantizer_amd as K
+    from synth import inputs as I
+    dev = torch.device("cuda:0")
+    rows = []
+    for name in ADALN_WORKLOADS:
+        M, d, _ = I.CONFIGS[name]
+        T = I.tokens_per_sample(name)
+        elems = M * d
+        alg = elems * BYTES_PER_ELEM
+        nsets = max(2, int(np.ceil(ROTATE_BYTES / alg)))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(I.data_seed(name))
+        chan = torch.ones(d, device=dev)
+        chan[torch.randperm(d, generator=gen, device=dev)[:max(1, d // 100)]] = 50.0
+        shift, scale = (torch.from_numpy(a).to(dev) for a in I.adaln_modulation((M + T - 1) // T, d, I.adaln_seed(name)))
+        f = torch.from_numpy(I.random_factors(d // 32, I.factor_seed(name))).to(dev)
+        sets = []
+        for _ in range(nsets):
+            sets.append(dict(h=(torch.randn(M, d, generator=gen, device=dev) * chan).to(torch.bfloat16),
+                             x=torch.empty((M, d), dtype=torch.bfloat16, device=dev),
+                             q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
+                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev),
+                             w=torch.empty((M, 2), dtype=torch.float64, device=dev)))
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream
+
+        def fused(i):
+            b = sets[i]
+            K.kq_adaln_quantize(b["h"], shift, scale, T, ADALN_EPS, f, b["q"], b["s"], stats=b["w"], stream=cur())
+
+        def modulate(i):
+            b = sets[i]
+            K.adaln_modulate(b["h"], shift, scale, T, ADALN_EPS, b["x"], stats=b["w"], stream=cur())
+
+        def unfused(variant):
+            def run(i):
+                b = sets[i]
+                K.adaln_modulate(b["h"], shift, scale, T, ADALN_EPS, b["x"], stats=b["w"], stream=cur())
+                K.kq_quantize(b["x"], f, b["q"], b["s"], stream=cur(), variant=variant)
+            return run
+
+        nS = (M + T - 1) // T
+
+        def torch_unfused(i):
+            # torch's own layer norm and modulation (several kernels, bf16 out), then the quantizer
+            b = sets[i]
+            n = torch.nn.functional.layer_norm(b["h"], (d,), eps=ADALN_EPS)
+            if M % T == 0:
+                x = (n.view(nS, T, d) * (1.0 + scale[:, None, :]) + shift[:, None, :]).to(torch.bfloat16).view(M, d)
+            else:
+                idx = torch.arange(M, device=dev) // T
+                x = (n * (1.0 + scale[idx]) + shift[idx]).to(torch.bfloat16)
+            K.kq_quantize(x, f, b["q"], b["s"], stream=cur())
+
+        t = {"fused": _time_leg(fused, nsets, args.steps),
+             "torch_layernorm_then_kq_mfma": _time_leg(torch_unfused, nsets, args.steps),
+             "unfused_mfma": _time_leg(unfused(1), nsets, args.steps),
+             "unfused_butterfly": _time_leg(unfused(2), nsets, args.steps),
+             "modulate_alone": _time_leg(modulate, nsets, args.steps)}
+        fused_gbs = alg / t["fused"] / 1e9
+        row = {"workload": name, "M": M, "d": d, "tokens_per_sample": T,
+               "us": {k: round(v * 1e6, 2) for k, v in t.items()},
+               "fused_GB/s": round(fused_gbs, 1),
+               "fused_roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4)},
+               "fused_speedup_vs_unfused_mfma": round(t["unfused_mfma"] / t["fused"], 3),
+               "fused_speedup_vs_unfused_butterfly": round(t["unfused_butterfly"] / t["fused"], 3),
+               "fused_speedup_vs_torch_layernorm": round(t["torch_layernorm_then_kq_mfma"] / t["fused"], 3),
+               "unfused_mfma_GB/s_at_6.53B": round(elems * 6.53125 / t["unfused_mfma"] / 1e9, 1)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
-    if args.all_configs or args.gemm:
+    if args.all_configs or args.gemm or args.adaln:
         if args.gpus != 1:
             sys.exit(2)
-        all_configs(args) if args.all_configs else gemm_bench(args)
+        if args.all_configs:
+            all_configs(args)
+        elif args.gemm:
+            gemm_bench(args)
+        else:
+            adaln_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "

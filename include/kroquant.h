@@ -160,32 +160,36 @@ int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *
  * (mean and biased variance over the row's d channels; LayerNorm without a
  * learned affine - a reading, the pages print no formula), x rounded to bf16
  * (nearest, ties to even) from its double value, then the Kronecker transform
- * of every 32-channel block and MXFP4 as kq_quantize, in one pass over h: the
- * normalised activation is never written.  The transform is the butterfly
- * form (KQ_VARIANT_BUTTERFLY); the result equals
+ * of every 32-channel block and MXFP4 as kq_quantize.  The normalised x is
+ * never written: one pass writes the row statistics into `stats`, a second
+ * reads h again and quantizes.  The transform is the butterfly form
+ * (KQ_VARIANT_BUTTERFLY); the result equals
  * kq_quantize_ex(adaln_modulate(h), ..., KQ_VARIANT_BUTTERFLY) bit for bit.
- *   h      dev, bf16 [M, d] (the residual stream), 16-byte aligned, d <= 8192
+ *   h      dev, bf16 [M, d] (the residual stream), 16-byte aligned
  *   shift  dev, float32 [ceil(M / tokens_per_sample), d], 4-byte aligned
  *   scale  dev, float32, same shape and alignment as shift
  *   tokens_per_sample  >= 1 (rows of one sample are consecutive)
  *   eps    > 0 and finite (KQ_ERR_ARG otherwise)
+ *   stats  dev, float64 [M, 2], 8-byte aligned: workspace owned by the caller
+ *          (row mean and 1/sqrt(var + eps), overwritten; its contents after
+ *          the call are those values, in double)
  *   factors, nT, q, s  as kq_quantize
- * Statistics and normalisation run in double.  d > 8192 is KQ_ERR_SHAPE (a
- * workgroup holds whole rows).  Outputs may not overlap h, shift, scale or
- * each other (KQ_ERR_OVERLAP).  Otherwise the same contract as kq_quantize.
+ * Statistics and normalisation run in double.  Two launches on `stream`.
+ * Outputs and the workspace may not overlap h, shift, scale, factors or each
+ * other (KQ_ERR_OVERLAP).  Otherwise the same contract as kq_quantize.
  */
 int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
-                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
-                      void *stream);
+                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
+                      uint8_t *q, uint8_t *s, void *stream);
 
 /*
  * adaln_modulate: the same normalisation alone (the unfused front-end): x as
  * kq_adaln_quantize computes it, written as bf16.
- *   x  dev, bf16 [M, d], 16-byte aligned, not overlapping h, shift or scale
+ *   x  dev, bf16 [M, d], 16-byte aligned, not overlapping h, shift, scale or stats
  * Same arguments and errors as kq_adaln_quantize otherwise.
  */
 int adaln_modulate(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
-                   int64_t tokens_per_sample, float eps, uint16_t *x, void *stream);
+                   int64_t tokens_per_sample, float eps, double *stats, uint16_t *x, void *stream);
 
 /*
  * mx_gemm: the W4A4 consumer of the quantizer's output (abstract: MXFP4 W4A4,

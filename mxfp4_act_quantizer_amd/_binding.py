@@ -54,8 +54,8 @@ _lib.fwht_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.fwht_transform_f32.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.kq_lu_factors.argtypes = [_P, _I64, _P]
 _lib.mx_gemm.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]
-_lib.kq_adaln_quantize.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P]
-_lib.adaln_modulate.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P]
+_lib.kq_adaln_quantize.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P, _P]
+_lib.adaln_modulate.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
 _lib.kq_block_matrix.argtypes = [_P, _I64, _P]
 _lib.kq_block_inverse.argtypes = [_P, _I64, _P]
@@ -276,30 +276,42 @@ def mx_quantize_f32(x, q=None, s=None, stream=None):
     return q, s
 
 
-def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, s=None, stream=None):
+def _stats(h, M, stats):
+    torch = _torch()
+    if stats is None:
+        stats = torch.empty((M, 2), dtype=torch.float64, device=h.device)
+    return stats
+
+
+def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, s=None, stats=None, stream=None):
     """AdaLN front-end fused with the quantizer: x = LN(h) (1 + scale[b]) +
     shift[b] (b = row // tokens_per_sample) rounded to bf16, then the
-    butterfly transform and MXFP4.  Returns (q, s)."""
+    butterfly transform and MXFP4.  `stats` is the [M, 2] float64 workspace
+    (allocated here when not given).  Returns (q, s)."""
     torch = _torch()
     M, d = _md(h)
     q, s = _outputs(h, M, d, q, s)
+    stats = _stats(h, M, stats)
     st = _lib.kq_adaln_quantize(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
                                 _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
-                                _dev(factors, (torch.float32,), "factors"), _nT(factors), _dev(q, (torch.uint8,), "q"),
+                                _dev(factors, (torch.float32,), "factors"), _nT(factors),
+                                _dev(stats, (torch.float64,), "stats"), _dev(q, (torch.uint8,), "q"),
                                 _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
     _check(st, "kq_adaln_quantize")
     return q, s
 
 
-def adaln_modulate(h, shift, scale, tokens_per_sample, eps, x=None, stream=None):
+def adaln_modulate(h, shift, scale, tokens_per_sample, eps, x=None, stats=None, stream=None):
     """The AdaLN front-end alone: x (bf16 [M, d]) as kq_adaln_quantize computes it."""
     torch = _torch()
     M, d = _md(h)
     if x is None:
         x = torch.empty((M, d), dtype=torch.bfloat16, device=h.device)
+    stats = _stats(h, M, stats)
     st = _lib.adaln_modulate(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
                              _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
-                             _dev(x, _bf16_types(), "x"), _stream_handle(stream))
+                             _dev(stats, (torch.float64,), "stats"), _dev(x, _bf16_types(), "x"),
+                             _stream_handle(stream))
     _check(st, "adaln_modulate")
     return x
 

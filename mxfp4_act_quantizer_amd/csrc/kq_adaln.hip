@@ -1,4 +1,4 @@
-// AdaLN front-end of the KroQuant quantizer, fused (pages describing arXiv
+// AdaLN front-end of the KroQuant quantizer (pages describing arXiv
 // 2607.21446: the abstract on the mlsanity.com paper page says the
 // normalisation layers between transformer blocks force the transform to run
 // online at every step; the pith.science verdict record's
@@ -7,20 +7,27 @@
 // Per token row m (sample b = m / T):
 //   x_c = (h_c - mean) / sqrt(var + eps) * (1 + scale[b][c]) + shift[b][c]
 // (LayerNorm without affine, biased variance), rounded to bf16, then the
-// Kronecker transform of every 32-channel block and MXFP4 - in one pass over
-// h, so the normalised x never goes to memory.
+// Kronecker transform of every 32-channel block and MXFP4.  The normalised x
+// never goes to memory.
 //
-// Structure: a workgroup spans whole rows (one wave per 512 channels, up to
-// 16 waves, so d <= 8192: the hidden widths AdaLN normalises) and walks a run
-// of rows, two at a time.  Each lane keeps its 8 channels for the whole run:
-// its butterfly factors and the current sample's modulation stay in
-// registers.  Row statistics: each lane sums its values and squares in fp64,
-// the wave reduces, the waves meet in LDS, and every wave adds the partials
-// in the same order, so all waves (and the x-writing variant) see identical
-// mean and 1/sqrt(var + eps).  The per-element arithmetic is fp64 and the
-// bf16 rounding is taken from the double value.  The transform is the
-// butterfly (five DPP / in-lane 2x2 stages) shared with kq_quantize_ex's
-// butterfly variant, and the encoding is the shared MX step.
+// Two streaming kernels, no barriers:
+//   adaln_stats_kernel   one wave per run of rows: per row, the sum and the
+//                        sum of squares of h in fp64 (lane-strided over the
+//                        row, then a wave reduction), mean and
+//                        1/sqrt(var + eps) in fp64 into a 16-byte record.
+//                        h is read with the default cache policy so that the
+//                        second pass finds it in the caches.
+//   adaln_stream_kernel  the streaming quantizer's structure (one lane per 8
+//                        channels, a wave per 512-channel column tile walking
+//                        a run of rows): the row's record arrives by scalar
+//                        loads, the lane's modulation and butterfly factors
+//                        stay in registers; per element fp64 normalisation,
+//                        bf16 rounding from the double value, then the
+//                        butterfly transform and MX step shared with
+//                        kq_quantize_ex's butterfly variant (kQuant), or the
+//                        bf16 x written out (the unfused front-end).
+// Both modes read the same records, so the fused result equals the butterfly
+// quantizer applied to the written x bit for bit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,24 +39,49 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kU = 2;      // rows per step
-constexpr int kMaxW = 16;  // waves per workgroup: 16 x 512 channels = the widest row
-constexpr int kAuxNTa = 2; // nontemporal loads: h is read once
+constexpr int kAuxNTa = 2;   // nontemporal: the second pass reads h for the last time
+constexpr int kStatRows = 2;   // rows per wave of the statistics kernel
+constexpr int kStatChunks = 4; // 16-byte pieces per lane and row loaded at a time
+constexpr int kU = 4;        // rows per pipeline stage of the streaming pass
 
-// bf16 bits of (h - mu) * (rstd * g) + t, computed in double and rounded once
-// to the nearest bf16 (ties to even).  The double -> float conversion rounds
-// to nearest even; only when that lands exactly on a bf16 midpoint can the
-// second rounding differ from a direct one, and then the sign of the (exact)
-// remainder v - f decides.
-__device__ __forceinline__ unsigned adaln_bf16(float h, double mu, double rstd, double g, double t)
+// x = (h - mu) * (rstd * g) + t in double for 8 channels, rounded once to the
+// nearest bf16 (ties to even) and packed two per dword.  The double -> float
+// conversion rounds to nearest even and the hardware bf16 convert rounds the
+// float to nearest even; the two steps differ from one direct rounding only
+// when the float lands exactly on a bf16 midpoint (low 16 bits 0x8000) while
+// the double is not the float: then the sign of the exact remainder v - f
+// decides.  That case is rare and taken as a branch.
+__device__ __forceinline__ void adaln_bf16x8(const u32x4 &hv, double mu, double rstd, const double (&g)[8],
+                                             const double (&t)[8], unsigned (&xw)[4])
 {
-    const double v = __builtin_fma((double)h - mu, rstd * g, t);
-    const float f = (float)v;
-    const double r = v - (double)f;
-    const unsigned b = __float_as_uint(f);
-    if ((b & 0xFFFFu) == 0x8000u && r != 0.0)
-        return ((r > 0.0) == (f > 0.0)) ? (b + 0x8000u) >> 16 : b >> 16;
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+    double v[8];
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float hf = (e & 1) ? bf16hi(hv[e >> 1]) : bf16lo(hv[e >> 1]);
+        v[e] = __builtin_fma((double)hf - mu, rstd * g[e], t[e]);
+        f[e] = (float)v[e];
+    }
+    bool mid = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        mid |= (__float_as_uint(f[e]) & 0xFFFFu) == 0x8000u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xw[i] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f[2 * i]) |
+                ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)f[2 * i + 1]) << 16);
+    if (mid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned b = __float_as_uint(f[e]);
+            const double r = v[e] - (double)f[e];
+            if ((b & 0xFFFFu) == 0x8000u && r != 0.0) {
+                const unsigned x16 = ((r > 0.0) == (f[e] > 0.0)) ? (b + 0x8000u) >> 16 : b >> 16;
+                const int sh = 16 * (e & 1);
+                xw[e >> 1] = (xw[e >> 1] & ~(0xFFFFu << sh)) | (x16 << sh);
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -60,23 +92,72 @@ __device__ __forceinline__ double wave_sum(double v)
     return v;
 }
 
-struct HRows {
-    u32x4 v[kU]; // the lane's 8 channels of kU rows
-};
-
-// rows mr .. mr + kU - 1 of the run (relative to its first row); rows past the
-// run and lanes past the row end fall outside the range: zeros, no access
-__device__ __forceinline__ void load_h(HRows &in, __amdgpu_buffer_rsrc_t rh, int mr, int d, unsigned lane_off)
+// ---------------------------------------------------------------------------
+// Row statistics: wave w of the grid takes rows kStatRows w .. + kStatRows-1,
+// kStatChunks 16-byte pieces of each row per lane in flight at a time.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void adaln_stats_kernel(const uint16_t *__restrict__ h, int64_t M, int d, float eps,
+                                                          double *__restrict__ stats)
 {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = wave * kStatRows;
+    if (m0 >= M)
+        return; // wave-uniform; no barrier in this kernel
+    const int64_t rows = (M - m0) < kStatRows ? (M - m0) : kStatRows;
+    const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + m0 * d), rows * d * 2);
+    const int nOct = d >> 3;
+    double s1[kStatRows], s2[kStatRows];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-        in.v[u] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)((mr + u) * d * 2) + lane_off), 0, kAuxNTa));
+    for (int j = 0; j < kStatRows; ++j)
+        s1[j] = s2[j] = 0.0;
+    // lane-strided over the row's 16-byte pieces; rows past the run and
+    // pieces past the row end fall outside the range and read as zeros
+    for (int base = 0; base < nOct; base += 64 * kStatChunks) {
+        u32x4 v[kStatRows][kStatChunks];
+#pragma unroll
+        for (int j = 0; j < kStatRows; ++j)
+#pragma unroll
+            for (int c = 0; c < kStatChunks; ++c) {
+                const int o = base + 64 * c + lane;
+                const unsigned drop = (unsigned)(o >= nOct) << 31;
+                v[j][c] = __builtin_bit_cast(
+                    u32x4,
+                    __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)(j * d * 2 + o * 16) | drop), 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < kStatRows; ++j)
+#pragma unroll
+            for (int c = 0; c < kStatChunks; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const double a = (double)bf16lo(v[j][c][i]), e = (double)bf16hi(v[j][c][i]);
+                    s1[j] += a;
+                    s2[j] = __builtin_fma(a, a, s2[j]);
+                    s1[j] += e;
+                    s2[j] = __builtin_fma(e, e, s2[j]);
+                }
+    }
+#pragma unroll
+    for (int j = 0; j < kStatRows; ++j) {
+        const double t1 = wave_sum(s1[j]), t2 = wave_sum(s2[j]);
+        if (j < rows && lane == j) {
+            const double mu = t1 / (double)d;
+            double var = t2 / (double)d - mu * mu;
+            var = var > 0.0 ? var : 0.0;
+            stats[2 * (m0 + j)] = mu;
+            stats[2 * (m0 + j) + 1] = 1.0 / sqrt(var + (double)eps);
+        }
+    }
 }
 
+// ---------------------------------------------------------------------------
+// Second pass: normalise, modulate, round to bf16, then transform + MXFP4 or
+// write x.
+// ---------------------------------------------------------------------------
 struct Modulation {
-    float g[8], t[8]; // scale and shift of the lane's channels for the current sample
-    int64_t next;     // first row of the next sample
+    double g[8], t[8]; // 1 + scale and shift of the lane's channels for the current sample
+    int64_t next;      // first row of the next sample
 };
 
 __device__ __forceinline__ void load_modulation(Modulation &md, const float *__restrict__ shift,
@@ -85,72 +166,48 @@ __device__ __forceinline__ void load_modulation(Modulation &md, const float *__r
     md.next = (b + 1) * T;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        md.g[e] = scale[b * d + octc * 8 + e];
-        md.t[e] = shift[b * d + octc * 8 + e];
+        md.g[e] = 1.0 + (double)scale[b * d + octc * 8 + e];
+        md.t[e] = (double)shift[b * d + octc * 8 + e];
     }
 }
 
-// One step of kU rows: statistics, then normalise, modulate, round to bf16
-// and either write x (kQuant false) or transform and quantize.
+struct HRows {
+    u32x4 v[kU];
+};
+
+__device__ __forceinline__ void load_rows(HRows &in, __amdgpu_buffer_rsrc_t rh, int mr, int d, unsigned lane_off)
+{
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+        in.v[u] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)((mr + u) * d * 2) + lane_off), 0, kAuxNTa));
+}
+
 template <bool kQuant>
-__device__ __forceinline__ void adaln_rows(const HRows &in, double (&part)[kU][kMaxW][2], int64_t m, int64_t m0,
-                                           int64_t m1, int d, int nW, int wave, int lane, float eps, int64_t T,
-                                           const float *__restrict__ shift, const float *__restrict__ scale,
-                                           Modulation &md, int oct, int octc, bool cok, const Bfly &B,
-                                           __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
-                                           __amdgpu_buffer_rsrc_t rxo)
+__device__ __forceinline__ void adaln_process(const HRows &in, int64_t m, int64_t m0, int64_t m1, int d, int oct,
+                                              int octc, bool cok, int qp, const double *__restrict__ stats,
+                                              const float *__restrict__ shift, const float *__restrict__ scale,
+                                              int64_t T, Modulation &md, const Bfly &B, __amdgpu_buffer_rsrc_t rq,
+                                              __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rxo)
 {
     const int nB = d >> 5;
-    const int qp = lane & 3;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-        double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double a = (double)bf16lo(in.v[u][i]), c = (double)bf16hi(in.v[u][i]);
-            s1 += a;
-            s2 = __builtin_fma(a, a, s2);
-            s1 += c;
-            s2 = __builtin_fma(c, c, s2);
-        }
-        s1 = wave_sum(s1);
-        s2 = wave_sum(s2);
-        if (lane == 0) {
-            part[u][wave][0] = s1;
-            part[u][wave][1] = s2;
-        }
-    }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int64_t mm = m + u;
         if (mm >= m1)
-            break; // uniform over the workgroup
-        double s1 = 0.0, s2 = 0.0;
-        for (int w = 0; w < nW; ++w) {
-            s1 += part[u][w][0];
-            s2 += part[u][w][1];
-        }
-        const double mu = s1 / (double)d;
-        double var = s2 / (double)d - mu * mu;
-        var = var > 0.0 ? var : 0.0;
-        const double rstd = 1.0 / sqrt(var + (double)eps);
+            break; // wave-uniform
+        const double mu = stats[2 * mm], rstd = stats[2 * mm + 1];
         if (mm >= md.next)
             load_modulation(md, shift, scale, mm / T, T, d, octc);
-        unsigned xb[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xb[2 * i] = adaln_bf16(bf16lo(in.v[u][i]), mu, rstd, 1.0 + (double)md.g[2 * i], (double)md.t[2 * i]);
-            xb[2 * i + 1] =
-                adaln_bf16(bf16hi(in.v[u][i]), mu, rstd, 1.0 + (double)md.g[2 * i + 1], (double)md.t[2 * i + 1]);
-        }
+        unsigned xw[4];
+        adaln_bf16x8(in.v[u], mu, rstd, md.g, md.t, xw);
         const int mr = (int)(mm - m0);
         const unsigned drop = (unsigned)(cok ? 0 : 1) << 31;
         if constexpr (kQuant) {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                v[e] = __uint_as_float(xb[e] << 16);
+                v[e] = (e & 1) ? bf16hi(xw[e >> 1]) : bf16lo(xw[e >> 1]);
             bfly_stages(v, B);
             unsigned b;
             const unsigned w = mx_encode_quad(v, b);
@@ -159,79 +216,94 @@ __device__ __forceinline__ void adaln_rows(const HRows &in, double (&part)[kU][k
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)((unsigned)(mr * nB + (oct >> 2)) | drop_s), 0,
                                                  0);
         } else {
-            const u32x4 o = {xb[0] | xb[1] << 16, xb[2] | xb[3] << 16, xb[4] | xb[5] << 16, xb[6] | xb[7] << 16};
+            const u32x4 o = {xw[0], xw[1], xw[2], xw[3]};
             __builtin_amdgcn_raw_buffer_store_b128(o, rxo, (int)((unsigned)(mr * d * 2 + oct * 16) | drop), 0, 0);
         }
     }
 }
 
-// Workgroup: nW waves over whole rows (wave w owns channels 512 w ..
-// 512 w + 511), rows [m0, m0 + rows_per_wg).
+// A workgroup covers four column tiles of one run of rows; the runs are dealt
+// to the XCDs in turn (blockIdx % 8), all column groups of a run on one XCD.
 template <bool kQuant>
-__global__ __launch_bounds__(64 * kMaxW) void adaln_kernel(const uint16_t *__restrict__ h, int64_t M, int d,
+__global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__restrict__ h, int64_t M, int d,
+                                                           const double *__restrict__ stats,
                                                            const float *__restrict__ shift,
-                                                           const float *__restrict__ scale, int64_t T, float eps,
+                                                           const float *__restrict__ scale, int64_t T,
                                                            const float *__restrict__ factors, int per_block,
                                                            uint8_t *__restrict__ q, uint8_t *__restrict__ s,
-                                                           uint16_t *__restrict__ xo, int rows_per_wg)
+                                                           uint16_t *__restrict__ xo, int rows_per_wave, int nCT)
 {
-    __shared__ double part[2][kU][kMaxW][2]; // [step parity][row of the step][wave][sum, sum of squares]
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nW = blockDim.x >> 6;
-    const int64_t m0 = (int64_t)blockIdx.x * rows_per_wg;
-    const int64_t m1 = (m0 + rows_per_wg < M) ? m0 + rows_per_wg : M; // m0 < M: the grid covers M exactly
+    const int nCG = (nCT + 3) / 4;
+    const unsigned xcd = blockIdx.x % 8u;
+    const unsigned slot = blockIdx.x / 8u;
+    const int cg = (int)(slot % (unsigned)nCG);
+    const int64_t rg = (int64_t)(slot / (unsigned)nCG) * 8 + xcd;
+    const int ct = cg * 4 + (threadIdx.x >> 6);
+    const int64_t m0 = rg * rows_per_wave;
+    if (m0 >= M || ct >= nCT)
+        return; // wave-uniform; no barrier in this kernel
+    const int64_t m1 = (m0 + rows_per_wave < M) ? m0 + rows_per_wave : M;
     const int nOct = d >> 3;
-    const int oct = wave * 64 + lane;
+    const int oct = ct * 64 + lane;
     const bool cok = oct < nOct;
     const int octc = cok ? oct : nOct - 1; // parameter index for lanes past the row end (nothing stored)
-    const unsigned lane_off = (unsigned)(oct * 16) | ((unsigned)(cok ? 0 : 1) << 31);
+    const int qp = lane & 3;
     const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + m0 * d), (m1 - m0) * d * 2);
+    const unsigned lane_off = (unsigned)(oct * 16) | ((unsigned)(cok ? 0 : 1) << 31);
+    HRows bufA, bufB;
+    load_rows(bufA, rh, 0, d, lane_off);
     const __amdgpu_buffer_rsrc_t rq = out_buffer(kQuant ? q + m0 * (d >> 1) : nullptr, kQuant ? (m1 - m0) * (d >> 1) : 0);
     const __amdgpu_buffer_rsrc_t rs = out_buffer(kQuant ? s + m0 * (d >> 5) : nullptr, kQuant ? (m1 - m0) * (d >> 5) : 0);
     const __amdgpu_buffer_rsrc_t rxo = out_buffer(kQuant ? nullptr : xo + m0 * d, kQuant ? 0 : (m1 - m0) * d * 2);
-
-    HRows bufA, bufB;
-    load_h(bufA, rh, 0, d, lane_off);
     Bfly B;
     if constexpr (kQuant)
-        bfly_setup(B, factors + (int64_t)(per_block ? (octc >> 2) : 0) * 20, lane & 3);
+        bfly_setup(B, factors + (int64_t)(per_block ? (octc >> 2) : 0) * 20, qp);
     Modulation md;
     load_modulation(md, shift, scale, m0 / T, T, d, octc);
 
-    // two-step pipeline; a prefetch past the run falls outside the range and fetches nothing
-    for (int64_t m = m0; m < m1; m += 2 * kU) {
-        load_h(bufB, rh, (int)(m + kU - m0), d, lane_off);
-        adaln_rows<kQuant>(bufA, part[0], m, m0, m1, d, nW, wave, lane, eps, T, shift, scale, md, oct, octc, cok, B,
-                           rq, rs, rxo);
-        if (m + kU >= m1)
-            break; // uniform
-        load_h(bufA, rh, (int)(m + 2 * kU - m0), d, lane_off);
-        adaln_rows<kQuant>(bufB, part[1], m + kU, m0, m1, d, nW, wave, lane, eps, T, shift, scale, md, oct, octc, cok,
-                           B, rq, rs, rxo);
+    // two-stage pipeline; a prefetch past the run falls outside the range and fetches nothing
+    int64_t m = m0;
+    for (; m + kU < m1; m += 2 * kU) {
+        load_rows(bufB, rh, (int)(m + kU - m0), d, lane_off);
+        adaln_process<kQuant>(bufA, m, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
+        load_rows(bufA, rh, (int)(m + 2 * kU - m0), d, lane_off);
+        adaln_process<kQuant>(bufB, m + kU, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
     }
+    if (m < m1)
+        adaln_process<kQuant>(bufA, m, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
 }
 
 } // namespace
 
 hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
-                        float eps, const float *factors, int64_t nT, uint8_t *q, uint8_t *s, uint16_t *x,
-                        hipStream_t stream)
+                        float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
+                        uint16_t *x, hipStream_t stream)
 {
-    const int nW = (int)((d / 8 + 63) / 64); // waves: 512 channels each
+    // pass 1: row statistics
+    const int64_t waves = (M + kStatRows - 1) / kStatRows;
+    const int64_t grid1 = (waves + 3) / 4;
+    // pass 2: runs of R rows, four column tiles per workgroup, runs dealt to the XCDs
+    const int nCT = (int)((d / 8 + 63) / 64);
     int R = tuning().adaln_rows_per_wg;
     if (R <= 0)
-        R = 8;
-    const int64_t grid = (M + R - 1) / R;
-    if (grid > 0x7FFFFFFF || nW > kMaxW)
+        R = 4; // one pipeline stage per wave: more, shorter waves (measured best of 4..32 on MI355X)
+    const int64_t nRG = (M + R - 1) / R;
+    const int64_t grid2 = (nRG + 7) / 8 * 8 * ((nCT + 3) / 4);
+    if (grid1 > 0x7FFFFFFF || grid2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;
+    void *args1[] = {(void *)&h, (void *)&M, (void *)&di, (void *)&eps, (void *)&stats};
+    hipError_t e = hipLaunchKernel((const void *)adaln_stats_kernel, dim3((unsigned)grid1), dim3(256), args1, 0, stream);
+    if (e != hipSuccess)
+        return e;
     int per_block = nT > 1 ? 1 : 0;
-    void *args[] = {(void *)&h, (void *)&M,   (void *)&di,      (void *)&shift,     (void *)&scale,
-                    (void *)&T, (void *)&eps, (void *)&factors, (void *)&per_block, (void *)&q,
-                    (void *)&s, (void *)&x,   (void *)&R};
-    const void *fn = x == nullptr ? (const void *)adaln_kernel<true> : (const void *)adaln_kernel<false>;
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * nW), args, 0, stream);
+    const double *cst = stats;
+    void *args2[] = {(void *)&h,     (void *)&M, (void *)&di,      (void *)&cst,       (void *)&shift,
+                     (void *)&scale, (void *)&T, (void *)&factors, (void *)&per_block, (void *)&q,
+                     (void *)&s,     (void *)&x, (void *)&R,       (void *)&nCT};
+    const void *fn = x == nullptr ? (const void *)adaln_stream_kernel<true> : (const void *)adaln_stream_kernel<false>;
+    return hipLaunchKernel(fn, dim3((unsigned)grid2), dim3(256), args2, 0, stream);
 }
 
 } // namespace kq

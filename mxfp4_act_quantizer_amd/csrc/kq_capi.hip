@@ -251,30 +251,31 @@ int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, 
     return hip_status(kq::launch_mx_gemm(qa, sa, M, qb, sb, N, K, out, out_bf16, (hipStream_t)stream));
 }
 
-// shared checks of the AdaLN entry points (h, shift, scale, T, eps); out and
-// out2 are the outputs, each with its byte count
+// shared checks of the AdaLN entry points (h, shift, scale, T, eps, the
+// statistics workspace); out and out2 are the outputs, each with its byte count
 static int check_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
-                       float eps, const void *out, int64_t ob, const void *out2, int64_t ob2)
+                       float eps, const double *stats, const void *out, int64_t ob, const void *out2, int64_t ob2)
 {
-    if (d > kq::kMaxAdalnD)
-        return KQ_ERR_SHAPE;
     if (T < 1 || !(eps > 0.0f) || eps > 3.0e38f)
         return KQ_ERR_ARG;
-    if (!h || !shift || !scale || !out)
+    if (!h || !shift || !scale || !stats || !out)
         return KQ_ERR_ARG;
-    if (!aligned(h, 16) || !aligned(out, 16) || !aligned(shift, 4) || !aligned(scale, 4))
+    if (!aligned(h, 16) || !aligned(out, 16) || !aligned(shift, 4) || !aligned(scale, 4) || !aligned(stats, 8))
         return KQ_ERR_ALIGN;
-    const int64_t hb = M * d * 2, pb = ((M + T - 1) / T) * d * 4;
-    if (overlap(out, ob, h, hb) || overlap(out, ob, shift, pb) || overlap(out, ob, scale, pb) ||
-        overlap(out2, ob2, h, hb) || overlap(out2, ob2, shift, pb) || overlap(out2, ob2, scale, pb) ||
-        overlap(out, ob, out2, ob2))
+    const int64_t hb = M * d * 2, pb = ((M + T - 1) / T) * d * 4, wb = M * 16;
+    const void *in[3] = {h, shift, scale};
+    const int64_t inb[3] = {hb, pb, pb};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(out, ob, in[i], inb[i]) || overlap(out2, ob2, in[i], inb[i]) || overlap(stats, wb, in[i], inb[i]))
+            return KQ_ERR_OVERLAP;
+    if (overlap(out, ob, out2, ob2) || overlap(stats, wb, out, ob) || overlap(stats, wb, out2, ob2))
         return KQ_ERR_OVERLAP;
     return KQ_OK;
 }
 
 int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
-                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
-                      void *stream)
+                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
+                      uint8_t *q, uint8_t *s, void *stream)
 {
     int st = check_md(M, d);
     if (st)
@@ -286,26 +287,28 @@ int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shif
     if (!s)
         return KQ_ERR_ARG;
     const int64_t qb = M * (d / 2), sb = M * (d / 32);
-    if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, q, qb, s, sb)))
+    if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, stats, q, qb, s, sb)))
         return st;
     if ((st = check_param(factors, nT * 20, h, M * d * 2, q, qb, s, sb)))
         return st;
-    return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, q, s, nullptr,
-                                       (hipStream_t)stream));
+    if (overlap(factors, nT * 80, stats, M * 16))
+        return KQ_ERR_OVERLAP;
+    return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, stats, q, s,
+                                       nullptr, (hipStream_t)stream));
 }
 
 int adaln_modulate(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
-                   int64_t tokens_per_sample, float eps, uint16_t *x, void *stream)
+                   int64_t tokens_per_sample, float eps, double *stats, uint16_t *x, void *stream)
 {
     int st = check_md(M, d);
     if (st)
         return st;
     if (M == 0)
         return KQ_OK;
-    if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, x, M * d * 2, nullptr, 0)))
+    if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, stats, x, M * d * 2, nullptr, 0)))
         return st;
-    return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, nullptr, 1, nullptr, nullptr, x,
-                                       (hipStream_t)stream));
+    return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, nullptr, 1, stats, nullptr,
+                                       nullptr, x, (hipStream_t)stream));
 }
 
 const char *kq_status_string(int status)

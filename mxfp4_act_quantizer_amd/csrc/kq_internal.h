@@ -30,20 +30,18 @@ hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8
 // (float32, or bf16 when bf16 != 0) = A[M, K] . B[N, K]^T
 hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
                           int64_t N, int64_t K, void *out, int bf16, hipStream_t stream);
-// AdaLN front-end: x = LayerNorm(h) (1 + scale[m / T]) + shift[m / T] rounded
-// to bf16, then (x null) the butterfly transform and MXFP4 into q, s, or
-// (x given) x written out.  d <= kMaxAdalnD.
+// AdaLN front-end: row statistics (mean, 1/sqrt(var + eps), fp64) into the
+// workspace stats [M, 2], then x = LayerNorm(h) (1 + scale[m / T]) +
+// shift[m / T] rounded to bf16 and either (x null) the butterfly transform and
+// MXFP4 into q, s, or (x given) x written out.  Two launches on `stream`.
 hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
-                        float eps, const float *factors, int64_t nT, uint8_t *q, uint8_t *s, uint16_t *x,
-                        hipStream_t stream);
+                        float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
+                        uint16_t *x, hipStream_t stream);
 // normalised Walsh-Hadamard-32 comparison: quantize (y null) or export y
 hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
 
 // Largest row count / width the launchers accept (grid and 32-bit lane math).
 constexpr int64_t kMaxD = (int64_t)1 << 20;
 constexpr int64_t kMaxBlocksTotal = (int64_t)1 << 40;
-// Widest row of the AdaLN front-end: a workgroup holds whole rows (16 waves
-// of 512 channels).
-constexpr int64_t kMaxAdalnD = 8192;
 
 } // namespace kq

@@ -293,17 +293,17 @@ def test_mx_gemm_validation():
 
 
 def test_adaln_validation():
-    h, sh, sc, f, q, s, x = (FAKE + (k << 30) for k in range(7))
+    h, sh, sc, f, q, s, x, w = (FAKE + (k << 30) for k in range(8))
     ok = dict(T=2, eps=1e-6)
 
-    def fused(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], f=f, nT=1, q=q, s=s):
-        return raw("kq_adaln_quantize", h, M, d, sh, sc, T, eps, f, nT, q, s, None)
+    def fused(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], f=f, nT=1, w=w, q=q, s=s):
+        return raw("kq_adaln_quantize", h, M, d, sh, sc, T, eps, f, nT, w, q, s, None)
 
-    def alone(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], x=x):
-        return raw("adaln_modulate", h, M, d, sh, sc, T, eps, x, None)
+    def alone(h=h, M=4, d=64, sh=sh, sc=sc, T=ok["T"], eps=ok["eps"], w=w, x=x):
+        return raw("adaln_modulate", h, M, d, sh, sc, T, eps, w, x, None)
 
     assert fused(d=48) == K.KQ_ERR_SHAPE
-    assert fused(d=8192 + 32) == K.KQ_ERR_SHAPE  # a workgroup holds whole rows
+    assert fused(d=(1 << 20) + 32) == K.KQ_ERR_SHAPE
     assert fused(nT=3) == K.KQ_ERR_SHAPE
     assert fused(T=0) == K.KQ_ERR_ARG
     for e in (0.0, -1.0, float("inf"), float("nan")):
@@ -312,18 +312,24 @@ def test_adaln_validation():
     assert fused(h=None) == K.KQ_ERR_ARG
     assert fused(sc=None) == K.KQ_ERR_ARG
     assert fused(f=None) == K.KQ_ERR_ARG
+    assert fused(w=None) == K.KQ_ERR_ARG
     assert fused(h=h + 2) == K.KQ_ERR_ALIGN
     assert fused(q=q + 8) == K.KQ_ERR_ALIGN
     assert fused(sh=sh + 2) == K.KQ_ERR_ALIGN
+    assert fused(w=w + 4) == K.KQ_ERR_ALIGN
     assert fused(q=h + 16) == K.KQ_ERR_OVERLAP
     assert fused(s=sh + 4) == K.KQ_ERR_OVERLAP
     assert fused(s=q + 8) == K.KQ_ERR_OVERLAP
     assert fused(f=q + 16) == K.KQ_ERR_OVERLAP
+    assert fused(w=q + 16) == K.KQ_ERR_OVERLAP
+    assert fused(w=h + 64) == K.KQ_ERR_OVERLAP
+    assert fused(w=f + 8) == K.KQ_ERR_OVERLAP
     assert fused(M=0, h=None, q=None) == K.KQ_OK
-    assert alone(d=8192 + 32) == K.KQ_ERR_SHAPE
     assert alone(x=None) == K.KQ_ERR_ARG
+    assert alone(w=None) == K.KQ_ERR_ARG
     assert alone(x=x + 8) == K.KQ_ERR_ALIGN
     assert alone(x=sc) == K.KQ_ERR_OVERLAP
     assert alone(x=h + 64) == K.KQ_ERR_OVERLAP
+    assert alone(x=w + 16) == K.KQ_ERR_OVERLAP
     assert alone(T=-3) == K.KQ_ERR_ARG
     assert alone(M=0, x=None) == K.KQ_OK

@@ -89,11 +89,11 @@ def check(K, h, shift, scale, T, f, label):
     return res
 
 
-# (M, d, tokens per sample): ragged row counts against 8 rows per workgroup,
-# samples that end inside a workgroup, every width from one block to the
-# widest row a workgroup holds
+# (M, d, tokens per sample): ragged row counts against runs of 8 rows and
+# pipeline stages of 4, samples that end inside a run, widths from one block
+# to past several 512-channel column tiles
 ADALN_CASES = [(1, 32, 1), (5, 64, 2), (37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (19, 3072, 7),
-               (9, 8192, 4), (24, 544, 5)]
+               (9, 8192, 4), (24, 544, 5), (3, 8960, 2), (6, 12288, 3)]
 
 
 @pytest.mark.parametrize("M,d,T", ADALN_CASES, ids=[f"{m}x{d}_T{t}" for m, d, t in ADALN_CASES])
@@ -137,6 +137,25 @@ def test_adaln_special_rows(K):
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
     # the constant row: x = shift of its sample, exactly representable or rounded
     assert np.array_equal(xg[0], xb[0])
+
+
+def test_adaln_stats_workspace(K):
+    # the caller's workspace holds each row's mean and 1/sqrt(var + eps) in
+    # double after the call (numpy's float64 statistics of the same bf16 rows)
+    M, d, T = 21, 2240, 4
+    say(f"[adaln stats] M={M} d={d} T={T}")
+    h = I.act_dit_lognormal(M, d, 8300)[0]
+    shift, scale = I.adaln_modulation((M + T - 1) // T, d, 8301)
+    w = torch.full((M, 2), float("nan"), dtype=torch.float64, device="cuda")
+    K.kq_adaln_quantize(dev_bf16(h), dev_f32(shift), dev_f32(scale), T, EPS,
+                        dev_f32(I.random_factors(d // 32, 8302)), stats=w)
+    torch.cuda.synchronize()
+    hd = I.bf16_bits_to_f32(h).astype(np.float64)
+    mu = hd.mean(axis=1)
+    rstd = 1.0 / np.sqrt(hd.var(axis=1) + float(np.float32(EPS)))
+    got = w.cpu().numpy()
+    assert np.allclose(got[:, 0], mu, rtol=1e-12, atol=1e-14 * np.abs(hd).mean())
+    assert np.allclose(got[:, 1], rstd, rtol=1e-12, atol=0)
 
 
 def test_adaln_empty(K):
