@@ -33,6 +33,9 @@
  *          blocks.
  *   [W4A4] the abstract: the quantized activations feed a W4A4 MXFP4 product
  *          with weights that carry the folded inverse transform.
+ *   [INF]  same record, pith_inferences[0] (an editorial inference): the
+ *          construction should carry over to other blockwise formats, e.g.
+ *          16-element blocks, by changing the number of Kronecker factors.
  *   [ADALN] the abstract: normalization layers between the blocks force the
  *          transform to run online at every denoising step; the verdict
  *          record's referee_report.summary: AdaLN is what prevents absorbing
@@ -65,6 +68,10 @@
  *     scalars stored as (a, b, c) per factor, factors A1..A5 in order.
  *   - FWHT comparison: the normalised Sylvester-order Walsh-Hadamard matrix,
  *     y_c = 2^-2.5 * sum_r x_r (-1)^popcount(r & c), then the same MXFP4.
+ *   - 16-element blocks [INF]: K16 = A1 (x) A2 (x) A3 (x) A4 (A1 on the most
+ *     significant bit of the 4-bit in-block index), factor sets nT = 1 or
+ *     d/16, and the MX rules applied to 16-element blocks (one E8M0 scale per
+ *     16 elements, E2M1 elements, nibble order as above).
  *   - AdaLN front-end (the pages name AdaLN but print no formula): per token
  *     row, LayerNorm without a learned affine (mean and biased variance over
  *     the row's d channels, 1/sqrt(var + eps)), then the per-sample
@@ -650,6 +657,127 @@ int oracle_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, co
             double mid = (floor(a / ulp) + 0.5) * ulp;
             double margin = ldexp((sabs / (double)d) * r * fabs(g) + fabs(dv) * r * fabs(g) * cancel + a + fabs(t), -40);
             xflag[m * d + c] = fabs(a - mid) <= margin;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Other block widths [INF]: 16-element blocks with four factors.       */
+/* ------------------------------------------------------------------ */
+
+/* K16[r][c] = A1[r3][c3] A2[r2][c2] A3[r1][c1] A4[r0][c0] for r = (r3 r2 r1 r0),
+ * factors f[k][row][col] = f[4k + 2 row + col]. */
+void oracle_kron_block16(const float *f, double *K)
+{
+    for (int r = 0; r < 16; ++r) {
+        for (int c = 0; c < 16; ++c) {
+            double p = 1.0;
+            for (int k = 0; k < 4; ++k) {
+                int rk = (r >> (3 - k)) & 1;
+                int ck = (c >> (3 - k)) & 1;
+                p *= (double)f[k * 4 + rk * 2 + ck];
+            }
+            K[r * 16 + c] = p;
+        }
+    }
+}
+
+/* The MX encoding of one 16-element block: shared exponent from the block's
+ * amax, elements on the E2M1 grid, 8 code bytes and one scale byte. */
+void oracle_mx_block16(const float *y16, uint8_t *q8, uint8_t *sbyte)
+{
+    int finite = 1;
+    float amax = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        if (!isfinite(y16[i]))
+            finite = 0;
+        else if (fabsf(y16[i]) > amax)
+            amax = fabsf(y16[i]);
+    }
+    if (!finite) {
+        *sbyte = 0xFF;
+        memset(q8, 0, 8);
+        return;
+    }
+    int E = oracle_e8m0_exponent(amax);
+    *sbyte = (uint8_t)(E + 127);
+    for (int i = 0; i < 8; ++i) {
+        int lo = oracle_fp4_code(y16[2 * i], E);
+        int hi = oracle_fp4_code(y16[2 * i + 1], E);
+        q8[i] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+static int check_shape16(int64_t M, int64_t d, int64_t nT)
+{
+    if (M < 0 || d <= 0)
+        return OR_ERR_ARG;
+    if (d % 16)
+        return OR_ERR_SHAPE;
+    if (nT != 1 && nT != d / 16)
+        return OR_ERR_SHAPE;
+    return OR_OK;
+}
+
+/* y = x_blk . K16_j per 16-element block (set j = block index in the row, or
+ * the one shared set), in double; z = sum_r |x_r| |K[r][c]| */
+int oracle_kq_transform16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, double *y,
+                          double *z)
+{
+    int st = check_shape16(M, d, nT);
+    if (st)
+        return st;
+    if (!x || !factors)
+        return OR_ERR_ARG;
+    int64_t nB = d / 16;
+    double K[256];
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nB; ++j) {
+            oracle_kron_block16(factors + (nT == 1 ? 0 : j) * 16, K);
+            for (int c = 0; c < 16; ++c) {
+                double acc = 0.0, mag = 0.0;
+                for (int r = 0; r < 16; ++r) {
+                    double xv = oracle_bf16_to_double(x[m * d + j * 16 + r]);
+                    acc += xv * K[r * 16 + c];
+                    mag += fabs(xv) * fabs(K[r * 16 + c]);
+                }
+                if (y)
+                    y[m * d + j * 16 + c] = acc;
+                if (z)
+                    z[m * d + j * 16 + c] = mag;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* The transformed 16-element block rounded once to fp32, then the MX
+ * encoding of the block: q [M, d/2], s [M, d/16]. */
+int oracle_kq_quantize16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                         uint8_t *s, float *y32)
+{
+    int st = check_shape16(M, d, nT);
+    if (st)
+        return st;
+    if (!x || !factors || !q || !s)
+        return OR_ERR_ARG;
+    int64_t nB = d / 16;
+    double K[256];
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < nB; ++j) {
+            oracle_kron_block16(factors + (nT == 1 ? 0 : j) * 16, K);
+            float yb[16];
+            for (int c = 0; c < 16; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < 16; ++r)
+                    acc += oracle_bf16_to_double(x[m * d + j * 16 + r]) * K[r * 16 + c];
+                yb[c] = (float)acc;
+            }
+            int64_t b = m * nB + j;
+            oracle_mx_block16(yb, q + b * 8, s + b);
+            if (y32)
+                memcpy(y32 + m * d + j * 16, yb, sizeof yb);
         }
     }
     return OR_OK;

@@ -75,6 +75,14 @@ def bind(L):
     L.oracle_mx_dequant.restype = ctypes.c_int
     L.oracle_mx_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
     L.oracle_mx_gemm.restype = ctypes.c_int
+    L.oracle_kron_block16.argtypes = [P, P]
+    L.oracle_kron_block16.restype = None
+    L.oracle_mx_block16.argtypes = [P, P, P]
+    L.oracle_mx_block16.restype = None
+    L.oracle_kq_transform16.argtypes = [P, I64, I64, P, I64, P, P]
+    L.oracle_kq_transform16.restype = ctypes.c_int
+    L.oracle_kq_quantize16.argtypes = [P, I64, I64, P, I64, P, P, P]
+    L.oracle_kq_quantize16.restype = ctypes.c_int
     L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
     L.oracle_double_to_bf16.restype = ctypes.c_uint16
     L.oracle_adaln.argtypes = [P, I64, I64, P, P, I64, ctypes.c_float, P, P, P]
@@ -284,6 +292,47 @@ def mx_gemm(qa, sa, qb, sb, want_mag=True):
     mag = np.empty((M, N), np.float64) if want_mag else None
     _check(lib().oracle_mx_gemm(_ptr(qa), _ptr(sa), M, _ptr(qb), _ptr(sb), N, K, _ptr(out), _ptr(mag)))
     return (out, mag) if want_mag else out
+
+
+def kron_block16(f4):
+    """Dense 16x16 block (float64) from four 2x2 factors [4, 2, 2]."""
+    f = _f32(f4).reshape(16)
+    K = np.empty((16, 16), np.float64)
+    lib().oracle_kron_block16(_ptr(f), _ptr(K))
+    return K
+
+
+def mx_block16(y16):
+    y = _f32(y16).reshape(16)
+    q = np.empty(8, np.uint8)
+    s = np.empty(1, np.uint8)
+    lib().oracle_mx_block16(_ptr(y), _ptr(q), _ptr(s))
+    return q, int(s[0])
+
+
+def kq_transform16(x_u16, factors, want_z=True):
+    """16-element blocks, four factors per set [nT, 4, 2, 2]: y and z [M, d]."""
+    x = _u16(x_u16)
+    M, d = x.shape
+    f = _f32(factors)
+    nT = f.reshape(-1, 16).shape[0]
+    y = np.empty((M, d), np.float64)
+    z = np.empty((M, d), np.float64) if want_z else None
+    _check(lib().oracle_kq_transform16(_ptr(x), M, d, _ptr(f), nT, _ptr(y), _ptr(z)))
+    return (y, z) if want_z else y
+
+
+def kq_quantize16(x_u16, factors, want_y32=False):
+    """16-element blocks: codes [M, d/2], scales [M, d/16] (one per 16 elements)."""
+    x = _u16(x_u16)
+    M, d = x.shape
+    f = _f32(factors)
+    nT = f.reshape(-1, 16).shape[0]
+    q = np.empty((M, d // 2), np.uint8)
+    s = np.empty((M, d // 16), np.uint8)
+    y32 = np.empty((M, d), np.float32) if want_y32 else None
+    _check(lib().oracle_kq_quantize16(_ptr(x), M, d, _ptr(f), nT, _ptr(q), _ptr(s), _ptr(y32)))
+    return (q, s, y32) if want_y32 else (q, s)
 
 
 def double_to_bf16(v):

@@ -328,3 +328,13 @@ def tokens_per_sample(name, M=None):
     if _CFG_ID[name] == 1:
         return max(M, 1)
     return max((M + 1) // 2, 1)
+
+
+def random_factors16(nT, seed, sigma=0.3, cond_max=10.0):
+    """nT sets of four 2x2 factors (16-element blocks), drawn as random_factors
+    draws its five."""
+    return np.ascontiguousarray(random_factors(nT, seed, sigma, cond_max)[:, :4])
+
+
+def integer_unimodular_factors16(nT, seed):
+    return np.ascontiguousarray(integer_unimodular_factors(nT, seed)[:, :4])

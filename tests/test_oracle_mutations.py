@@ -86,6 +86,20 @@ MUTATIONS = {
         "if (rem > half || (rem == half && fmod(m, 2.0) == 1.0))\n        m += 1.0;\n    double r = m * ulp;",
         "if (rem >= half)\n        m += 1.0;\n    double r = m * ulp;",
         "test_double_to_bf16_nearest_even", {}),
+    "kron16_bit_order_lsb_first": (
+        "int rk = (r >> (3 - k)) & 1;\n                int ck = (c >> (3 - k)) & 1;",
+        "int rk = (r >> k) & 1;\n                int ck = (c >> k) & 1;",
+        "test_kron_block16_equals_numpy_kron", {"seed": 21}),
+    "transform16_set_of_the_wrong_block": (
+        "oracle_kron_block16(factors + (nT == 1 ? 0 : j) * 16, K);\n            for (int c = 0; c < 16; ++c) {\n"
+        "                double acc = 0.0, mag = 0.0;",
+        "oracle_kron_block16(factors + (nT == 1 ? 0 : j / 2) * 16, K);\n            for (int c = 0; c < 16; ++c) {\n"
+        "                double acc = 0.0, mag = 0.0;",
+        "test_transform16_per_block_sets_equal_modewise_product", {}),
+    "mx16_amax_over_half_the_block": (
+        "for (int i = 0; i < 16; ++i) {\n        if (!isfinite(y16[i]))",
+        "for (int i = 0; i < 8; ++i) {\n        if (!isfinite(y16[i]))",
+        "test_mx_block16_equals_padded_mx32", {}),
     "wht_sign_flipped": (
         "K[r * 32 + c] = par ? -scale : scale;",
         "K[r * 32 + c] = par ? scale : -scale;",

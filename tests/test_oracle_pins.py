@@ -549,3 +549,77 @@ def test_adaln_flags_a_value_on_a_midpoint(oracle_lib):
     x, xb, fl = oracle_lib.adaln(h, shift, scale, T, 1e-6)
     assert np.all(x[0] == float(mid)) and np.all(xb[0] == 0x3F80) and fl[0].all()
     assert np.all(xb[1] == 0x3F81) and not fl[1].any()
+
+
+# ---------------------------------------------------------------------------
+# 16-element blocks with four factors (the verdict record's pith_inferences:
+# the construction carries over to 16-element blocks by changing the number of
+# Kronecker factors).  Reading: K16 = A1 (x) A2 (x) A3 (x) A4, one E8M0 scale
+# per 16 elements.
+# ---------------------------------------------------------------------------
+def kron4(f4):
+    K = np.array([[1.0]])
+    for k in range(4):
+        K = np.kron(K, f4[k].astype(np.float64))
+    return K
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_kron_block16_equals_numpy_kron(oracle_lib, seed):
+    f = I.random_factors16(1, seed)[0]
+    assert np.allclose(oracle_lib.kron_block16(f), kron4(f), rtol=1e-15, atol=0.0)
+
+
+def test_transform16_per_block_sets_equal_modewise_product(oracle_lib):
+    # each 16-element block through its own set, as four mode-wise 2x2
+    # products on the block reshaped [2, 2, 2, 2] (A1 on the first mode)
+    M, d = 3, 96
+    nT = d // 16
+    x = I.act_gaussian_outliers(M, d, 23, 2, 20.0)[0]
+    f = I.random_factors16(nT, 24)
+    y, z = oracle_lib.kq_transform16(x, f)
+    xd = I.bf16_bits_to_f32(x).astype(np.float64)
+    for j in range(nT):
+        blk = xd[:, 16 * j:16 * j + 16].reshape(M, 2, 2, 2, 2)
+        F = f[j].astype(np.float64)
+        ref = np.einsum("mabcd,ae,bf,cg,dh->mefgh", blk, F[0], F[1], F[2], F[3]).reshape(M, 16)
+        assert np.allclose(y[:, 16 * j:16 * j + 16], ref, rtol=1e-13, atol=1e-13)
+    assert np.all(z >= np.abs(y))
+
+
+def test_mx_block16_equals_padded_mx32(oracle_lib):
+    # a 16-element block encodes exactly as the first half of a 32-element
+    # block whose second half is zero (zeros change neither amax nor codes)
+    rng = np.random.default_rng(25)
+    for k in range(300):
+        y = (rng.standard_normal(16) * np.exp2(rng.integers(-20, 20))).astype(np.float32)
+        if k % 7 == 0:
+            y[:] = 0.0
+        q16, s16 = oracle_lib.mx_block16(y)
+        q32, s32 = oracle_lib.mx_block(np.concatenate([y, np.zeros(16, np.float32)]))
+        assert s16 == s32 and np.array_equal(q16, q32[:8])
+
+
+def test_kq16_identity_factors_are_plain_mx16(oracle_lib):
+    M, d = 4, 64
+    x = I.act_gaussian_outliers(M, d, 26, 3, 30.0)[0]
+    f = np.tile(np.eye(2, dtype=np.float32), (1, 4, 1, 1))
+    q, s = oracle_lib.kq_quantize16(x, f)
+    xf = I.bf16_bits_to_f32(x)
+    for m in range(M):
+        for j in range(d // 16):
+            qb, sb = oracle_lib.mx_block16(xf[m, 16 * j:16 * j + 16])
+            assert s[m, j] == sb and np.array_equal(q[m, 8 * j:8 * j + 8], qb)
+
+
+def test_kq16_exact_integer_invariance(oracle_lib):
+    # (X T16)(T16^-1 W^T) = X W^T exactly for integer unimodular factors
+    M, d, N = 3, 64, 5
+    rng = np.random.default_rng(27)
+    X = rng.integers(-4, 5, (M, d)).astype(np.float32)
+    x = I.f32_to_bf16_bits(X)
+    f = I.integer_unimodular_factors16(d // 16, 28)
+    y = oracle_lib.kq_transform16(x, f, want_z=False)
+    W = rng.integers(-3, 4, (N, d)).astype(np.float64)
+    Tinv = scipy.linalg.block_diag(*[np.round(np.linalg.inv(kron4(f[j]))) for j in range(d // 16)])
+    assert np.array_equal(y @ (Tinv @ W.T), X.astype(np.float64) @ W.T)
