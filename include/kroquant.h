@@ -151,6 +151,31 @@ int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *
 int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *stream);
 
 /*
+ * kq_quantize16: the same quantizer on 16-element blocks with four Kronecker
+ * factors (pith.science record, pith_inferences[0], an editorial inference:
+ * the construction carries over to 16-element blockwise formats by changing
+ * the number of factors).  Reading: K16 = A1 (x) A2 (x) A3 (x) A4 per
+ * 16-channel block (A1 on the most significant bit of the 4-bit in-block
+ * index), y = x_blk . K16_j in fp32, and the MX rules applied to 16-element
+ * blocks: one E8M0 scale per 16 elements, E2M1 codes, element 2i in the low
+ * nibble.  The transform runs as four butterfly stages (one cross-lane stage
+ * over a lane pair by DPP, three in-lane stages).
+ *   x        dev, bf16 [M, d], d % 16 == 0, 16-byte aligned
+ *   factors  dev, float32 [nT, 4, 2, 2], nT = 1 or d/16, 4-byte aligned
+ *   q        dev, u8 [M, d/2], 16-byte aligned
+ *   s        dev, u8 [M, d/16] (one scale byte per 16 elements)
+ * Otherwise the same contract and errors as kq_quantize (KQ_ERR_SHAPE for
+ * d % 16 != 0 or nT not in {1, d/16}).
+ */
+int kq_quantize16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
+                  void *stream);
+
+/* The transformed values of kq_quantize16 (fp32), for inspection.
+ *   y  dev, float32 [M, d], 16-byte aligned */
+int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                       void *stream);
+
+/*
  * kq_adaln_quantize: the quantizer fused with the AdaLN normalisation in
  * front of it (abstract on the mlsanity.com paper page: the normalisation
  * layers between blocks make the transform run online at every step;

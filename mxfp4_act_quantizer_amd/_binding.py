@@ -31,7 +31,7 @@ EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
     "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors", "mx_gemm",
-    "kq_adaln_quantize", "adaln_modulate", "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
+    "kq_adaln_quantize", "adaln_modulate", "kq_quantize16", "kq_transform16_f32", "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -54,6 +54,8 @@ _lib.fwht_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.fwht_transform_f32.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.kq_lu_factors.argtypes = [_P, _I64, _P]
 _lib.mx_gemm.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]
+_lib.kq_quantize16.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
+_lib.kq_transform16_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
 _lib.kq_adaln_quantize.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P, _P]
 _lib.adaln_modulate.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
@@ -274,6 +276,41 @@ def mx_quantize_f32(x, q=None, s=None, stream=None):
                               _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
     _check(st, "mx_quantize_f32")
     return q, s
+
+
+def _nT16(factors):
+    n = factors.numel()
+    if n % 16:
+        raise ValueError("factors must hold [nT, 4, 2, 2] float32 values")
+    return n // 16
+
+
+def kq_quantize16(x, factors, q=None, s=None, stream=None):
+    """16-element blocks with four factors per set [nT, 4, 2, 2]: returns
+    (q [M, d/2] u8, s [M, d/16] u8)."""
+    torch = _torch()
+    M, d = _md(x)
+    if q is None:
+        q = torch.empty((M, d // 2), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, d // 16), dtype=torch.uint8, device=x.device)
+    st = _lib.kq_quantize16(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
+                            _nT16(factors), _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"),
+                            _stream_handle(stream))
+    _check(st, "kq_quantize16")
+    return q, s
+
+
+def kq_transform16_f32(x, factors, y=None, stream=None):
+    """The transformed values of kq_quantize16 (fp32 [M, d])."""
+    torch = _torch()
+    M, d = _md(x)
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.float32, device=x.device)
+    st = _lib.kq_transform16_f32(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
+                                 _nT16(factors), _dev(y, (torch.float32,), "y"), _stream_handle(stream))
+    _check(st, "kq_transform16_f32")
+    return y
 
 
 def _stats(h, M, stats):

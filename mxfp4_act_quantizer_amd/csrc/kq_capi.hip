@@ -251,6 +251,58 @@ int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, 
     return hip_status(kq::launch_mx_gemm(qa, sa, M, qb, sb, N, K, out, out_bf16, (hipStream_t)stream));
 }
 
+// shape checks of the 16-element-block entry points
+static int check_md16(int64_t M, int64_t d, int64_t nT)
+{
+    if (M < 0 || d <= 0)
+        return KQ_ERR_ARG;
+    if (d % 16 != 0 || d > kq::kMaxD || (M > 0 && (M * (d / 16)) > kq::kMaxBlocksTotal))
+        return KQ_ERR_SHAPE;
+    if (nT != 1 && nT != d / 16)
+        return KQ_ERR_SHAPE;
+    return KQ_OK;
+}
+
+int kq_quantize16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
+                  void *stream)
+{
+    int st = check_md16(M, d, nT);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if (!x || !q || !s)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t xb = M * d * 2, qb = M * (d / 2), sb = M * (d / 16);
+    if (overlap(x, xb, q, qb) || overlap(x, xb, s, sb) || overlap(q, qb, s, sb))
+        return KQ_ERR_OVERLAP;
+    if ((st = check_param(factors, nT * 16, x, xb, q, qb, s, sb)))
+        return st;
+    return hip_status(kq::launch_kq16(x, M, d, factors, nT, q, s, nullptr, (hipStream_t)stream));
+}
+
+int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                       void *stream)
+{
+    int st = check_md16(M, d, nT);
+    if (st)
+        return st;
+    if (M == 0)
+        return KQ_OK;
+    if (!x || !y)
+        return KQ_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t xb = M * d * 2, yb = M * d * 4;
+    if (overlap(x, xb, y, yb))
+        return KQ_ERR_OVERLAP;
+    if ((st = check_param(factors, nT * 16, x, xb, y, yb, nullptr, 0)))
+        return st;
+    return hip_status(kq::launch_kq16(x, M, d, factors, nT, nullptr, nullptr, y, (hipStream_t)stream));
+}
+
 // shared checks of the AdaLN entry points (h, shift, scale, T, eps, the
 // statistics workspace); out and out2 are the outputs, each with its byte count
 static int check_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,

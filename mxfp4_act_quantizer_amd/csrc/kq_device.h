@@ -146,4 +146,57 @@ __device__ __forceinline__ unsigned mx_encode_quad(const float (&v)[8], unsigned
     return w;
 }
 
+// ---- 16-element blocks with four factors (two lanes per block) ------------
+// The lane's channels are 8 qp + e of its 16-element block (qp = lane % 2):
+// index bit 3 is the lane's position in the pair, bits 2..0 are e.
+struct Bfly16 {
+    float a2[4], a3[4], a4[4]; // full 2x2 factors for the in-lane stages
+    float s1, o1;              // cross-lane stage (A1): coefficient on own / partner value
+};
+
+__device__ __forceinline__ void bfly16_setup(Bfly16 &B, const float *__restrict__ F, int qp)
+{
+    const int b3 = qp & 1;
+    // stage on index bit 3 (A1): new(self) = A[b][b] self + A[1-b][b] other
+    B.s1 = F[b3 * 2 + b3];
+    B.o1 = F[(1 - b3) * 2 + b3];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        B.a2[k] = F[4 + k];
+        B.a3[k] = F[8 + k];
+        B.a4[k] = F[12 + k];
+    }
+}
+
+// The four stages of y = x K16 on one lane's 8 channels: the cross-lane
+// stage (index bit 3, partner lane ^ 1), then the in-lane bits 2, 1, 0.
+__device__ __forceinline__ void bfly16_stages(float (&v)[8], const Bfly16 &B)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float other = dpp_xor1(v[i]);
+        v[i] = __builtin_fmaf(B.o1, other, B.s1 * v[i]);
+    }
+    bfly_inlane<4, false>(v, B.a2);
+    bfly_inlane<2, false>(v, B.a3);
+    bfly_inlane<1, true>(v, B.a4);
+}
+
+// MX encoding of a 16-element block held by a pair of lanes: amax over the
+// pair, E8M0 byte b, and this lane's 8 packed FP4 codes.
+__device__ __forceinline__ unsigned mx_encode_pair(const float (&v)[8], unsigned &b)
+{
+    float am = __builtin_fabsf(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        am = amax_step(am, v[i]);
+    am = vmax(am, dpp_xor1(am));
+    b = e8m0_byte(am);
+    const float sc = scale_operand(b);
+    unsigned w = cvt8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
+    if (b == 0xFFu)
+        w = 0u;
+    return w;
+}
+
 } // namespace kq

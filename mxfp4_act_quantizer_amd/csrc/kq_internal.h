@@ -23,6 +23,10 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
                           uint8_t *s, float *y, int lu, hipStream_t stream);
 hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
                                uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
+// 16-element blocks, four factors per set [nT, 4, 2, 2] (nT = 1 or d/16):
+// quantize into q [M, d/2], s [M, d/16] (y null) or export y
+hipError_t launch_kq16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                       uint8_t *s, float *y, hipStream_t stream);
 hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
                      hipStream_t stream);
 hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream);

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
 // Streaming variants: one lane per 8 channels, a wave covers 512 channels
 // (16 blocks) of U rows at a time and walks a run of rows.
 // ---------------------------------------------------------------------------
-enum StreamMode { kSQ = 0, kMXF32 = 1, kBflyQ = 2, kBflyT = 3, kFwhtQ = 4, kFwhtT = 5 };
+enum StreamMode { kSQ = 0, kMXF32 = 1, kBflyQ = 2, kBflyT = 3, kFwhtQ = 4, kFwhtT = 5, kBfly16Q = 6, kBfly16T = 7 };
 
 // Unnormalised Walsh-Hadamard stage on an in-lane index bit (stride ST):
 // pairs (u at bit 0, w at bit 1) become (u + w, u - w).
@@ -436,6 +436,7 @@ __device__ __forceinline__ void load_rows(RowsIn<kMode> &in, __amdgpu_buffer_rsr
 template <int kMode>
 __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m, int64_t m0, int64_t m1, int d, int nB,
                                              int oct, bool cok, int qp, const float (&r)[8], const Bfly &B,
+                                             const Bfly16 &B16,
                                              __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
                                              float *__restrict__ y)
 {
@@ -462,6 +463,8 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
         }
         if constexpr (kMode == kBflyQ || kMode == kBflyT)
             bfly_stages(v, B);
+        if constexpr (kMode == kBfly16Q || kMode == kBfly16T)
+            bfly16_stages(v, B16);
         if constexpr (kMode == kFwhtQ || kMode == kFwhtT) {
             // Walsh-Hadamard comparison transform: the same five stages with
             // fixed +-1 coefficients.  Cross-lane bits 4 and 3: a lane at bit
@@ -483,22 +486,25 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
                 v[i] = __builtin_fmaf(v[i], kInvSqrt32, 0.0f);
         }
         const int64_t mm = m + u;
-        if constexpr (kMode == kBflyT || kMode == kFwhtT) {
+        if constexpr (kMode == kBflyT || kMode == kFwhtT || kMode == kBfly16T) {
             if (mm < m1 && cok) {
                 f32x4 *o = (f32x4 *)(y + mm * d + (int64_t)oct * 8);
                 o[0] = f32x4{v[0], v[1], v[2], v[3]};
                 o[1] = f32x4{v[4], v[5], v[6], v[7]};
             }
         } else {
+            // 32-element blocks span a quad of lanes, 16-element blocks a pair
+            constexpr bool k16 = kMode == kBfly16Q;
             unsigned b;
-            const unsigned w = mx_encode_quad(v, b);
+            const unsigned w = k16 ? mx_encode_pair(v, b) : mx_encode_quad(v, b);
             // rows past the run fall outside the wave's ranges; lanes past the row
-            // end (and three of the four lanes of a block for s) set bit 31 of their offset
+            // end (and all lanes of a block but the first for s) set bit 31 of their offset
             const int mr = (int)(mm - m0);
             const unsigned drop_q = (unsigned)(cok ? 0 : 1) << 31;
-            const unsigned drop_s = drop_q | ((unsigned)(qp != 0) << 31);
+            const unsigned drop_s = drop_q | ((unsigned)((qp & (k16 ? 1 : 3)) != 0) << 31);
             __builtin_amdgcn_raw_buffer_store_b32(w, rq, (int)((unsigned)(mr * (d >> 1) + oct * 4) | drop_q), 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)((unsigned)(mr * nB + (oct >> 2)) | drop_s), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs,
+                                                 (int)((unsigned)(mr * nB + (oct >> (k16 ? 1 : 2))) | drop_s), 0, 0);
         }
     }
 }
@@ -524,7 +530,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
         return; // wave-uniform; this kernel has no barrier
     const int64_t m1 = (m0 + rows_per_wave < M) ? m0 + rows_per_wave : M;
     const int nOct = d >> 3;
-    const int nB = d >> 5;
+    constexpr bool k16 = kMode == kBfly16Q || kMode == kBfly16T;
+    const int nB = k16 ? d >> 4 : d >> 5; // scale blocks per row
     const int oct = ct * 64 + lane;
     const bool cok = oct < nOct;
     const int octc = cok ? oct : nOct - 1; // parameter index for lanes past the row end (results not stored)
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
 
     RowsIn<kMode> bufA, bufB;
     load_rows<kMode>(bufA, rx, 0, d, lane_off);
-    const bool quant = (kMode != kBflyT && kMode != kFwhtT);
+    const bool quant = (kMode != kBflyT && kMode != kFwhtT && kMode != kBfly16T);
     __amdgpu_buffer_rsrc_t rq = out_buffer(quant ? q + m0 * (d >> 1) : nullptr, quant ? (m1 - m0) * (d >> 1) : 0);
     __amdgpu_buffer_rsrc_t rs = out_buffer(quant ? s + m0 * nB : nullptr, quant ? (m1 - m0) * nB : 0);
 
@@ -551,21 +558,26 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
         const int set = per_block ? (octc >> 2) : 0;
         bfly_setup(B, aux + (int64_t)set * 20, qp);
     }
+    Bfly16 B16;
+    if constexpr (k16) {
+        const int set = per_block ? (octc >> 1) : 0;
+        bfly16_setup(B16, aux + (int64_t)set * 16, lane & 1);
+    }
 
     // two-stage pipeline; a prefetch past the run falls outside the range and fetches nothing
     int64_t m = m0;
     for (; m + kStreamU < m1; m += 2 * kStreamU) {
         load_rows<kMode>(bufB, rx, (int)(m + kStreamU - m0), d, lane_off);
         __builtin_amdgcn_sched_barrier(0); // keep the prefetch ahead of these rows' stores
-        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
+        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, B16, rq, rs, y);
         __builtin_amdgcn_sched_barrier(0);
         load_rows<kMode>(bufA, rx, (int)(m + 2 * kStreamU - m0), d, lane_off);
         __builtin_amdgcn_sched_barrier(0);
-        process_rows<kMode>(bufB, m + kStreamU, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
+        process_rows<kMode>(bufB, m + kStreamU, m0, m1, d, nB, oct, cok, qp, r, B, B16, rq, rs, y);
         __builtin_amdgcn_sched_barrier(0);
     }
     if (m < m1)
-        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, rq, rs, y);
+        process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, B16, rq, rs, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,6 +745,8 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
     case kMXF32: fn = (const void *)stream_kernel<kMXF32>; break;
     case kBflyQ: fn = (const void *)stream_kernel<kBflyQ>; break;
     case kBflyT: fn = (const void *)stream_kernel<kBflyT>; break;
+    case kBfly16Q: fn = (const void *)stream_kernel<kBfly16Q>; break;
+    case kBfly16T: fn = (const void *)stream_kernel<kBfly16T>; break;
     case kFwhtQ: fn = (const void *)stream_kernel<kFwhtQ>; break;
     default: fn = (const void *)stream_kernel<kFwhtT>; break;
     }
@@ -743,6 +757,13 @@ hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const fl
                                uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
 {
     return launch_stream(y ? kBflyT : kBflyQ, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y,
+                         tuning().bfly_rows_per_wave, stream);
+}
+
+hipError_t launch_kq16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                       uint8_t *s, float *y, hipStream_t stream)
+{
+    return launch_stream(y ? kBfly16T : kBfly16Q, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y,
                          tuning().bfly_rows_per_wave, stream);
 }
 

@@ -47,15 +47,16 @@ def shared_exponent(amax):
     return np.clip(E, -127, 127)
 
 
-def boundary_flags(z, y32, tol=TOL):
-    """Flags (elements [M, d], blocks [M, d/32]) where a tolerance-sized change
-    of the transformed value may change the code or the scale."""
+def boundary_flags(z, y32, tol=TOL, bw=32):
+    """Flags (elements [M, d], blocks [M, d/bw]) where a tolerance-sized change
+    of the transformed value may change the code or the scale (bw: elements
+    per scale block)."""
     M, d = y32.shape
-    nB = d // 32
+    nB = d // bw
     a = np.abs(y32.astype(np.float64))
     delta = tol * np.maximum(z, a) + TOL_ABS
-    ab = a.reshape(M, nB, 32)
-    db = delta.reshape(M, nB, 32)
+    ab = a.reshape(M, nB, bw)
+    db = delta.reshape(M, nB, bw)
     amax = ab.max(axis=2)
     dmax = db.max(axis=2)
     # blocks holding Inf/NaN give inf - inf here; their scale byte is 0xFF
@@ -68,7 +69,7 @@ def boundary_flags(z, y32, tol=TOL):
     scale = np.ldexp(1.0, -E)[:, :, None]
     lo = (ab - db) * scale
     hi = (ab + db) * scale
-    elem = np.zeros((M, nB, 32), bool)
+    elem = np.zeros((M, nB, bw), bool)
     for t in THRESHOLDS:
         elem |= (lo <= t) & (t <= hi)
     # within delta of zero: the computed value may carry either sign (code 0 vs 8)

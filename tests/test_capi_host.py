@@ -333,3 +333,21 @@ def test_adaln_validation():
     assert alone(x=w + 16) == K.KQ_ERR_OVERLAP
     assert alone(T=-3) == K.KQ_ERR_ARG
     assert alone(M=0, x=None) == K.KQ_OK
+
+
+def test_kq16_validation():
+    x, f, q, s, y = (FAKE + (k << 30) for k in range(5))
+    assert raw("kq_quantize16", x, 4, 24, f, 1, q, s, None) == K.KQ_ERR_SHAPE  # d % 16
+    assert raw("kq_quantize16", x, 4, 48, f, 2, q, s, None) == K.KQ_ERR_SHAPE  # nT not in {1, 3}
+    assert raw("kq_quantize16", x, -1, 48, f, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize16", None, 4, 48, f, 3, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize16", x, 4, 48, None, 3, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_quantize16", x + 8, 4, 48, f, 3, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize16", x, 4, 48, f + 2, 3, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize16", x, 4, 48, f, 3, x + 32, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_quantize16", x, 4, 48, f, 3, q, q + 95, None) == K.KQ_ERR_OVERLAP  # s overlaps q's 96 bytes
+    assert raw("kq_quantize16", x, 4, 48, q, 3, q, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_quantize16", None, 0, 48, None, 1, None, None, None) == K.KQ_OK
+    assert raw("kq_transform16_f32", x, 4, 40, f, 1, y, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_transform16_f32", x, 4, 48, f, 3, x + 16, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_transform16_f32", x, 4, 48, f, 3, y + 4, None) == K.KQ_ERR_ALIGN
