@@ -263,12 +263,14 @@ def all_configs(args):
         for _ in range(nsets):
             x = (torch.randn(M, d, generator=gen, device=dev) * chan).to(torch.bfloat16)
             bufs.append(dict(x=x, q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
-                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
+                             s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev),
+                             s16=torch.empty((M, d // 16), dtype=torch.uint8, device=dev)))
         amax = bufs[0]["x"].float().abs().amax(dim=0)
         scale = torch.sqrt(torch.clamp(amax, min=1e-5))
         f_pb = torch.from_numpy(I.random_factors(d // 32, I.factor_seed(name))).to(dev)
         f_sh = torch.from_numpy(I.random_factors(1, I.factor_seed(name))).to(dev)
         lu_pb = torch.from_numpy(I.random_lu(d // 32, I.factor_seed(name) + 77)).to(dev)
+        f16 = torch.from_numpy(I.random_factors16(d // 16, I.factor_seed(name) + 16)).to(dev)
         torch.cuda.synchronize()
         cur = torch.cuda.current_stream
         legs = {
@@ -277,6 +279,7 @@ def all_configs(args):
             "kq_butterfly_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=2),
             "kq_lu_perblock": lambda b: K.kq_quantize_lu(b["x"], lu_pb, b["q"], b["s"], stream=cur()),
             "fwht": lambda b: K.fwht_quantize(b["x"], b["q"], b["s"], stream=cur()),
+            "kq16_perblock": lambda b: K.kq_quantize16(b["x"], f16, b["q"], b["s16"], stream=cur()),
             "smoothquant": lambda b: K.sq_quantize(b["x"], scale, b["q"], b["s"], stream=cur()),
             "copy41": lambda b: K.measure_copy41(b["x"], b["q"], stream=cur()),
         }
@@ -302,7 +305,8 @@ def all_configs(args):
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps
-            nbytes = elems * 2.5 if leg == "copy41" else alg
+            # copy: 2 + 0.5 B per element; 16-element blocks: 2 + 0.5 + 1/16
+            nbytes = elems * 2.5 if leg == "copy41" else (elems * (2.5 + 1.0 / 16) if leg == "kq16_perblock" else alg)
             row[leg] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                         "hbm_pct": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "rows/s": round(M / us * 1e6, 1)}
         row["kq_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_perblock"]["us"], 4)
@@ -314,15 +318,15 @@ def all_configs(args):
         torch.cuda.empty_cache()
     print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ MFMA shared us | KQ butterfly us | "
           "K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | copy 4:1 us (GB/s) | KQ/SQ speed | "
-          "KQ/copy speed | K2/FWHT speed |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "KQ/copy speed | K2/FWHT speed | KQ16 butterfly us (GB/s) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in table:
         a, b, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_butterfly_perblock",
                                                    "kq_lu_perblock", "fwht", "smoothquant", "copy41"))
         print(f"| {r['config']} | {r['M']}x{r['d']} | {a['us']} ({a['GB/s']}, {a['hbm_pct']}%) | {b['us']} | "
               f"{c['us']} | {l2['us']} | {fw['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | "
               f"{cp['us']} ({cp['GB/s']}) | {r['kq_over_sq_speed']} | {r['kq_over_copy41_speed']} | "
-              f"{r['k2_lu_over_fwht_speed']} |", flush=True)
+              f"{r['k2_lu_over_fwht_speed']} | {r['kq16_perblock']['us']} ({r['kq16_perblock']['GB/s']}) |", flush=True)
 
 
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak (TFLOP/s)
