@@ -191,12 +191,21 @@ __device__ __forceinline__ void adaln_process(const HRows &in, int64_t m, int64_
                                               __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rxo)
 {
     const int nB = d >> 5;
+    // the stage's records, all requested before any is used (rows past the
+    // run read the run's last record, which is never used)
+    double mus[kU], rstds[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const int64_t mc = (m + u < m1) ? m + u : m1 - 1;
+        mus[u] = stats[2 * mc];
+        rstds[u] = stats[2 * mc + 1];
+    }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int64_t mm = m + u;
         if (mm >= m1)
             break; // wave-uniform
-        const double mu = stats[2 * mm], rstd = stats[2 * mm + 1];
+        const double mu = mus[u], rstd = rstds[u];
         if (mm >= md.next)
             load_modulation(md, shift, scale, mm / T, T, d, octc);
         unsigned xw[4];
