@@ -349,11 +349,463 @@ mx_gemm_kernel(const uint8_t *__restrict__ qa, const uint8_t *__restrict__ sa, i
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Persistent form, used when K % 128 == 0 and the output rows split into
+// whole 16-byte pieces (every layer of the transformer shapes): each
+// workgroup owns a fixed list of tiles and runs one continuous stream of k
+// chunks over all of them, so the loads of the next tile are in flight while
+// the last chunk of this one is multiplied and stored.  Codes and scales go straight from global memory into LDS
+// (buffer_load ... lds, 16 or 4 bytes per lane) through a ring of kS stages;
+// no register staging.
+//
+// LDS layout of a stage: the code rows of A (BM of them) then of B (BN), RB =
+// KC/2 bytes each, then the scale rows of A and B (SB = KC/32 bytes each).
+// One 64-lane load writes 1 KB of consecutive LDS, so the conflict-avoiding
+// permutation is applied to what each lane fetches: slot s of row r holds the
+// row's 16-byte piece s ^ rot(r), rot(r) = (r / (16 / PR)) % PR with PR
+// pieces per row.  A fragment read (16 lanes = 16 consecutive rows, one piece)
+// then covers all 64 banks once.
+// ---------------------------------------------------------------------------
+template <int kWM_, int kWN_, int kTX_, int kTY_, int kKC_, int kS_>
+struct PGeom {
+    static constexpr int WM = kWM_, WN = kWN_, TX = kTX_, TY = kTY_, KC = kKC_, S = kS_;
+    static constexpr int W = WM * WN, T = 64 * W;
+    static constexpr int BM = WM * TX * 32, BN = WN * TY * 32;
+    static constexpr int STEPS = KC / 64;
+    static constexpr int PR = KC / 32;       // 16-byte pieces (MX blocks) per row and chunk
+    static constexpr int RB = KC / 2;        // code bytes per row and chunk
+    static constexpr int RPI = 1024 / RB;    // rows per code load (64 lanes x 16 bytes)
+    static constexpr int SB = KC / 32;       // scale bytes per row and chunk
+    static constexpr int SRPI = 256 / SB;    // rows per scale load (64 lanes x 4 bytes)
+    static constexpr int NCI = (BM + BN) / RPI, NSI = (BM + BN) / SRPI;
+    // scale loads padded to a whole number per wave: the extra ones fetch
+    // nothing and land in slack at the end of the stage
+    static constexpr int NSP = (NSI + W - 1) / W * W;
+    static constexpr int LC = NCI / W, LS = NSP / W, L = LC + LS; // loads per wave and chunk
+    static constexpr int SOFF = (BM + BN) * RB;                  // scale rows within a stage
+    static constexpr int SZ = SOFF + NSP * 256;                   // bytes per stage
+    static constexpr int ROWS256 = 16 / PR;                      // rows per 256 bytes of LDS
+    // workgroups per CU that the 160 KB of LDS hold, and the waves per SIMD
+    // that gives (the register budget is set to match)
+    static constexpr int WGS = (160 * 1024) / (S * SZ) < 1 ? 1 : (160 * 1024) / (S * SZ);
+    static constexpr int OCC = WGS * W / 4 < 1 ? 1 : (WGS * W / 4 > 8 ? 8 : WGS * W / 4);
+    static_assert(KC == 128 || KC == 256, "chunk of 2 or 4 MFMA steps");
+    static_assert(NCI % W == 0, "the code loads split evenly over the waves");
+    static_assert(BM % RPI == 0 && BM % SRPI == 0, "no load straddles A and B");
+    static_assert(S >= 2 && S <= 4, "ring of 2 to 4 stages");
+};
+
+// A chunk's scale words for one wave: byte u of the word of lane half h is the
+// scale of block 2u + h of the lane's row.
+template <class G>
+__device__ __forceinline__ void p_scales(unsigned (&sca)[G::TX], unsigned (&scb)[G::TY], const unsigned char *stg,
+                                         unsigned sa_off, unsigned sb_off, unsigned scale_sel)
+{
+#pragma unroll
+    for (int x = 0; x < G::TX; ++x) {
+        if constexpr (G::SB == 8) {
+            const u32x2 w = *(const u32x2 *)(stg + sa_off + x * 32 * 8);
+            sca[x] = __builtin_amdgcn_perm(w[1], w[0], scale_sel);
+        } else {
+            const unsigned w = *(const unsigned *)(stg + sa_off + x * 32 * 4);
+            sca[x] = __builtin_amdgcn_perm(w, w, scale_sel);
+        }
+    }
+#pragma unroll
+    for (int y = 0; y < G::TY; ++y) {
+        if constexpr (G::SB == 8) {
+            const u32x2 w = *(const u32x2 *)(stg + sb_off + y * 32 * 8);
+            scb[y] = __builtin_amdgcn_perm(w[1], w[0], scale_sel);
+        } else {
+            const unsigned w = *(const unsigned *)(stg + sb_off + y * 32 * 4);
+            scb[y] = __builtin_amdgcn_perm(w, w, scale_sel);
+        }
+    }
+}
+
+// Steps kU0 .. kU1 - 1 of one chunk's products for one wave from a stage (the
+// last chunk of a tile whose k range ends half way runs steps 0 and 1 only).
+template <class G, int kU0, int kU1>
+__device__ __forceinline__ void p_compute(f32x16 (&acc)[G::TY][G::TX], const unsigned char *stg,
+                                          const unsigned (&fa_off)[G::STEPS], const unsigned (&fb_off)[G::STEPS],
+                                          const unsigned (&sca)[G::TX], const unsigned (&scb)[G::TY])
+{
+#define KQ_PSTEP(U)                                                                                                  \
+    if constexpr (U >= kU0 && U < kU1) {                                                                                         \
+        u32x4 fa[G::TX], fb[G::TY];                                                                                  \
+        _Pragma("unroll") for (int x = 0; x < G::TX; ++x) fa[x] =                                                    \
+            *(const u32x4 *)(stg + fa_off[U] + x * 32 * G::RB);                                                      \
+        _Pragma("unroll") for (int y = 0; y < G::TY; ++y) fb[y] =                                                    \
+            *(const u32x4 *)(stg + fb_off[U] + y * 32 * G::RB);                                                      \
+        _Pragma("unroll") for (int y = 0; y < G::TY; ++y) _Pragma("unroll") for (int x = 0; x < G::TX; ++x)         \
+            acc[y][x] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fb[y]), widen(fa[x]), acc[y][x], 4, 4, \
+                                                                        U, (int)scb[y], U, (int)sca[x]);             \
+    }
+    KQ_PSTEP(0)
+    KQ_PSTEP(1)
+    KQ_PSTEP(2)
+    KQ_PSTEP(3)
+#undef KQ_PSTEP
+}
+
+constexpr int slab_rows(int bm, int fit)
+{
+    int r = 32;
+    while (r * 2 <= bm && r * 2 <= fit && bm % (r * 2) == 0)
+        r *= 2;
+    return r;
+}
+
+// LDS stores of the epilogue, written as instructions: the compiler cannot
+// tell them apart from the loads still filling other stages and would wait
+// for all of those first.  A store has no output register; the barrier that
+// follows is preceded by an explicit lgkmcnt(0) wait.
+__device__ __forceinline__ void lds_store_b64(unsigned char *p, u32x2 v)
+{
+    const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)p;
+    asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_b128(unsigned char *p, u32x4 v)
+{
+    const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)p;
+    asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+template <class G, bool kBf16>
+__global__ __launch_bounds__(G::T) __attribute__((amdgpu_waves_per_eu(G::OCC, G::OCC))) void mx_gemm_persistent(const uint8_t *__restrict__ qa,
+                                                           const uint8_t *__restrict__ sa, int64_t M,
+                                                           const uint8_t *__restrict__ qb,
+                                                           const uint8_t *__restrict__ sb, int64_t N, int K,
+                                                           void *__restrict__ out, int tilesN, int tiles)
+{
+    __shared__ __align__(16) unsigned char lds0[G::SZ];
+    __shared__ __align__(16) unsigned char lds1[G::SZ];
+    __shared__ __align__(16) unsigned char lds2[G::S > 2 ? G::SZ : 16];
+    __shared__ __align__(16) unsigned char lds3[G::S > 3 ? G::SZ : 16];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    // tiles of this workgroup: XCD x = blockIdx % 8 owns the contiguous range
+    // [x T / 8, (x + 1) T / 8) of tiles (n fastest), and its g = grid / 8
+    // workgroups take every g-th tile of it, so the tiles in flight on one
+    // XCD at any time are neighbours sharing A rows in its L2
+    const unsigned g8 = gridDim.x / kGemmXcds;
+    const unsigned xcd = blockIdx.x % kGemmXcds, slot = blockIdx.x / kGemmXcds;
+    const unsigned lo = (unsigned)(((uint64_t)tiles * xcd) / kGemmXcds);
+    const unsigned hi = (unsigned)(((uint64_t)tiles * (xcd + 1)) / kGemmXcds);
+    if (lo + slot >= hi)
+        return; // uniform, before any barrier
+    const int mine = (int)((hi - lo - slot + g8 - 1) / g8);
+    const int nC = (K + G::KC - 1) / G::KC;
+    const bool half_last = (K % G::KC) != 0; // K % 128 == 0: the last chunk has 2 of 4 steps
+    const int total = mine * nC;
+    const int Kh = K / 2, Ks = K / 32;
+
+    // per-lane load offsets within a tile (the chunk offset is added per load)
+    unsigned voff[G::L];
+#pragma unroll
+    for (int u = 0; u < G::LC; ++u) {
+        const int f = wave + G::W * u; // code load index within the stage
+        const int row = f * G::RPI + lane / G::PR; // stage row: A rows, then B rows
+        const int rot = (row / G::ROWS256) % G::PR;
+        const int mrow = row < G::BM ? row : row - G::BM;
+        voff[u] = (unsigned)(mrow * Kh + (((lane % G::PR) ^ rot) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < G::LS; ++u) {
+        const int f = wave + G::W * u;
+        const int row = f * G::SRPI + (G::SB == 8 ? lane / 2 : lane);
+        const int mrow = row < G::BM ? row : row - G::BM;
+        // a padding load (f >= NSI) carries bit 31: outside every range
+        voff[G::LC + u] = f < G::NSI ? (unsigned)(mrow * Ks + (G::SB == 8 ? (lane & 1) * 4 : 0)) : 0x80000000u;
+    }
+
+    // fragment and scale read offsets within a stage
+    const int wm = wave / G::WN, wn = wave % G::WN;
+    const int i = lane & 31, h = lane >> 5;
+    const int rot_i = (i / G::ROWS256) % G::PR;
+    unsigned fa_off[G::STEPS], fb_off[G::STEPS];
+#pragma unroll
+    for (int u = 0; u < G::STEPS; ++u) {
+        const unsigned p = (unsigned)(((2 * u + h) ^ rot_i) << 4);
+        fa_off[u] = (unsigned)((32 * G::TX * wm + i) * G::RB) + p;
+        fb_off[u] = (unsigned)((G::BM + 32 * G::TY * wn + i) * G::RB) + p;
+    }
+    const unsigned sa_off = (unsigned)(G::SOFF + (32 * G::TX * wm + i) * G::SB);
+    const unsigned sb_off = (unsigned)(G::SOFF + (G::BM + 32 * G::TY * wn + i) * G::SB);
+    // scale word for lane half h: byte u = the scale of block 2u + h
+    const unsigned scale_sel = G::SB == 8 ? (h ? 0x07050301u : 0x06040200u) : (h ? 0x03010301u : 0x02000200u);
+
+    // load cursor: chunk dq of the stream is chunk dkc of tile dtile.  The
+    // cursors advance without branches and the descriptors are rebuilt from
+    // the tile every chunk (a few scalar operations): state written on one
+    // side of a branch only was merged by the compiler into a store through a
+    // selected address, which kept it out of registers.
+    int dq = 0, dkc = 0;
+    unsigned dtile = lo + slot;
+    // Loads of the next chunk of the stream into stage `stg`; past the end of
+    // the stream the same loads go out with bit 31 set in the offset (outside
+    // every range: nothing is fetched), so every wave always has the same
+    // number of loads in flight and the wait below stays a constant.
+    auto load_next = [&](unsigned char *stg) {
+        const int64_t m0 = (int64_t)(dtile / (unsigned)tilesN) * G::BM;
+        const int64_t n0 = (int64_t)(dtile % (unsigned)tilesN) * G::BN;
+        const int64_t ra = (M - m0) < G::BM ? (M - m0) : G::BM;
+        const int64_t rb = (N - n0) < G::BN ? (N - n0) : G::BN;
+        const bool live = dq < total;
+        const __amdgpu_buffer_rsrc_t rca = rsrc(qa + m0 * Kh, live ? ra * Kh : 0);
+        const __amdgpu_buffer_rsrc_t rcb = rsrc(qb + n0 * Kh, live ? rb * Kh : 0);
+        const __amdgpu_buffer_rsrc_t rsa = rsrc(sa + m0 * Ks, live ? ra * Ks : 0);
+        const __amdgpu_buffer_rsrc_t rsb = rsrc(sb + n0 * Ks, live ? rb * Ks : 0);
+        const unsigned addc = live ? (unsigned)(dkc * G::RB) : 0x80000000u;
+        const unsigned adds = live ? (unsigned)(dkc * G::SB) : 0x80000000u;
+#pragma unroll
+        for (int u = 0; u < G::LC; ++u) {
+            const int f = wave + G::W * u;
+            const bool on_a = f * G::RPI < G::BM;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(on_a ? rca : rcb,
+                                                     (__attribute__((address_space(3))) void *)(stg + f * 1024), 16,
+                                                     (int)(voff[u] + addc), 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < G::LS; ++u) {
+            const int f = wave + G::W * u;
+            const bool on_a = f * G::SRPI < G::BM;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                on_a ? rsa : rsb, (__attribute__((address_space(3))) void *)(stg + G::SOFF + f * 256), 4,
+                (int)(voff[G::LC + u] + adds), 0, 0, 0);
+        }
+        ++dq;
+        const bool wrap = dkc == nC - 1;
+        dkc = wrap ? 0 : dkc + 1;
+        dtile += wrap ? g8 : 0u;
+    };
+
+    f32x16 acc[G::TY][G::TX];
+#pragma unroll
+    for (int y = 0; y < G::TY; ++y)
+#pragma unroll
+        for (int x = 0; x < G::TX; ++x)
+            acc[y][x] = f32x16{};
+
+    // store cursor: tile ctile is finished after chunk nC - 1 of it
+    int ckc = 0;
+    unsigned ctile = lo + slot;
+    // Epilogue through LDS, in the stage just multiplied: the tile goes in
+    // row slabs (all of it for bf16; two halves for f32 when a stage is
+    // smaller than the tile) into the stage in the accumulator layout, and
+    // leaves by rows, 16 bytes per lane and whole row segments per store
+    // instruction.  The next chunk's loads target other stages, so they stay
+    // in flight meanwhile; the stage itself is next filled after the barrier
+    // that opens the next step.
+    constexpr int kES = kBf16 ? 2 : 4;
+    constexpr int kOP = kBf16 ? G::BN * 2 + 8 : G::BN * 4 + 16; // padded row pitch in bytes
+    // rows per slab: the largest power-of-two multiple of 32 dividing BM whose
+    // rows fit a stage
+    constexpr int kSR = slab_rows(G::BM, G::SZ / kOP);
+    static_assert(kSR >= 32 && G::BM % kSR == 0, "slabs of whole 32-row blocks");
+    constexpr int kLR = G::BN * kES / 16; // lanes per output row
+    constexpr int kRP = G::T / kLR;       // rows per pass
+    constexpr int kEL = 16 / kES;         // elements per lane
+    static_assert(G::T % kLR == 0 && kSR % kRP == 0, "whole rows per pass");
+    constexpr unsigned kLgkm0 = 0xC07Fu;  // s_waitcnt lgkmcnt(0) alone
+    auto store_tile = [&](unsigned char *stg) {
+        const int64_t m0 = (int64_t)(ctile / (unsigned)tilesN) * G::BM;
+        const int64_t n0 = (int64_t)(ctile % (unsigned)tilesN) * G::BN;
+        const int64_t rows = (M - m0) < G::BM ? (M - m0) : G::BM;
+        const __amdgpu_buffer_rsrc_t ro = rsrc((unsigned char *)out + m0 * N * kES, rows * N * kES);
+        const int c16 = t % kLR;
+        const int64_t col = n0 + c16 * kEL;
+        const unsigned drop = (unsigned)(col >= N) << 31;
+#pragma unroll
+        for (int r0 = 0; r0 < G::BM; r0 += kSR) {
+            // every wave is done reading the stage (products, or the slab before)
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int y = 0; y < G::TY; ++y)
+#pragma unroll
+                for (int x = 0; x < G::TX; ++x) {
+                    const int rb = 32 * G::TX * wm + 32 * x; // uniform: the 32-row block is in or out
+                    if (rb < r0 || rb >= r0 + kSR)
+                        continue;
+                    const int row = rb - r0 + i;
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int c = 32 * G::TY * wn + 32 * y + 8 * gq + 4 * h;
+                        const f32x16 &a = acc[y][x];
+                        if constexpr (kBf16) {
+                            const unsigned w0 =
+                                (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a[4 * gq]) |
+                                ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)a[4 * gq + 1]) << 16);
+                            const unsigned w1 =
+                                (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a[4 * gq + 2]) |
+                                ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)a[4 * gq + 3]) << 16);
+                            lds_store_b64(stg + row * kOP + c * 2, u32x2{w0, w1});
+                        } else {
+                            lds_store_b128(stg + row * kOP + c * 4,
+                                           u32x4{__float_as_uint(a[4 * gq]), __float_as_uint(a[4 * gq + 1]),
+                                                 __float_as_uint(a[4 * gq + 2]), __float_as_uint(a[4 * gq + 3])});
+                        }
+                    }
+                }
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int pss = 0; pss < kSR / kRP; ++pss) {
+                const int rr = t / kLR + pss * kRP;
+                const u32x4 v = *(const u32x4 *)(stg + rr * kOP + c16 * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)((unsigned)(((r0 + rr) * N + col) * kES) | drop),
+                                                       0, 0);
+            }
+        }
+#pragma unroll
+        for (int y = 0; y < G::TY; ++y)
+#pragma unroll
+            for (int x = 0; x < G::TX; ++x)
+                acc[y][x] = f32x16{};
+    };
+
+    // prologue: chunks 0 .. S-2 in flight
+    load_next(lds0);
+    if constexpr (G::S > 2)
+        load_next(lds1);
+    if constexpr (G::S > 3)
+        load_next(lds2);
+
+    // One step of the stream: wait for this wave's loads of chunk q (the
+    // S - 2 later chunks may stay in flight; stores issued since only make
+    // the wait longer), barrier (every wave's loads of chunk q have landed,
+    // and every wave is done with chunk q - 1, whose stage takes chunk
+    // q + S - 1), then multiply.  The stream is padded to a multiple of S
+    // chunks so that every unrolled step runs unconditionally and names its
+    // stage statically (the compiler then tracks which load filled which
+    // stage); a padding step multiplies stale data into accumulators that are
+    // never stored.
+    constexpr int kWait = (G::S - 2) * G::L;
+    static_assert(kWait < 64, "vmcnt field");
+    constexpr unsigned kWaitImm = 0x0F70u | (kWait & 15) | ((kWait >> 4) << 14);
+    int qq = 0;
+    auto step = [&](unsigned char *cur, unsigned char *nxt) {
+        // A plain s_barrier: __syncthreads() adds a workgroup release fence,
+        // which counts the loads still filling later stages as pending LDS
+        // writes and waits for all of them.  What the fence would order is
+        // ordered here already: this wave's loads of chunk q by the wait, its
+        // LDS reads of chunk q - 1 by their use in the products before it,
+        // and the empty asm keeps the compiler from moving LDS accesses
+        // across the barrier.
+        __builtin_amdgcn_s_waitcnt(kWaitImm);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load_next(nxt);
+        const bool last = ckc == nC - 1;
+        unsigned sca[G::TX], scb[G::TY];
+        p_scales<G>(sca, scb, cur, sa_off, sb_off, scale_sel);
+        p_compute<G, 0, 2>(acc, cur, fa_off, fb_off, sca, scb);
+        if (!(half_last && last))
+            p_compute<G, 2, G::STEPS>(acc, cur, fa_off, fb_off, sca, scb);
+        if (last && qq < total)
+            store_tile(cur);
+        ckc = last ? 0 : ckc + 1;
+        ctile += last ? g8 : 0u;
+        ++qq;
+    };
+    for (int q = 0; q < total; q += G::S) {
+        step(lds0, G::S == 2 ? lds1 : G::S == 3 ? lds2 : lds3);
+        step(lds1, lds0);
+        if constexpr (G::S > 2)
+            step(lds2, lds1);
+        if constexpr (G::S > 3)
+            step(lds3, lds2);
+    }
+}
+
+} // namespace
+
+namespace {
+
+int gemm_cus()
+{
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
+// Resident workgroups per CU of a kernel (from the runtime), cached per kernel.
+int gemm_occupancy(const void *fn, int threads)
+{
+    static const void *keys[8] = {};
+    static int vals[8] = {};
+    for (int i = 0; i < 8; ++i)
+        if (keys[i] == fn)
+            return vals[i];
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu <= 0)
+        per_cu = 1;
+    for (int i = 0; i < 8; ++i)
+        if (!keys[i]) {
+            keys[i] = fn;
+            vals[i] = per_cu;
+            break;
+        }
+    return per_cu;
+}
+
+template <class G>
+hipError_t launch_persistent(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
+                             int64_t N, int64_t K, void *out, int bf16, hipStream_t stream)
+{
+    const int64_t tilesM = (M + G::BM - 1) / G::BM, tilesN = (N + G::BN - 1) / G::BN;
+    const int64_t tiles = tilesM * tilesN;
+    if (tiles > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const void *fn = bf16 ? (const void *)mx_gemm_persistent<G, true> : (const void *)mx_gemm_persistent<G, false>;
+    int64_t grid = (int64_t)gemm_cus() * gemm_occupancy(fn, G::T);
+    const int64_t tiles8 = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
+    if (grid > tiles8)
+        grid = tiles8;
+    grid = grid / kGemmXcds * kGemmXcds;
+    if (grid < (int64_t)kGemmXcds)
+        grid = kGemmXcds;
+    int Ki = (int)K, tn = (int)tilesN, tt = (int)tiles;
+    void *args[] = {(void *)&qa, (void *)&sa, (void *)&M, (void *)&qb, (void *)&sb, (void *)&N, (void *)&Ki,
+                    (void *)&out, (void *)&tn, (void *)&tt};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(G::T), args, 0, stream);
+}
+
+// 128 x 128 tiles, 4 waves of 64 x 64, two workgroups per CU.  Measured on
+// the transformer layer shapes: k chunks of 256 in a ring of 2 stages (68 KB)
+// beat chunks of 128 in a ring of 4 (68 KB), and every one-workgroup-per-CU
+// form (rings of 3 or 4 chunks of 256, 256 x 128 and 128 x 256 tiles), where
+// a single wave per SIMD leaves the LDS and matrix-core latencies exposed.
+using GemmP256 = PGeom<2, 2, 2, 2, 256, 2>;
+using GemmP128 = PGeom<2, 2, 2, 2, 128, 4>;
+
 } // namespace
 
 hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
                           int64_t N, int64_t K, void *out, int bf16, hipStream_t stream)
 {
+    // the persistent form stores whole 16-byte output pieces and reads whole
+    // dwords of scales
+    const bool persistent = K % 128 == 0 && N % (bf16 ? 8 : 4) == 0 && (uintptr_t)out % 16 == 0 &&
+                            (uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0;
+    const int variant = tuning().gemm_variant;
+    if (persistent && variant != 1) {
+        if (variant == 3)
+            return launch_persistent<GemmP128>(qa, sa, M, qb, sb, N, K, out, bf16, stream);
+        return launch_persistent<GemmP256>(qa, sa, M, qb, sb, N, K, out, bf16, stream);
+    }
     const int64_t tilesM = (M + kBM - 1) / kBM, tilesN = (N + kBN - 1) / kBN;
     const int64_t grid = (tilesM * tilesN + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
     if (grid > 0x7FFFFFFF)

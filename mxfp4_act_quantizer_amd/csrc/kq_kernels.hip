@@ -43,7 +43,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0, 0, 0, 0, 0};
+    static Tuning t{0, 0, 0, 0, 0, 0, 0, 0};
     return t;
 }
 

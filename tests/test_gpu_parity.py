@@ -553,6 +553,57 @@ def test_mx_gemm_against_oracle(K_lib, M, N, Kd):
     assert torch.equal(outb.cpu().view(torch.int16), rne.view(torch.int16))
 
 
+# Shapes on the persistent path (K % 128 == 0, 16-byte output pieces):
+# a k range ending half way through a 256-wide chunk, one chunk per tile
+# (the epilogue after every chunk), ragged M and N, and more tiles than
+# resident workgroups (528 tiles: some workgroups run two).
+PERSIST_CASES = [(1000, 520, 384), (300, 4104, 640), (64, 64, 128), (129, 136, 256), (4160, 2048, 256)]
+
+
+@pytest.mark.parametrize("M,N,Kd", PERSIST_CASES, ids=[f"{m}x{n}x{k}" for m, n, k in PERSIST_CASES])
+def test_mx_gemm_persistent_against_oracle(K_lib, M, N, Kd):
+    qa, sa = _mx_operand(M, Kd, 9600 + M)
+    qb, sb = _mx_operand(N, Kd, 9700 + N)
+    say(f"[mx_gemm persistent] M={M} N={N} K={Kd}")
+    d = [torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)]
+    out = K_lib.mx_gemm(*d)
+    outb = K_lib.mx_gemm(*d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    # the oracle on 40 sampled rows, both ends of the first and last row tiles
+    rng = np.random.default_rng(9800 + M)
+    rows = np.unique(np.concatenate([[0, 127 % M, M - 1, max(M - 128, 0)], rng.integers(0, M, 36)]))
+    ref, mag = O.mx_gemm(qa[rows], sa[rows], qb, sb)
+    o = out.cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(o - ref)
+    assert np.all(err <= _gemm_tol(Kd, mag) + 1e-300), float((err / (mag + 1e-300)).max())
+    rne = torch.from_numpy(out.cpu().numpy()).to(torch.bfloat16)
+    assert torch.equal(outb.cpu().view(torch.int16), rne.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,Kd", [(8192, 3456, 1152), (1000, 520, 384), (64, 64, 128), (4160, 2048, 256)],
+                         ids=["dit_qkv", "ragged", "one_chunk", "two_tiles_per_wg"])
+def test_mx_gemm_kernels_agree(K_lib, M, N, Kd):
+    # The persistent kernels (k chunks of 256 and of 128) and the per-tile
+    # kernel accumulate the same fp32 sums in the same k order: outputs equal
+    # bit for bit, in both output types.
+    qa, sa = _mx_operand(M, Kd, 9900 + M)
+    qb, sb = _mx_operand(N, Kd, 9901 + N)
+    d = [torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)]
+    try:
+        for dt in (torch.float32, torch.bfloat16):
+            outs = []
+            for v in (1, 2, 3):
+                say(f"[mx_gemm kernels] M={M} N={N} K={Kd} dtype={dt} variant={v}")
+                K_lib.set_tuning(7, v)
+                outs.append(K_lib.mx_gemm(*d, out_dtype=dt))
+            torch.cuda.synchronize()
+            iv = torch.int32 if dt == torch.float32 else torch.int16
+            for o in outs[1:]:
+                assert torch.equal(o.view(iv), outs[0].view(iv))
+    finally:
+        K_lib.set_tuning(7, 0)
+
+
 def test_mx_gemm_output_alignment_and_guards(K_lib):
     # The product written into caller buffers that start 4 or 2 bytes past a
     # 16-byte boundary (element-wise stores) must equal the one written into
