@@ -340,7 +340,8 @@ def gemm_bench(args):
     own kernels on synthetic data; each shape a graph of --steps launches over
     rotating operand sets, timed with HIP events.  Roofline per shape:
     max(2MNK / FP4 peak, bytes / HBM peak) with bytes = A, B codes and scales
-    plus the bf16 output."""
+    plus the bf16 output.  The per-tile kernel (the fallback for shapes the
+    persistent kernel does not take) is timed on the same operands beside it."""
     import torch
 
     import mxfp4_act_quantizer_amd as K
@@ -383,13 +384,21 @@ def gemm_bench(args):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
+        # the per-tile kernel on the same operands, for comparison
+        K.set_tuning(7, 1)
+        try:
+            us_tile = _time_leg(lambda i: K.mx_gemm(*sets[i][:4], out=sets[i][4],
+                                                    stream=torch.cuda.current_stream()), nsets, args.steps) * 1e6
+        finally:
+            K.set_tuning(7, 0)
         flops = 2.0 * M * N * Kd
         t_mfma = flops / (FP4_PEAK_TFLOPS * 1e12) * 1e6
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
         row = {"layer": name, "M": M, "N": N, "K": Kd, "us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
                "GB/s": round(nbytes / us / 1e3, 1), "bound": bound,
-               "roofline_us": round(max(t_mfma, t_hbm), 2), "frac": round(max(t_mfma, t_hbm) / us, 4)}
+               "roofline_us": round(max(t_mfma, t_hbm), 2), "frac": round(max(t_mfma, t_hbm) / us, 4),
+               "per_tile_kernel_us": round(us_tile, 2)}
         rows.append(row)
         print(json.dumps(row), flush=True)
         del sets
@@ -397,7 +406,8 @@ def gemm_bench(args):
     tot_us = sum(r["us"] for r in rows)
     tot_roof = sum(r["roofline_us"] for r in rows)
     print(json.dumps({"gemm_block_us": round(tot_us, 2), "roofline_us": round(tot_roof, 2),
-                      "frac": round(tot_roof / tot_us, 4)}), flush=True)
+                      "frac": round(tot_roof / tot_us, 4),
+                      "per_tile_kernel_block_us": round(sum(r["per_tile_kernel_us"] for r in rows), 2)}), flush=True)
 
 
 def _time_leg(fn, nsets, steps):
