@@ -13,12 +13,17 @@
 // accumulator holds D[row 8(v/4) + 4(l/32) + v%4][column l % 32] in element
 // v of lane l.
 //
-// Data path: 128 x 128 output tile per workgroup of 4 waves (64 x 64 per
-// wave as 2 x 2 MFMA tiles), two workgroups per CU.  k advances in chunks
-// of 256 (4 MFMA steps): codes and scales of a chunk go global -> registers
-// (buffer loads, two chunks ahead) -> LDS (double buffered) -> fragments.
-// The finished tile goes back through LDS so that every store instruction
-// writes whole 256-byte (bf16) or 512-byte (f32) row segments.
+// Two kernels share that operand handling, both with 128 x 128 output tiles
+// per workgroup of 4 waves (64 x 64 per wave as 2 x 2 MFMA tiles) and two
+// workgroups per CU, and both send the finished tile back through LDS so
+// that every store instruction writes whole 256-byte (bf16) or 512-byte
+// (f32) row segments:
+//  - mx_gemm_persistent (K % 128 == 0, whole 16-byte output pieces): one
+//    resident round of workgroups, each streaming the k chunks of all its
+//    tiles through a ring of LDS stages filled by LDS-DMA loads;
+//  - mx_gemm_kernel (every other shape): one workgroup per tile, chunks of
+//    256 going global -> registers (two chunks ahead) -> LDS (double
+//    buffered) -> fragments.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
