@@ -351,3 +351,15 @@ def test_kq16_validation():
     assert raw("kq_transform16_f32", x, 4, 40, f, 1, y, None) == K.KQ_ERR_SHAPE
     assert raw("kq_transform16_f32", x, 4, 48, f, 3, x + 16, None) == K.KQ_ERR_OVERLAP
     assert raw("kq_transform16_f32", x, 4, 48, f, 3, y + 4, None) == K.KQ_ERR_ALIGN
+
+
+def test_tuning_keys():
+    # the launch-shape knobs: keys 0..7 are accepted (and reset to automatic),
+    # anything else is refused; no HIP call is made
+    L = K.lib()
+    for key in range(8):
+        assert L.kq_set_tuning(key, 0) == K.KQ_OK
+    for key in (-1, 8, 100):
+        assert L.kq_set_tuning(key, 0) == K.KQ_ERR_ARG
+    with pytest.raises(K.KQError):
+        K.set_tuning(8, 1)
