@@ -357,8 +357,8 @@ def set_tuning(key, value):
     """Launch-shape knobs for measurements (0 = automatic everywhere): 0 MFMA tiles
     per workgroup, 1 butterfly rows/wave, 2 SmoothQuant/fp32 rows/wave, 3 MFMA
     token groups (1 contiguous, 2 interleaved), 4 MFMA strip width (8 or 16
-    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat), 6 AdaLN rows per
-    workgroup, 7 W4A4 product kernel (1 per-tile, 2 persistent with k chunks of
+    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat), 6 AdaLN row blocks
+    per wave (rounded up to 4), 7 W4A4 product kernel (1 per-tile, 2 persistent with k chunks of
     256, 3 persistent with k chunks of 128; the persistent forms apply when K %
     128 == 0 and the output rows split into 16-byte pieces)."""
     _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")

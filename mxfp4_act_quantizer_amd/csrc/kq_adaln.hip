@@ -17,11 +17,11 @@
 //                        1/sqrt(var + eps) in fp64 into a 16-byte record.
 //                        h is read with the default cache policy so that the
 //                        second pass finds it in the caches.
-//   adaln_stream_kernel  the streaming quantizer's structure (one lane per 8
-//                        channels, a wave per 512-channel column tile walking
-//                        a run of rows): the row's record arrives by scalar
-//                        loads, the lane's modulation and butterfly factors
-//                        stay in registers; per element fp64 normalisation,
+//   adaln_stream_kernel  one lane per 8 channels in flat row blocks (every
+//                        lane busy at any width; see adaln_stage): the row
+//                        records arrive by per-lane loads, the lane's
+//                        modulation and butterfly factors stay in registers;
+//                        per element fp64 normalisation,
 //                        bf16 rounding from the double value, then the
 //                        butterfly transform and MX step shared with
 //                        kq_quantize_ex's butterfly variant (kQuant), or the
@@ -42,7 +42,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAuxNTa = 2;   // nontemporal: the second pass reads h for the last time
 constexpr int kStatRows = 2;   // rows per wave of the statistics kernel
 constexpr int kStatChunks = 4; // 16-byte pieces per lane and row loaded at a time
-constexpr int kU = 4;        // rows per pipeline stage of the streaming pass
+constexpr int kU = 4;        // row blocks per pipeline stage of the streaming pass
 
 // x = (h - mu) * (rstd * g) + t in double for 8 channels, rounded once to the
 // nearest bf16 (ties to even) and packed two per dword.  The double -> float
@@ -183,35 +183,41 @@ __device__ __forceinline__ void load_rows(HRows &in, __amdgpu_buffer_rsrc_t rh, 
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)((mr + u) * d * 2) + lane_off), 0, kAuxNTa));
 }
 
+// Flat row blocks.  Rb = 64 / gcd(nOct, 64) rows of nOct octets (8 channels
+// each) are a whole number Wb = Rb nOct / 64 of waves with every lane busy
+// (a 512-channel column tile per wave would leave lanes idle at d = 1152).
+// Lane l of wave wb of a block takes the block's flat octet f = 64 wb + l:
+// row f / nOct of the block, octet f % nOct, the same octet in every block,
+// so the lane's factors and modulation stay in registers.  A wave walks the
+// kIt blocks of its group, kU blocks per pipeline stage; a wave's loads and
+// code stores cover 64 consecutive octets of memory.
 template <bool kQuant>
-__device__ __forceinline__ void adaln_process(const HRows &in, int64_t m, int64_t m0, int64_t m1, int d, int oct,
-                                              int octc, bool cok, int qp, const double *__restrict__ stats,
-                                              const float *__restrict__ shift, const float *__restrict__ scale,
-                                              int64_t T, Modulation &md, const Bfly &B, __amdgpu_buffer_rsrc_t rq,
-                                              __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rxo)
+__device__ __forceinline__ void adaln_stage(const HRows &in, int64_t rb0, int ro, int Rb, int64_t M, int64_t mlo,
+                                            int d, int oct, int qp, const double *__restrict__ stats,
+                                            const float *__restrict__ shift, const float *__restrict__ scale,
+                                            int64_t T, Modulation &md, const Bfly &B, __amdgpu_buffer_rsrc_t rq,
+                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rxo)
 {
     const int nB = d >> 5;
-    // the stage's records, all requested before any is used (rows past the
-    // run read the run's last record, which is never used)
+    // the stage's row records, all requested before any is used (rows past M
+    // read the last record; nothing of theirs is stored)
     double mus[kU], rstds[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-        const int64_t mc = (m + u < m1) ? m + u : m1 - 1;
+        const int64_t m = rb0 + (int64_t)u * Rb + ro;
+        const int64_t mc = m < M ? m : M - 1;
         mus[u] = stats[2 * mc];
         rstds[u] = stats[2 * mc + 1];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-        const int64_t mm = m + u;
-        if (mm >= m1)
-            break; // wave-uniform
-        const double mu = mus[u], rstd = rstds[u];
-        if (mm >= md.next)
-            load_modulation(md, shift, scale, mm / T, T, d, octc);
+        const int64_t m = rb0 + (int64_t)u * Rb + ro;
+        if (m >= md.next)
+            load_modulation(md, shift, scale, (m < M ? m : M - 1) / T, T, d, oct);
         unsigned xw[4];
-        adaln_bf16x8(in.v[u], mu, rstd, md.g, md.t, xw);
-        const int mr = (int)(mm - m0);
-        const unsigned drop = (unsigned)(cok ? 0 : 1) << 31;
+        adaln_bf16x8(in.v[u], mus[u], rstds[u], md.g, md.t, xw);
+        // rows past M fall outside the output ranges, which end at row M
+        const int mr = (int)(m - mlo);
         if constexpr (kQuant) {
             float v[8];
 #pragma unroll
@@ -220,19 +226,20 @@ __device__ __forceinline__ void adaln_process(const HRows &in, int64_t m, int64_
             bfly_stages(v, B);
             unsigned b;
             const unsigned w = mx_encode_quad(v, b);
-            const unsigned drop_s = drop | ((unsigned)(qp != 0) << 31);
-            __builtin_amdgcn_raw_buffer_store_b32(w, rq, (int)((unsigned)(mr * (d >> 1) + oct * 4) | drop), 0, 0);
+            const unsigned drop_s = (unsigned)(qp != 0) << 31;
+            __builtin_amdgcn_raw_buffer_store_b32(w, rq, mr * (d >> 1) + oct * 4, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)((unsigned)(mr * nB + (oct >> 2)) | drop_s), 0,
                                                  0);
         } else {
             const u32x4 o = {xw[0], xw[1], xw[2], xw[3]};
-            __builtin_amdgcn_raw_buffer_store_b128(o, rxo, (int)((unsigned)(mr * d * 2 + oct * 16) | drop), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(o, rxo, mr * d * 2 + oct * 16, 0, 0);
         }
     }
 }
 
-// A workgroup covers four column tiles of one run of rows; the runs are dealt
-// to the XCDs in turn (blockIdx % 8), all column groups of a run on one XCD.
+// The workgroups (4 waves each) are dealt so that each XCD (blockIdx % 8) runs
+// a contiguous range of waves: the partial lines of the scale rows written by
+// neighbouring waves merge in one L2.
 template <bool kQuant>
 __global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__restrict__ h, int64_t M, int d,
                                                            const double *__restrict__ stats,
@@ -240,47 +247,62 @@ __global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__res
                                                            const float *__restrict__ scale, int64_t T,
                                                            const float *__restrict__ factors, int per_block,
                                                            uint8_t *__restrict__ q, uint8_t *__restrict__ s,
-                                                           uint16_t *__restrict__ xo, int rows_per_wave, int nCT)
+                                                           uint16_t *__restrict__ xo, int Rb, int Wb, int kIt)
 {
     const int lane = threadIdx.x & 63;
-    const int nCG = (nCT + 3) / 4;
-    const unsigned xcd = blockIdx.x % 8u;
-    const unsigned slot = blockIdx.x / 8u;
-    const int cg = (int)(slot % (unsigned)nCG);
-    const int64_t rg = (int64_t)(slot / (unsigned)nCG) * 8 + xcd;
-    const int ct = cg * 4 + (threadIdx.x >> 6);
-    const int64_t m0 = rg * rows_per_wave;
-    if (m0 >= M || ct >= nCT)
+    const unsigned per_xcd = gridDim.x / 8u;
+    const int64_t wg = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
+    const int64_t gw = wg * 4 + (threadIdx.x >> 6); // global wave
+    const int64_t grp = gw / Wb;
+    const int wb = (int)(gw % Wb);
+    const int64_t mlo = grp * kIt * Rb; // first row of the group
+    if (mlo >= M)
         return; // wave-uniform; no barrier in this kernel
-    const int64_t m1 = (m0 + rows_per_wave < M) ? m0 + rows_per_wave : M;
+    const int64_t mhi = (mlo + (int64_t)kIt * Rb < M) ? mlo + (int64_t)kIt * Rb : M;
     const int nOct = d >> 3;
-    const int oct = ct * 64 + lane;
-    const bool cok = oct < nOct;
-    const int octc = cok ? oct : nOct - 1; // parameter index for lanes past the row end (nothing stored)
-    const int qp = lane & 3;
-    const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + m0 * d), (m1 - m0) * d * 2);
-    const unsigned lane_off = (unsigned)(oct * 16) | ((unsigned)(cok ? 0 : 1) << 31);
-    HRows bufA, bufB;
-    load_rows(bufA, rh, 0, d, lane_off);
-    const __amdgpu_buffer_rsrc_t rq = out_buffer(kQuant ? q + m0 * (d >> 1) : nullptr, kQuant ? (m1 - m0) * (d >> 1) : 0);
-    const __amdgpu_buffer_rsrc_t rs = out_buffer(kQuant ? s + m0 * (d >> 5) : nullptr, kQuant ? (m1 - m0) * (d >> 5) : 0);
-    const __amdgpu_buffer_rsrc_t rxo = out_buffer(kQuant ? nullptr : xo + m0 * d, kQuant ? 0 : (m1 - m0) * d * 2);
+    const int f = wb * 64 + lane;
+    const int ro = f / nOct;  // row within a block
+    const int oct = f - ro * nOct;
+    const int qp = lane & 3;  // == oct & 3: 64 wb is a multiple of 4
+    const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + mlo * d), (mhi - mlo) * d * 2);
+    const __amdgpu_buffer_rsrc_t rq = out_buffer(kQuant ? q + mlo * (d >> 1) : nullptr, kQuant ? (mhi - mlo) * (d >> 1) : 0);
+    const __amdgpu_buffer_rsrc_t rs = out_buffer(kQuant ? s + mlo * (d >> 5) : nullptr, kQuant ? (mhi - mlo) * (d >> 5) : 0);
+    const __amdgpu_buffer_rsrc_t rxo = out_buffer(kQuant ? nullptr : xo + mlo * d, kQuant ? 0 : (mhi - mlo) * d * 2);
+    // row (block k, lane row ro) of the group starts at byte (k Rb + ro) d 2 of
+    // rh; rows past M fall outside its range and read as zeros
+    const unsigned lane_off = (unsigned)((ro * d + oct * 8) * 2);
+    const unsigned blk_bytes = (unsigned)(Rb * d * 2);
+    auto load_stage = [&](HRows &in, int k0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            in.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rh, (int)(lane_off + (unsigned)(k0 + u) * blk_bytes), 0, kAuxNTa));
+    };
     Bfly B;
     if constexpr (kQuant)
-        bfly_setup(B, factors + (int64_t)(per_block ? (octc >> 2) : 0) * 20, qp);
+        bfly_setup(B, factors + (int64_t)(per_block ? (oct >> 2) : 0) * 20, qp);
     Modulation md;
-    load_modulation(md, shift, scale, m0 / T, T, d, octc);
-
-    // two-stage pipeline; a prefetch past the run falls outside the range and fetches nothing
-    int64_t m = m0;
-    for (; m + kU < m1; m += 2 * kU) {
-        load_rows(bufB, rh, (int)(m + kU - m0), d, lane_off);
-        adaln_process<kQuant>(bufA, m, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
-        load_rows(bufA, rh, (int)(m + 2 * kU - m0), d, lane_off);
-        adaln_process<kQuant>(bufB, m + kU, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
+    {
+        const int64_t m = mlo + ro;
+        load_modulation(md, shift, scale, (m < M ? m : M - 1) / T, T, d, oct);
     }
-    if (m < m1)
-        adaln_process<kQuant>(bufA, m, m0, m1, d, oct, octc, cok, qp, stats, shift, scale, T, md, B, rq, rs, rxo);
+
+    // two-stage pipeline over the group's blocks; loads past the group fall
+    // outside the range and fetch nothing
+    HRows bufA, bufB;
+    load_stage(bufA, 0);
+    int k = 0;
+    for (; k + kU < kIt; k += 2 * kU) {
+        load_stage(bufB, k + kU);
+        adaln_stage<kQuant>(bufA, mlo + (int64_t)k * Rb, ro, Rb, M, mlo, d, oct, qp, stats, shift, scale, T, md, B,
+                            rq, rs, rxo);
+        load_stage(bufA, k + 2 * kU);
+        adaln_stage<kQuant>(bufB, mlo + (int64_t)(k + kU) * Rb, ro, Rb, M, mlo, d, oct, qp, stats, shift, scale, T,
+                            md, B, rq, rs, rxo);
+    }
+    if (k < kIt)
+        adaln_stage<kQuant>(bufA, mlo + (int64_t)k * Rb, ro, Rb, M, mlo, d, oct, qp, stats, shift, scale, T, md, B,
+                            rq, rs, rxo);
 }
 
 } // namespace
@@ -292,13 +314,20 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
     // pass 1: row statistics
     const int64_t waves = (M + kStatRows - 1) / kStatRows;
     const int64_t grid1 = (waves + 3) / 4;
-    // pass 2: runs of R rows, four column tiles per workgroup, runs dealt to the XCDs
-    const int nCT = (int)((d / 8 + 63) / 64);
-    int R = tuning().adaln_rows_per_wg;
-    if (R <= 0)
-        R = 4; // one pipeline stage per wave: more, shorter waves (measured best of 4..32 on MI355X)
-    const int64_t nRG = (M + R - 1) / R;
-    const int64_t grid2 = (nRG + 7) / 8 * 8 * ((nCT + 3) / 4);
+    // pass 2: flat row blocks of Rb rows = Wb full waves; kIt blocks per wave
+    const int nOct = (int)(d / 8);
+    int g = 64;
+    while (nOct % g)
+        g >>= 1; // gcd(nOct, 64): nOct is a multiple of 4
+    const int Rb = 64 / g;
+    const int Wb = Rb * nOct / 64;
+    int kIt = tuning().adaln_blocks_per_wave;
+    if (kIt <= 0)
+        kIt = kU; // blocks per wave: one pipeline stage (measured best of 4..16 on MI355X)
+    kIt = (kIt + kU - 1) / kU * kU;
+    const int64_t nGroups = (M + (int64_t)kIt * Rb - 1) / ((int64_t)kIt * Rb);
+    const int64_t nWaves = nGroups * Wb;
+    const int64_t grid2 = ((nWaves + 3) / 4 + 7) / 8 * 8;
     if (grid1 > 0x7FFFFFFF || grid2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;
@@ -308,9 +337,10 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
         return e;
     int per_block = nT > 1 ? 1 : 0;
     const double *cst = stats;
+    int rb = Rb, wbn = Wb, kit = kIt;
     void *args2[] = {(void *)&h,     (void *)&M, (void *)&di,      (void *)&cst,       (void *)&shift,
                      (void *)&scale, (void *)&T, (void *)&factors, (void *)&per_block, (void *)&q,
-                     (void *)&s,     (void *)&x, (void *)&R,       (void *)&nCT};
+                     (void *)&s,     (void *)&x, (void *)&rb,      (void *)&wbn,       (void *)&kit};
     const void *fn = x == nullptr ? (const void *)adaln_stream_kernel<true> : (const void *)adaln_stream_kernel<false>;
     return hipLaunchKernel(fn, dim3((unsigned)grid2), dim3(256), args2, 0, stream);
 }

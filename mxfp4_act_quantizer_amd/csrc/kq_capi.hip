@@ -397,7 +397,7 @@ int kq_set_tuning(int key, int value)
     case 3: kq::tuning().mfma_interleave = value; return KQ_OK;
     case 4: kq::tuning().mfma_strip = value; return KQ_OK;
     case 5: kq::tuning().mfma_order = value; return KQ_OK;
-    case 6: kq::tuning().adaln_rows_per_wg = value; return KQ_OK;
+    case 6: kq::tuning().adaln_blocks_per_wave = value; return KQ_OK;
     case 7: kq::tuning().gemm_variant = value; return KQ_OK;
     default: return KQ_ERR_ARG;
     }

@@ -14,7 +14,7 @@ struct Tuning {
     int mfma_interleave;      // 0 = automatic, 1 = contiguous token groups, 2 = interleaved groups
     int mfma_strip;           // 0 = automatic, 8 or 16 blocks per workgroup
     int mfma_order;           // 0 = automatic, 1 = XCD-grouped workgroups, 2 = flat order
-    int adaln_rows_per_wg;    // 0 = automatic: token rows per workgroup of the AdaLN front-end
+    int adaln_blocks_per_wave;    // 0 = automatic: row blocks per wave of the AdaLN front-end's second pass
     int gemm_variant;         // 0 = automatic, 1 = per-tile kernel, 2 / 3 = persistent, k chunks of 256 / 128
 };
 Tuning &tuning();
