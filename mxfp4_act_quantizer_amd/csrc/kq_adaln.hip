@@ -237,9 +237,6 @@ __device__ __forceinline__ void adaln_stage(const HRows &in, int64_t rb0, int ro
     }
 }
 
-// The workgroups (4 waves each) are dealt so that each XCD (blockIdx % 8) runs
-// a contiguous range of waves: the partial lines of the scale rows written by
-// neighbouring waves merge in one L2.
 template <bool kQuant>
 __global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__restrict__ h, int64_t M, int d,
                                                            const double *__restrict__ stats,
@@ -250,18 +247,21 @@ __global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__res
                                                            uint16_t *__restrict__ xo, int Rb, int Wb, int kIt)
 {
     const int lane = threadIdx.x & 63;
-    const unsigned per_xcd = gridDim.x / 8u;
-    const int64_t wg = (int64_t)(blockIdx.x % 8u) * per_xcd + blockIdx.x / 8u;
-    const int64_t gw = wg * 4 + (threadIdx.x >> 6); // global wave
-    const int64_t grp = gw / Wb;
-    const int wb = (int)(gw % Wb);
+    // groups go to the XCDs in turn (blockIdx % 8), all waves of a group on
+    // one XCD: the XCDs stream one compact band of rows together, and the
+    // partial lines of a group's scale rows merge in one L2
+    const unsigned xcd = blockIdx.x % 8u;
+    const unsigned j = (blockIdx.x / 8u) * 4u + (threadIdx.x >> 6); // wave of this XCD (32-bit: the
+    const unsigned jg = j / (unsigned)Wb;                            // divisions run once per short-lived wave)
+    const int64_t grp = (int64_t)jg * 8 + xcd;
+    const int wb = (int)(j - jg * (unsigned)Wb);
     const int64_t mlo = grp * kIt * Rb; // first row of the group
     if (mlo >= M)
         return; // wave-uniform; no barrier in this kernel
     const int64_t mhi = (mlo + (int64_t)kIt * Rb < M) ? mlo + (int64_t)kIt * Rb : M;
     const int nOct = d >> 3;
     const int f = wb * 64 + lane;
-    const int ro = f / nOct;  // row within a block
+    const int ro = (int)((unsigned)f / (unsigned)nOct); // row within a block
     const int oct = f - ro * nOct;
     const int qp = lane & 3;  // == oct & 3: 64 wb is a multiple of 4
     const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + mlo * d), (mhi - mlo) * d * 2);
@@ -325,9 +325,12 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
     if (kIt <= 0)
         kIt = kU; // blocks per wave: one pipeline stage (measured best of 4..16 on MI355X)
     kIt = (kIt + kU - 1) / kU * kU;
+    // a group's byte offsets, the prefetch past it included, stay below 2^31
+    while (kIt > kU && (int64_t)(kIt + 2 * kU) * Rb * d * 2 >= ((int64_t)1 << 31))
+        kIt -= kU;
     const int64_t nGroups = (M + (int64_t)kIt * Rb - 1) / ((int64_t)kIt * Rb);
-    const int64_t nWaves = nGroups * Wb;
-    const int64_t grid2 = ((nWaves + 3) / 4 + 7) / 8 * 8;
+    const int64_t wavesPerXcd = (nGroups + 7) / 8 * Wb;
+    const int64_t grid2 = (wavesPerXcd + 3) / 4 * 8;
     if (grid1 > 0x7FFFFFFF || grid2 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     int di = (int)d;
