@@ -447,7 +447,8 @@ def adaln_bench(args):
     the unfused pipeline (adaln_modulate writing bf16 x, then kq_quantize with
     the MFMA or the butterfly transform) and against torch's layer_norm and
     modulation (bf16 out) followed by kq_quantize, at the hidden widths, two samples
-    (CFG) per batch.  Fused algorithmic bytes: 2.53125 B per element (h read,
+    (CFG) per batch.  Two more fused legs select the butterfly second pass and
+    the matrix-core second pass in strips of 4 blocks.  Fused algorithmic bytes: 2.53125 B per element (h read,
     codes and scales written) plus the modulation; unfused: 6.53125 (x
     written and read back).  Per-block factor sets; h drawn on the GPU as
     N(0,1) with 1% outlier channels x50 (the time does not depend on the
@@ -508,7 +509,20 @@ def adaln_bench(args):
                 x = (n * (1.0 + scale[idx]) + shift[idx]).to(torch.bfloat16)
             K.kq_quantize(x, f, b["q"], b["s"], stream=cur())
 
+        def fused_with(knobs):
+            def run(i):
+                for key, val in knobs.items():
+                    K.set_tuning(key, val)
+                try:
+                    fused(i)
+                finally:
+                    for key in knobs:
+                        K.set_tuning(key, 0)
+            return run
+
         t = {"fused": _time_leg(fused, nsets, args.steps),
+             "fused_butterfly_pass": _time_leg(fused_with({8: 2}), nsets, args.steps),
+             "fused_mfma_strip4": _time_leg(fused_with({8: 1, 9: 4}), nsets, args.steps),
              "torch_layernorm_then_kq_mfma": _time_leg(torch_unfused, nsets, args.steps),
              "unfused_mfma": _time_leg(unfused(1), nsets, args.steps),
              "unfused_butterfly": _time_leg(unfused(2), nsets, args.steps),

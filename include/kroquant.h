@@ -187,9 +187,9 @@ int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *fac
  * (nearest, ties to even) from its double value, then the Kronecker transform
  * of every 32-channel block and MXFP4 as kq_quantize.  The normalised x is
  * never written: one pass writes the row statistics into `stats`, a second
- * reads h again and quantizes.  The transform is the butterfly form
- * (KQ_VARIANT_BUTTERFLY); the result equals
- * kq_quantize_ex(adaln_modulate(h), ..., KQ_VARIANT_BUTTERFLY) bit for bit.
+ * reads h again, normalises it while staging it for the matrix cores, and
+ * quantizes.  The transform is the default (KQ_VARIANT_MFMA) form; the result
+ * equals kq_quantize(adaln_modulate(h), ...) bit for bit.
  *   h      dev, bf16 [M, d] (the residual stream), 16-byte aligned
  *   shift  dev, float32 [ceil(M / tokens_per_sample), d], 4-byte aligned
  *   scale  dev, float32, same shape and alignment as shift

@@ -360,7 +360,9 @@ def set_tuning(key, value):
     blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat), 6 AdaLN row blocks
     per wave (rounded up to 4), 7 W4A4 product kernel (1 per-tile, 2 persistent with k chunks of
     256, 3 persistent with k chunks of 128; the persistent forms apply when K %
-    128 == 0 and the output rows split into 16-byte pieces)."""
+    128 == 0 and the output rows split into 16-byte pieces), 8 AdaLN second pass of
+    kq_adaln_quantize (1 matrix cores, 2 butterfly), 9 its matrix-core strip width
+    (4 or 8 blocks)."""
     _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
 
 

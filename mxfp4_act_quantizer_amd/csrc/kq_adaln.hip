@@ -10,7 +10,13 @@
 // Kronecker transform of every 32-channel block and MXFP4.  The normalised x
 // never goes to memory.
 //
-// Two streaming kernels, no barriers:
+// The statistics kernel, then one of two second passes:
+//   - by default the MFMA quantizer kernel in its AdaLN form
+//     (kq_kernels.hip): h is normalised and modulated by adaln_bf16x8 as it
+//     is staged for the matrix cores, so the result equals kq_quantize of
+//     the x that adaln_modulate writes, bit for bit;
+//   - adaln_stream_kernel below, which also writes x for adaln_modulate.
+// Streaming kernels of this file, no barriers:
 //   adaln_stats_kernel   one wave per run of rows: per row, the sum and the
 //                        sum of squares of h in fp64 (lane-strided over the
 //                        row, then a wave reduction), mean and
@@ -26,8 +32,8 @@
 //                        butterfly transform and MX step shared with
 //                        kq_quantize_ex's butterfly variant (kQuant), or the
 //                        bf16 x written out (the unfused front-end).
-// Both modes read the same records, so the fused result equals the butterfly
-// quantizer applied to the written x bit for bit.
+// Both modes read the same records, so the butterfly form of the fused
+// result equals the butterfly quantizer applied to the written x bit for bit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,52 +43,10 @@
 namespace kq {
 namespace {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kAuxNTa = 2;   // nontemporal: the second pass reads h for the last time
 constexpr int kStatRows = 2;   // rows per wave of the statistics kernel
 constexpr int kStatChunks = 4; // 16-byte pieces per lane and row loaded at a time
 constexpr int kU = 4;        // row blocks per pipeline stage of the streaming pass
-
-// x = (h - mu) * (rstd * g) + t in double for 8 channels, rounded once to the
-// nearest bf16 (ties to even) and packed two per dword.  The double -> float
-// conversion rounds to nearest even and the hardware bf16 convert rounds the
-// float to nearest even; the two steps differ from one direct rounding only
-// when the float lands exactly on a bf16 midpoint (low 16 bits 0x8000) while
-// the double is not the float: then the sign of the exact remainder v - f
-// decides.  That case is rare and taken as a branch.
-__device__ __forceinline__ void adaln_bf16x8(const u32x4 &hv, double mu, double rstd, const double (&g)[8],
-                                             const double (&t)[8], unsigned (&xw)[4])
-{
-    double v[8];
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float hf = (e & 1) ? bf16hi(hv[e >> 1]) : bf16lo(hv[e >> 1]);
-        v[e] = __builtin_fma((double)hf - mu, rstd * g[e], t[e]);
-        f[e] = (float)v[e];
-    }
-    bool mid = false;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        mid |= (__float_as_uint(f[e]) & 0xFFFFu) == 0x8000u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        xw[i] = (unsigned)__builtin_bit_cast(unsigned short, (__bf16)f[2 * i]) |
-                ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)f[2 * i + 1]) << 16);
-    if (mid) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const unsigned b = __float_as_uint(f[e]);
-            const double r = v[e] - (double)f[e];
-            if ((b & 0xFFFFu) == 0x8000u && r != 0.0) {
-                const unsigned x16 = ((r > 0.0) == (f[e] > 0.0)) ? (b + 0x8000u) >> 16 : b >> 16;
-                const int sh = 16 * (e & 1);
-                xw[e >> 1] = (xw[e >> 1] & ~(0xFFFFu << sh)) | (x16 << sh);
-            }
-        }
-    }
-}
 
 __device__ __forceinline__ double wave_sum(double v)
 {
@@ -155,22 +119,6 @@ __global__ __launch_bounds__(256) void adaln_stats_kernel(const uint16_t *__rest
 // Second pass: normalise, modulate, round to bf16, then transform + MXFP4 or
 // write x.
 // ---------------------------------------------------------------------------
-struct Modulation {
-    double g[8], t[8]; // 1 + scale and shift of the lane's channels for the current sample
-    int64_t next;      // first row of the next sample
-};
-
-__device__ __forceinline__ void load_modulation(Modulation &md, const float *__restrict__ shift,
-                                                const float *__restrict__ scale, int64_t b, int64_t T, int d, int octc)
-{
-    md.next = (b + 1) * T;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        md.g[e] = 1.0 + (double)scale[b * d + octc * 8 + e];
-        md.t[e] = (double)shift[b * d + octc * 8 + e];
-    }
-}
-
 struct HRows {
     u32x4 v[kU];
 };
@@ -338,6 +286,8 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
     hipError_t e = hipLaunchKernel((const void *)adaln_stats_kernel, dim3((unsigned)grid1), dim3(256), args1, 0, stream);
     if (e != hipSuccess)
         return e;
+    if (x == nullptr && tuning().adaln_pass != 2)
+        return launch_adaln_mfma(h, M, d, stats, shift, scale, T, factors, nT, q, s, stream);
     int per_block = nT > 1 ? 1 : 0;
     const double *cst = stats;
     int rb = Rb, wbn = Wb, kit = kIt;

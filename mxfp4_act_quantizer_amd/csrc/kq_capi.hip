@@ -399,6 +399,8 @@ int kq_set_tuning(int key, int value)
     case 5: kq::tuning().mfma_order = value; return KQ_OK;
     case 6: kq::tuning().adaln_blocks_per_wave = value; return KQ_OK;
     case 7: kq::tuning().gemm_variant = value; return KQ_OK;
+    case 8: kq::tuning().adaln_pass = value; return KQ_OK;
+    case 9: kq::tuning().adaln_strip = value; return KQ_OK;
     default: return KQ_ERR_ARG;
     }
 }

@@ -1,7 +1,7 @@
 // Device helpers shared by the quantizer kernels (kq_kernels.hip) and the
 // AdaLN front-end (kq_adaln.hip): the MX encoding step, DPP exchanges inside
-// a quad of lanes, buffer descriptors, and the butterfly form of the
-// Kronecker transform.
+// a quad of lanes, buffer descriptors, the butterfly form of the Kronecker
+// transform, and the AdaLN normalisation of eight channels.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -197,6 +197,78 @@ __device__ __forceinline__ unsigned mx_encode_pair(const float (&v)[8], unsigned
     if (b == 0xFFu)
         w = 0u;
     return w;
+}
+
+// ---------------------------------------------------------------------------
+// AdaLN normalisation (LayerNorm without affine, then the per-sample
+// modulation of the adaptive-norm block) of eight consecutive channels.
+// ---------------------------------------------------------------------------
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// c + a b in double into a fresh register (the accumulating form of the
+// instruction would first copy the addend, which stays live across rows)
+__device__ __forceinline__ double fma_f64(double a, double b, double c)
+{
+    double r;
+    asm("v_fma_f64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// x = (h - mu) * (rstd * g) + t in double for 8 channels, rounded once to the
+// nearest bf16 (ties to even) and packed two per dword.  The double -> float
+// conversion rounds to nearest even and the hardware bf16 convert rounds the
+// float to nearest even; the two steps differ from one direct rounding only
+// when the float lands exactly on a bf16 midpoint (low 16 bits 0x8000) while
+// the double is not the float: then the sign of the exact remainder v - f
+// decides.  That case is rare; the wave takes the fix-up path when any of its
+// lanes has one.
+__device__ __forceinline__ void adaln_bf16x8(const u32x4 &hv, double mu, double rstd, const double (&g)[8],
+                                             const double (&t)[8], unsigned (&xw)[4])
+{
+    double v[8];
+    float f[8];
+    uint64_t tie = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float hf = (e & 1) ? bf16hi(hv[e >> 1]) : bf16lo(hv[e >> 1]);
+        v[e] = fma_f64((double)hf - mu, rstd * g[e], t[e]);
+        f[e] = (float)v[e];
+        tie |= __builtin_amdgcn_ballot_w64((__float_as_uint(f[e]) & 0xFFFFu) == 0x8000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xw[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){f[2 * i], f[2 * i + 1]}, bf16x2));
+    if (tie) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const unsigned b = __float_as_uint(f[e]);
+            const double r = v[e] - (double)f[e];
+            if ((b & 0xFFFFu) == 0x8000u && r != 0.0) {
+                const unsigned x16 = ((r > 0.0) == (f[e] > 0.0)) ? (b + 0x8000u) >> 16 : b >> 16;
+                const int sh = 16 * (e & 1);
+                xw[e >> 1] = (xw[e >> 1] & ~(0xFFFFu << sh)) | (x16 << sh);
+            }
+        }
+    }
+}
+
+struct Modulation {
+    double g[8], t[8]; // 1 + scale and shift of the lane's channels for the current sample
+    int64_t next;      // first row of the next sample
+};
+
+__device__ __forceinline__ void load_modulation(Modulation &md, const float *__restrict__ shift,
+                                                const float *__restrict__ scale, int64_t b, int64_t T, int d, int octc)
+{
+    md.next = (b + 1) * T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        md.g[e] = 1.0 + (double)scale[b * d + octc * 8 + e];
+        md.t[e] = (double)shift[b * d + octc * 8 + e];
+    }
 }
 
 } // namespace kq

@@ -16,6 +16,8 @@ struct Tuning {
     int mfma_order;           // 0 = automatic, 1 = XCD-grouped workgroups, 2 = flat order
     int adaln_blocks_per_wave;    // 0 = automatic: row blocks per wave of the AdaLN front-end's second pass
     int gemm_variant;         // 0 = automatic, 1 = per-tile kernel, 2 / 3 = persistent, k chunks of 256 / 128
+    int adaln_pass;           // 0 = automatic, 1 = matrix-core second pass, 2 = butterfly second pass
+    int adaln_strip;          // 0 = automatic, 4 or 8 blocks per workgroup of the matrix-core second pass
 };
 Tuning &tuning();
 
@@ -37,11 +39,18 @@ hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const
                           int64_t N, int64_t K, void *out, int bf16, hipStream_t stream);
 // AdaLN front-end: row statistics (mean, 1/sqrt(var + eps), fp64) into the
 // workspace stats [M, 2], then x = LayerNorm(h) (1 + scale[m / T]) +
-// shift[m / T] rounded to bf16 and either (x null) the butterfly transform and
-// MXFP4 into q, s, or (x given) x written out.  Two launches on `stream`.
+// shift[m / T] rounded to bf16 and either (x null) the transform and MXFP4
+// into q, s (the matrix-core second pass, or the butterfly one when the
+// tuning selects it), or (x given) x written out.  Two launches on `stream`.
 hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
                         float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
                         uint16_t *x, hipStream_t stream);
+// Second pass of the AdaLN front-end on the matrix cores: h normalised with
+// the statistics workspace and modulated while it is staged, then the MFMA
+// transform and MXFP4 into q, s.  One launch on `stream`.
+hipError_t launch_adaln_mfma(const uint16_t *h, int64_t M, int64_t d, const double *stats, const float *shift,
+                             const float *scale, int64_t T, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
+                             hipStream_t stream);
 // normalised Walsh-Hadamard-32 comparison: quantize (y null) or export y
 hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream);
 

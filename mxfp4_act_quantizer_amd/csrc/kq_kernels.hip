@@ -43,7 +43,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 Tuning &tuning()
 {
-    static Tuning t{0, 0, 0, 0, 0, 0, 0, 0};
+    static Tuning t{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     return t;
 }
 
@@ -288,12 +288,33 @@ __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool 
 #endif
 constexpr int kRing = KQ_RING; // tiles in flight per wave: kRing - 1 ahead of the one being staged
 
-template <bool kQuant, int kW>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) void kq_mfma_kernel(
+// With kAd the kernel is the second pass of the AdaLN front-end: x holds h,
+// and each lane normalises and modulates its two 16-byte pieces of a tile in
+// registers (adaln_bf16x8, the same arithmetic as the front-end's own
+// streaming pass) before they are staged, so the transform sees the bf16 x
+// that adaln_modulate would write.  The row statistics come from the
+// workspace the statistics kernel filled; a lane's record loads ride in the
+// ring with the tile's loads.
+struct AdArgs {
+    const double *stats;       // [M, 2]: mean, 1/sqrt(var + eps)
+    const float *shift, *scale; // [ceil(M / T), d]
+    int64_t T;                 // tokens per sample
+};
+#ifndef KQ_AD_OCC
+#define KQ_AD_OCC 2
+#endif
+#ifndef KQ_AD_RING
+#define KQ_AD_RING 4
+#endif
+
+template <bool kQuant, int kW, bool kAd = false>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? KQ_AD_OCC : 4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
-    int order, int lu)
+    int order, int lu, AdArgs ad)
 {
+    // tiles in flight per wave: the AdaLN form holds twice the registers per lane
+    constexpr int R = kAd ? KQ_AD_RING : kRing;
     __shared__ WgStage<kW> st;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -333,9 +354,46 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
     // loads are empty)
     auto trow = [&](int k) -> int64_t { return (tile0 + (int64_t)(k < n ? k : n - 1) * stride) * kTileT; };
 
-    // register ring of kRing tiles: tile k lives in ring[k % kRing] from its
-    // load (kRing - 1 steps ahead) until it is staged in LDS
-    XIn ring[kRing];
+    // register ring of R tiles: tile k lives in ring[k % R] from its
+    // load (R - 1 steps ahead) until it is staged in LDS
+    XIn ring[R];
+    // kAd: statistics records, lane l holding the one of its row for load
+    // k = l & 1 (its partner l ^ 1 holds the other)
+    u32x4 sring[kAd ? R : 1];
+    using S = Strip<kW>;
+    auto load_stat = [&](u32x4 &rec, int kk) {
+        const int64_t m = trow(kk) + S::kRowsPerWave * wave + S::kRowsPerLoad * (lane & 1) + lane / S::kLanesPerRow;
+        rec = *(const u32x4 *)(ad.stats + 2 * (m < M ? m : M - 1));
+    };
+    Modulation md;
+    int oct = 0; // kAd: the lane's octet (8 channels) of the row; blocks past the row end use the last one
+    if constexpr (kAd) {
+        const int chunk = lane % S::kLanesPerRow;
+        const int blk = bg * kW + (chunk >> 2);
+        oct = (blk < nB ? blk : nB - 1) * 4 + (chunk & 3);
+        const int64_t m = trow(0) + S::kRowsPerWave * wave + lane / S::kLanesPerRow;
+        load_modulation(md, ad.shift, ad.scale, (m < M ? m : M - 1) / ad.T, ad.T, d, oct);
+    }
+    // normalise the two pieces of step kk in place (rows past M: any finite
+    // stand-in, never stored)
+    auto normalize = [&](XIn &in, const u32x4 &rec, int kk) {
+        u32x4 oth;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            oth[i] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)rec[i], 0xB1, 0xF, 0xF, false);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const u32x4 r = (lane & 1) == k ? rec : oth;
+            const double mu = __builtin_bit_cast(double, ((uint64_t)r[1] << 32) | r[0]);
+            const double rstd = __builtin_bit_cast(double, ((uint64_t)r[3] << 32) | r[2]);
+            const int64_t m = trow(kk) + S::kRowsPerWave * wave + S::kRowsPerLoad * k + lane / S::kLanesPerRow;
+            if (m >= md.next)
+                load_modulation(md, ad.shift, ad.scale, (m < M ? m : M - 1) / ad.T, ad.T, d, oct);
+            unsigned xw[4];
+            adaln_bf16x8(in.v[k], mu, rstd, md.g, md.t, xw);
+            in.v[k] = u32x4{xw[0], xw[1], xw[2], xw[3]};
+        }
+    };
     // output ranges of one tile's rows
     auto store_prev = [&](int kp) {
         const int64_t r0 = trow(kp < 0 ? 0 : kp);
@@ -349,7 +407,9 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
     // the loop stay exact rather than falling back to the prologue's shorter
     // sequence.
 #pragma unroll
-    for (int k = 0; k < kRing - 1; ++k) {
+    for (int k = 0; k < R - 1; ++k) {
+        if constexpr (kAd)
+            load_stat(sring[k], k);
         load_x<kW>(ring[k], x, M, d, bg, nB, trow(k), k < n, wave, lane);
         if (kQuant)
             store_prev(-1);
@@ -358,8 +418,12 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
     bf16x8 A[3][2];
     build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * (lu ? 15 : 20), lu, lane);
 
-    auto step = [&](const XIn &cur, XIn &ld, int kk) {
-        load_x<kW>(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
+    auto step = [&](XIn &cur, XIn &ld, const u32x4 &rcur, u32x4 &rld, int kk) {
+        if constexpr (kAd)
+            load_stat(rld, kk + R - 1);
+        load_x<kW>(ld, x, M, d, bg, nB, trow(kk + R - 1), kk + R - 1 < n, wave, lane);
+        if constexpr (kAd)
+            normalize(cur, rcur, kk);
         stage_x(st, kk & 1, cur, wave, lane);
         __syncthreads();
         if (kQuant)
@@ -368,16 +432,17 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(4))) vo
     };
 
     int it = 0;
-    for (; it + kRing - 1 < n; it += kRing) {
+    for (; it + R - 1 < n; it += R) {
 #pragma unroll
-        for (int k = 0; k < kRing; ++k)
-            step(ring[k], ring[(k + kRing - 1) % kRing], it + k);
+        for (int k = 0; k < R; ++k)
+            step(ring[k], ring[(k + R - 1) % R], sring[kAd ? k : 0], sring[kAd ? (k + R - 1) % R : 0],
+                 it + k);
     }
-    // fewer than kRing tiles left, already in ring[0 ..]; their look-ahead loads are empty
+    // fewer than R tiles left, already in ring[0 ..]; their look-ahead loads are empty
 #pragma unroll
-    for (int k = 0; k < kRing - 1; ++k)
+    for (int k = 0; k < R - 1; ++k)
         if (it + k < n)
-            step(ring[k], ring[kRing - 1], it + k);
+            step(ring[k], ring[R - 1], sring[kAd ? k : 0], sring[kAd ? R - 1 : 0], it + k);
     if (kQuant) {
         __syncthreads();
         store_prev(n - 1);
@@ -618,14 +683,18 @@ static int mfma_wgs_per_xcd(const void *fn, int threads)
     return v;
 }
 
-template <int kW>
+template <int kW, bool kAd = false>
 static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                                   uint8_t *q, uint8_t *s, float *y, int lu, hipStream_t stream)
+                                   uint8_t *q, uint8_t *s, float *y, int lu, hipStream_t stream, AdArgs ad = {})
 {
     const int nB = (int)(d / 32);
     const int nBG = (nB + kW - 1) / kW;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const void *fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW>;
+    const void *fn;
+    if constexpr (kAd)
+        fn = (const void *)kq_mfma_kernel<true, kW, true>;
+    else
+        fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW>;
     const int64_t resident = mfma_wgs_per_xcd(fn, 64 * kW); // per XCD
     int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
     int interleave = tuning().mfma_interleave == 2 ? 1 : 0;
@@ -697,7 +766,8 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
     int nbg = nBG;
     int order = (interleave ? 1 : 0) | (flat ? 2 : 0);
     void *args_q[] = {(void *)&x,   (void *)&M,   (void *)&di,  (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s,   (void *)&y,   (void *)&nbg, (void *)&tpw,     (void *)&order,     (void *)&lu};
+                      (void *)&s,   (void *)&y,   (void *)&nbg, (void *)&tpw,     (void *)&order,     (void *)&lu,
+                      (void *)&ad};
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kW), args_q, 0, stream);
 }
 
@@ -729,6 +799,28 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
     if (w == 16)
         return launch_kq_mfma_w<16>(x, M, d, factors, nT, q, s, y, lu, stream);
     return launch_kq_mfma_w<8>(x, M, d, factors, nT, q, s, y, lu, stream);
+}
+
+// Second pass of the AdaLN front-end on the matrix cores: the quantizer's
+// launch shape with h in place of x, normalised at staging.
+hipError_t launch_adaln_mfma(const uint16_t *h, int64_t M, int64_t d, const double *stats, const float *shift,
+                             const float *scale, int64_t T, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
+                             hipStream_t stream)
+{
+    // The normalisation takes the registers of a lane to about 180 VGPRs (two
+    // waves per SIMD), so 16-block strips (1024 threads, at most 128 VGPRs)
+    // are not offered.  Strips of 4 blocks when they divide the row and
+    // strips of 8 do not (measured at 8192 x 1152: 18.95 against 19.83 us for
+    // the whole front-end; strips of 8 were as fast or faster at 2048 x 2240
+    // and 4608 x 3072).
+    const AdArgs ad{stats, shift, scale, T};
+    const int64_t nB = d / 32;
+    int w = tuning().adaln_strip;
+    if (w != 4 && w != 8)
+        w = (nB % 4 == 0 && nB % 8 != 0) ? 4 : 8;
+    if (w == 4)
+        return launch_kq_mfma_w<4, true>(h, M, d, factors, nT, q, s, nullptr, 0, stream, ad);
+    return launch_kq_mfma_w<8, true>(h, M, d, factors, nT, q, s, nullptr, 0, stream, ad);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,

@@ -354,12 +354,12 @@ def test_kq16_validation():
 
 
 def test_tuning_keys():
-    # the launch-shape knobs: keys 0..7 are accepted (and reset to automatic),
+    # the launch-shape knobs: keys 0..9 are accepted (and reset to automatic),
     # anything else is refused; no HIP call is made
     L = K.lib()
-    for key in range(8):
+    for key in range(10):
         assert L.kq_set_tuning(key, 0) == K.KQ_OK
-    for key in (-1, 8, 100):
+    for key in (-1, 10, 100):
         assert L.kq_set_tuning(key, 0) == K.KQ_ERR_ARG
     with pytest.raises(K.KQError):
-        K.set_tuning(8, 1)
+        K.set_tuning(10, 1)

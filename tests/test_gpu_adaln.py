@@ -8,9 +8,10 @@ Bars:
   - kq_adaln_quantize's codes and scales equal the oracle's MXFP4 of the
     transform of that x under tests/parity.py's rules, with every block that
     holds a flagged x element flagged as well;
-  - kq_adaln_quantize equals kq_quantize_ex(adaln_modulate(h), BUTTERFLY) bit
-    for bit (the fused kernel computes what the unfused pipeline stores and
-    reads back).
+  - kq_adaln_quantize equals kq_quantize(adaln_modulate(h)) bit for bit (the
+    fused kernels compute what the unfused pipeline stores and reads back);
+    with the butterfly second pass selected it equals
+    kq_quantize_ex(adaln_modulate(h), BUTTERFLY) bit for bit.
 Every case prints its name, shape and seed before it touches the GPU.
 """
 import sys
@@ -71,7 +72,7 @@ def run_gpu(K, h, shift, scale, T, f):
     hd, sh, sc, fd = dev_bf16(h), dev_f32(shift), dev_f32(scale), dev_f32(f)
     q, s = K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd)
     x = K.adaln_modulate(hd, sh, sc, T, EPS)
-    q2, s2 = K.kq_quantize(x, fd, variant=K.KQ_VARIANT_BUTTERFLY)
+    q2, s2 = K.kq_quantize(x, fd)
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy(), bits(x), q2.cpu().numpy(), s2.cpu().numpy()
 
@@ -137,6 +138,41 @@ def test_adaln_special_rows(K):
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
     # the constant row: x = shift of its sample, exactly representable or rounded
     assert np.array_equal(xg[0], xb[0])
+
+
+# launch knobs of kq_adaln_quantize: 8 selects the second pass (1 matrix
+# cores, 2 butterfly), 9 the matrix-core strip width (4 or 8 blocks)
+PASS_FORMS = [("mfma_strip4", {8: 1, 9: 4}, None), ("mfma_strip8", {8: 1, 9: 8}, None),
+              ("butterfly", {8: 2}, "KQ_VARIANT_BUTTERFLY")]
+FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300, 96, 1), (4100, 3072, 2048)]
+
+
+@pytest.mark.parametrize("form,knobs,variant", PASS_FORMS, ids=[p[0] for p in PASS_FORMS])
+def test_adaln_second_pass_forms(K, form, knobs, variant):
+    # every second-pass form equals the unfused pipeline through the matching
+    # quantizer bit for bit, on ragged rows, sample boundaries inside tiles and
+    # several widths; the knobs are reset afterwards
+    try:
+        for key, val in knobs.items():
+            K.set_tuning(key, val)
+        for M, d, T in FORM_CASES:
+            seed = 8400 + M + d
+            say(f"[adaln form {form}] M={M} d={d} T={T} seed={seed}")
+            h = I.act_dit_lognormal(M, d, seed)[0]
+            shift, scale = I.adaln_modulation((M + T - 1) // T, d, seed + 1)
+            hd, sh, sc = dev_bf16(h), dev_f32(shift), dev_f32(scale)
+            fd = dev_f32(I.random_factors(d // 32, seed + 2))
+            q, s = K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd)
+            x = K.adaln_modulate(hd, sh, sc, T, EPS)
+            if variant is None:
+                q2, s2 = K.kq_quantize(x, fd)
+            else:
+                q2, s2 = K.kq_quantize(x, fd, variant=getattr(K, variant))
+            torch.cuda.synchronize()
+            assert torch.equal(q, q2) and torch.equal(s, s2), f"{form} {M}x{d}: fused != unfused"
+    finally:
+        for key in knobs:
+            K.set_tuning(key, 0)
 
 
 def test_adaln_stats_workspace(K):
