@@ -300,21 +300,16 @@ struct AdArgs {
     const float *shift, *scale; // [ceil(M / T), d]
     int64_t T;                 // tokens per sample
 };
-#ifndef KQ_AD_OCC
-#define KQ_AD_OCC 2
-#endif
-#ifndef KQ_AD_RING
-#define KQ_AD_RING 4
-#endif
+// The AdaLN form needs about 180 VGPRs: two waves per SIMD (at three the
+// compiler spills, and that measured no faster).
+constexpr int kAdOcc = 2;
 
 template <bool kQuant, int kW, bool kAd = false>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? KQ_AD_OCC : 4))) void kq_mfma_kernel(
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? kAdOcc : 4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
     int order, int lu, AdArgs ad)
 {
-    // tiles in flight per wave: the AdaLN form holds twice the registers per lane
-    constexpr int R = kAd ? KQ_AD_RING : kRing;
     __shared__ WgStage<kW> st;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -354,12 +349,12 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? K
     // loads are empty)
     auto trow = [&](int k) -> int64_t { return (tile0 + (int64_t)(k < n ? k : n - 1) * stride) * kTileT; };
 
-    // register ring of R tiles: tile k lives in ring[k % R] from its
-    // load (R - 1 steps ahead) until it is staged in LDS
-    XIn ring[R];
+    // register ring of kRing tiles: tile k lives in ring[k % kRing] from its
+    // load (kRing - 1 steps ahead) until it is staged in LDS
+    XIn ring[kRing];
     // kAd: statistics records, lane l holding the one of its row for load
     // k = l & 1 (its partner l ^ 1 holds the other)
-    u32x4 sring[kAd ? R : 1];
+    u32x4 sring[kAd ? kRing : 1];
     using S = Strip<kW>;
     auto load_stat = [&](u32x4 &rec, int kk) {
         const int64_t m = trow(kk) + S::kRowsPerWave * wave + S::kRowsPerLoad * (lane & 1) + lane / S::kLanesPerRow;
@@ -407,7 +402,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? K
     // the loop stay exact rather than falling back to the prologue's shorter
     // sequence.
 #pragma unroll
-    for (int k = 0; k < R - 1; ++k) {
+    for (int k = 0; k < kRing - 1; ++k) {
         if constexpr (kAd)
             load_stat(sring[k], k);
         load_x<kW>(ring[k], x, M, d, bg, nB, trow(k), k < n, wave, lane);
@@ -420,8 +415,8 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? K
 
     auto step = [&](XIn &cur, XIn &ld, const u32x4 &rcur, u32x4 &rld, int kk) {
         if constexpr (kAd)
-            load_stat(rld, kk + R - 1);
-        load_x<kW>(ld, x, M, d, bg, nB, trow(kk + R - 1), kk + R - 1 < n, wave, lane);
+            load_stat(rld, kk + kRing - 1);
+        load_x<kW>(ld, x, M, d, bg, nB, trow(kk + kRing - 1), kk + kRing - 1 < n, wave, lane);
         if constexpr (kAd)
             normalize(cur, rcur, kk);
         stage_x(st, kk & 1, cur, wave, lane);
@@ -432,17 +427,17 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? K
     };
 
     int it = 0;
-    for (; it + R - 1 < n; it += R) {
+    for (; it + kRing - 1 < n; it += kRing) {
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-            step(ring[k], ring[(k + R - 1) % R], sring[kAd ? k : 0], sring[kAd ? (k + R - 1) % R : 0],
+        for (int k = 0; k < kRing; ++k)
+            step(ring[k], ring[(k + kRing - 1) % kRing], sring[kAd ? k : 0], sring[kAd ? (k + kRing - 1) % kRing : 0],
                  it + k);
     }
-    // fewer than R tiles left, already in ring[0 ..]; their look-ahead loads are empty
+    // fewer than kRing tiles left, already in ring[0 ..]; their look-ahead loads are empty
 #pragma unroll
-    for (int k = 0; k < R - 1; ++k)
+    for (int k = 0; k < kRing - 1; ++k)
         if (it + k < n)
-            step(ring[k], ring[R - 1], sring[kAd ? k : 0], sring[kAd ? R - 1 : 0], it + k);
+            step(ring[k], ring[kRing - 1], sring[kAd ? k : 0], sring[kAd ? kRing - 1 : 0], it + k);
     if (kQuant) {
         __syncthreads();
         store_prev(n - 1);
