@@ -17,7 +17,7 @@
 //     the x that adaln_modulate writes, bit for bit;
 //   - adaln_stream_kernel below, which also writes x for adaln_modulate.
 // Streaming kernels of this file, no barriers:
-//   adaln_stats_kernel   one wave per run of rows: per row, the sum and the
+//   adaln_stats_kernel   one wave per row: the sum and the
 //                        sum of squares of h in fp64 (lane-strided over the
 //                        row, then a wave reduction), mean and
 //                        1/sqrt(var + eps) in fp64 into a 16-byte record.
