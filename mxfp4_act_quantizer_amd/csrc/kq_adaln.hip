@@ -182,7 +182,7 @@ __device__ __forceinline__ void adaln_stage(const HRows &in, int64_t rb0, int ro
             unsigned b;
             const unsigned w = mx_encode_quad(v, b);
             const unsigned drop_s = (unsigned)(qp != 0) << 31;
-            __builtin_amdgcn_raw_buffer_store_b32(w, rq, mr * (d >> 1) + oct * 4, 0, kAuxNTa); // codes nontemporal
+            __builtin_amdgcn_raw_buffer_store_b32(w, rq, mr * (d >> 1) + oct * 4, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)((unsigned)(mr * nB + (oct >> 2)) | drop_s), 0,
                                                  0);
         } else {

@@ -250,13 +250,11 @@ __device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<k
 // workgroup (kW consecutive bytes per token).  rq and rs cover the tile's own
 // rows, so rows past M fall outside them; blocks past the row end, the spare
 // scale lanes, and every lane when `valid` is false set bit 31 of their
-// offsets, which the range check drops.  The code stores are nontemporal
-// (the codes are read by the next kernel, not by this one); the scale bytes
-// keep the default policy, so that a row's short pieces from the strips of a
-// token group merge in the XCD's L2 before they reach HBM.  Measured against
-// the default policy for both: 7.76 against 8.2 us at 8192 x 1152 and 19.1
-// against 19.9 at 8192 x 4608; nontemporal scale stores as well gave 8.1 and
-// 19.4 and wrote 9% more bytes to HBM at 8192 x 4608.
+// offsets, which the range check drops.  Both stores keep the default cache
+// policy, so that the codes are still in the caches when the W4A4 product
+// reads them right after: nontemporal code stores made the quantizer alone
+// 3-6% faster but quantize-then-product at the DiT qkv shape (8192 x 1152 by
+// 3456) 8% slower (41.7 against 38.4 us).
 template <int kW>
 __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool valid, int bg, int nB, int d, int wave,
                                            int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
@@ -268,7 +266,7 @@ __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool 
     const unsigned drop_q = (unsigned)(bg * kW + (c8 >> 1) >= nB || !valid) << 31;
     const u32x2 v = *(const u32x2 *)&st.q[par][tq][c8 * 8];
     __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * kW * 16 + c8 * 8) | drop_q), 0,
-                                          kAuxNT);
+                                          0);
     const int f = wave * 64 + lane; // flat lane of the workgroup
     const int ts = (f / kW) % kTileT;
     const int cs = f % kW;
@@ -568,9 +566,7 @@ __device__ __forceinline__ void process_rows(const RowsIn<kMode> &in, int64_t m,
             const int mr = (int)(mm - m0);
             const unsigned drop_q = (unsigned)(cok ? 0 : 1) << 31;
             const unsigned drop_s = drop_q | ((unsigned)((qp & (k16 ? 1 : 3)) != 0) << 31);
-            // codes nontemporal, as in the MFMA kernel's store_tile (measured 1-2% faster for
-            // SmoothQuant, 4% for the butterfly and Walsh-Hadamard forms)
-            __builtin_amdgcn_raw_buffer_store_b32(w, rq, (int)((unsigned)(mr * (d >> 1) + oct * 4) | drop_q), 0, kAuxNT);
+            __builtin_amdgcn_raw_buffer_store_b32(w, rq, (int)((unsigned)(mr * (d >> 1) + oct * 4) | drop_q), 0, 0);
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs,
                                                  (int)((unsigned)(mr * nB + (oct >> (k16 ? 1 : 2))) | drop_s), 0, 0);
         }
