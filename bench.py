@@ -341,7 +341,8 @@ def gemm_bench(args):
     rotating operand sets, timed with HIP events.  Roofline per shape:
     max(2MNK / FP4 peak, bytes / HBM peak) with bytes = A, B codes and scales
     plus the bf16 output.  The per-tile kernel (the fallback for shapes the
-    persistent kernel does not take) is timed on the same operands beside it."""
+    persistent kernel does not take) is timed on the same operands beside it, and
+    so is the quantizer of the activation followed by the product."""
     import torch
 
     import mxfp4_act_quantizer_amd as K
@@ -360,8 +361,8 @@ def gemm_bench(args):
             qa, sa = K.kq_quantize(x, f)
             w = torch.randn(N, Kd, generator=gen, device=dev) / math.sqrt(Kd)
             qb, sb = K.mx_quantize_f32(w)
-            sets.append((qa, sa, qb, sb, torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
-            del x, w
+            sets.append((qa, sa, qb, sb, torch.empty((M, N), dtype=torch.bfloat16, device=dev), x))
+            del w
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
@@ -391,6 +392,11 @@ def gemm_bench(args):
                                                     stream=torch.cuda.current_stream()), nsets, args.steps) * 1e6
         finally:
             K.set_tuning(7, 0)
+        # the activation quantizer followed by the product, as a layer runs them
+        us_pipe = _time_leg(lambda i: (K.kq_quantize(sets[i][5], f, sets[i][0], sets[i][1],
+                                                     stream=torch.cuda.current_stream()),
+                                       K.mx_gemm(*sets[i][:4], out=sets[i][4], stream=torch.cuda.current_stream())),
+                            nsets, args.steps) * 1e6
         flops = 2.0 * M * N * Kd
         t_mfma = flops / (FP4_PEAK_TFLOPS * 1e12) * 1e6
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
@@ -398,7 +404,7 @@ def gemm_bench(args):
         row = {"layer": name, "M": M, "N": N, "K": Kd, "us": round(us, 2), "TFLOP/s": round(flops / us / 1e6, 1),
                "GB/s": round(nbytes / us / 1e3, 1), "bound": bound,
                "roofline_us": round(max(t_mfma, t_hbm), 2), "frac": round(max(t_mfma, t_hbm) / us, 4),
-               "per_tile_kernel_us": round(us_tile, 2)}
+               "per_tile_kernel_us": round(us_tile, 2), "quantize_then_product_us": round(us_pipe, 2)}
         rows.append(row)
         print(json.dumps(row), flush=True)
         del sets
