@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Throughput of the KroQuant online quantizer on one MI355X.
 
-One step = the quantizer pass over one CFG-doubled DiT batch: both activation
-matrices of the DiT configuration (M = 8192 tokens, d = 1152 with 36 factor
-sets and d = 4608 with 144 factor sets, bf16, synthetic: per-token lognormal
-rows, 1% outlier channels x50), each through kq_quantize (bf16 -> per-block
-Kronecker transform -> MXFP4 codes + E8M0 scales).
+One step = one kq_quantize pass over the largest single-GPU workload: the
+65536 x 12288 bf16 activation of the bandwidth sweep (N(0,1), 1% outlier
+channels x50, 0.1% each of all-zero, subnormal, near-min-normal and exact-tie
+blocks; synthetic, from synth/inputs.py), with the configured
+[[1,1],[1,-1]]/sqrt(2) factors (the normalised Walsh-Hadamard-32 block,
+shared by every block): bf16 -> Kronecker transform -> MXFP4 codes + E8M0
+scales.
 
-  value     = algorithmic bytes of the step / step time  (GB/s)
+  value     = algorithmic bytes of the K timed steps / their wall time (GB/s)
               algorithmic bytes = 2.53125 B per element (2 read, 0.5 + 1/32 written)
   roofline  = the quantizer kernel's average launch against the 8 TB/s HBM peak,
-              timed with HIP events around graphs of back-to-back launches
-  cpu_baseline = the CPU oracle on a bounded sample of the same workload
-
-Inputs and outputs rotate over enough buffer sets (>= 1 GB per cycle) that
-every launch reads from HBM rather than the 256 MB last-level cache.
+              timed with HIP events on the launch stream around the timed graph
+  comparison = in the same run and on the same input: 384 per-block factor sets,
+              the SmoothQuant kernel, the butterfly variant, the K2 (LU) form,
+              the Walsh-Hadamard-32 kernel and the 4:1 copy ceiling (every copy
+              form, the fastest reported); plus per-shape entries for the DiT
+              CFG batch (8192 x 1152, 8192 x 4608) and the double-stream
+              12288-wide input (4608 x 12288)
+  cpu_baseline = the CPU oracle on the first 4096 rows of the same input
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 
@@ -22,14 +27,16 @@ HBM traffic (the roofline's "traffic" field) comes from two rocprofv3 counter
 passes over `bench.py --traffic-run` (FETCH_SIZE, then WRITE_SIZE), which
 launches a plain bf16->fp32 copy of known size as the calibration kernel and
 then the quantizer steps eagerly; `bench.py --summarize-traffic FETCH_DIR
-WRITE_DIR` turns the two runs' counter CSVs into profiles/kq_mfma_dit_traffic.md,
-which this script reads back while the kernel source hash still matches.
+WRITE_DIR` turns the two runs' counter CSVs into the traffic profile under
+profiles/, which this script reads back while the kernel source hash still
+matches.
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -42,9 +49,11 @@ METRIC = "quantizer GB/s (bf16→MXFP4+E8M0) and % HBM peak, KroQuant vs SmoothQ
 HBM_PEAK_GBS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 ROTATE_BYTES = 1 << 30
-WORKLOAD = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608)]
-KERNEL_SYMBOL = "kq_mfma_kernel<true"  # both strip-width instances: <true, 8> and <true, 16>
+HEADLINE = ("sweep_65536", 65536, 12288)
+PER_SHAPE = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608), ("dbl_12288", 4608, 12288)]
+KERNEL_SYMBOL = "kq_mfma_kernel<true"
 RAMP_S = 0.3  # untimed replays before the warm-up steps, for the GPU clocks to leave their idle state
+CPU_ROWS = 4096  # rows of the headline input the CPU oracle is timed on
 
 
 def parse():
@@ -52,8 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 mfma, 2 butterfly")
-    ap.add_argument("--no-extras", action="store_true", help="skip the SmoothQuant / butterfly comparison legs")
+    ap.add_argument("--no-extras", action="store_true", help="skip the comparison legs and per-shape entries")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU-oracle baseline")
     ap.add_argument("--traffic-run", action="store_true",
@@ -78,7 +86,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kq_mfma_dit_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kq_mfma_sweep65536_traffic.md")
 # calibration copy of the counter runs: bf16 -> fp32, 2^27 elements
 CAL_ELEMS = 1 << 27
 CAL_READ, CAL_WRITE = 2 * CAL_ELEMS, 4 * CAL_ELEMS
@@ -101,7 +109,7 @@ def load_traffic(src_hash):
 
 
 def _read_counters(folder):
-    """(dispatch id, kernel name, counter, value) rows of a rocprofv3 --pmc csv run."""
+    """(dispatch id, kernel name, grid, counter, value) rows of a rocprofv3 --pmc csv run."""
     import csv
     import glob
     rows = []
@@ -116,19 +124,16 @@ def _read_counters(folder):
 
 
 def summarize_traffic(fetch_dir, write_dir):
-    """Counter runs -> calibrated HBM bytes per quantizer launch -> the traffic profile.
-
-    The traffic run launches the shapes of WORKLOAD in turn, so the n-th
-    quantizer dispatch of a run is shape n mod len(WORKLOAD)."""
+    """Counter runs -> calibrated HBM bytes per quantizer launch -> the traffic profile."""
     cal, kq = {}, {}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        n = 0
         for _, name, grid, cname, val in _read_counters(folder):
             if cname != counter:
                 continue
             if KERNEL_SYMBOL in name:
-                kq.setdefault((n % len(WORKLOAD), grid), {}).setdefault(counter, []).append(val * 1024.0)
-                n += 1
+                kq.setdefault(counter, []).append(val * 1024.0)
+                kq["grid"] = grid
+                kq["name"] = name
             elif "copy" in name and ("BFloat16" in name or "bfloat16" in name):
                 cal.setdefault((name, grid), {}).setdefault(counter, []).append(val * 1024.0)
     cal = [v for v in cal.values() if len(v.get("FETCH_SIZE", [])) >= CAL_REPEAT]
@@ -137,37 +142,29 @@ def summarize_traffic(fetch_dir, write_dir):
     cal = cal[0]
     f_fetch = CAL_READ / float(np.median(cal["FETCH_SIZE"]))
     f_write = CAL_WRITE / float(np.median(cal["WRITE_SIZE"]))
-    if sorted(k[0] for k in kq) != list(range(len(WORKLOAD))):
-        raise SystemExit(f"quantizer dispatches do not alternate over the {len(WORKLOAD)} shapes: {sorted(kq)}")
-    shapes = {}
-    tot = 0.0
-    for (k, grid), v in sorted(kq.items()):
-        name, M, d = WORKLOAD[k]
-        rd = float(np.mean(v["FETCH_SIZE"])) * f_fetch
-        wr = float(np.mean(v["WRITE_SIZE"])) * f_write
-        alg = M * d * BYTES_PER_ELEM
-        shapes[name] = {"grid": grid, "dispatches": len(v["FETCH_SIZE"]), "read_bytes": round(rd),
-                        "write_bytes": round(wr), "hbm_bytes": round(rd + wr), "algorithmic_bytes": round(alg),
-                        "ratio": round((rd + wr) / alg, 4)}
-        tot += rd + wr
-    blob = {"kernel": "kq_mfma_kernel<true, kW>", "kernel_source_hash": kernel_source_hash(),
-            "hbm_bytes_per_launch": round(tot / len(shapes)),
-            "algorithmic_bytes_per_launch": round(sum(M * d for _, M, d in WORKLOAD) * BYTES_PER_ELEM / len(WORKLOAD)),
+    name, M, d = HEADLINE
+    rd = float(np.mean(kq["FETCH_SIZE"])) * f_fetch
+    wr = float(np.mean(kq["WRITE_SIZE"])) * f_write
+    alg = M * d * BYTES_PER_ELEM
+    blob = {"kernel": kq["name"], "workload": f"{name} ({M} x {d})", "kernel_source_hash": kernel_source_hash(),
+            "grid": kq["grid"], "dispatches": len(kq["FETCH_SIZE"]),
+            "read_bytes": round(rd), "write_bytes": round(wr),
+            "hbm_bytes_per_launch": round(rd + wr), "algorithmic_bytes_per_launch": round(alg),
+            "ratio": round((rd + wr) / alg, 4),
             "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4),
             "calibration": {"kernel": "torch bf16->fp32 copy", "elements": CAL_ELEMS,
                             "read_bytes": CAL_READ, "write_bytes": CAL_WRITE,
                             "fetch_kib_median": float(np.median(cal["FETCH_SIZE"])) / 1024,
-                            "write_kib_median": float(np.median(cal["WRITE_SIZE"])) / 1024},
-            "per_shape": shapes}
+                            "write_kib_median": float(np.median(cal["WRITE_SIZE"])) / 1024}}
     lines = [
-        "# HBM traffic of the KroQuant quantizer kernel, DiT CFG workload (8192 tokens, d=1152 and d=4608)",
+        f"# HBM traffic of the KroQuant quantizer kernel, {M} x {d} bf16 (Hadamard factors, one shared set)",
         "",
         "Commands (from the repository root, on one MI355X; each counter pass is a run of its own):",
         "",
         "    timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
-        "python3 bench.py --traffic-run --steps 20",
+        "python3 bench.py --traffic-run --steps 10",
         "    timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
-        "python3 bench.py --traffic-run --steps 20",
+        "python3 bench.py --traffic-run --steps 10",
         "    python3 bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
         "",
         f"Calibration: a plain bf16->fp32 copy of {CAL_ELEMS} elements reads {CAL_READ} B and writes {CAL_WRITE} B; "
@@ -175,65 +172,118 @@ def summarize_traffic(fetch_dir, write_dir):
         f"{blob['calibration']['write_kib_median']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by "
         f"{f_fetch:.4f} and WRITE_SIZE by {f_write:.4f}.",
         "",
-        "| shape | grid | dispatches | HBM read B | HBM write B | algorithmic B | HBM / algorithmic |",
+        "| kernel | grid | dispatches | HBM read B | HBM write B | algorithmic B | HBM / algorithmic |",
         "|---|---|---|---|---|---|---|",
-    ]
-    for name, v in shapes.items():
-        lines.append(f"| {name} | {v['grid']} | {v['dispatches']} | {v['read_bytes']} | {v['write_bytes']} | "
-                     f"{v['algorithmic_bytes']} | {v['ratio']} |")
-    lines += ["", "Per launch (average of the two shapes, as the roofline's `achieved`): "
-              f"{blob['hbm_bytes_per_launch']} HBM bytes against {blob['algorithmic_bytes_per_launch']} algorithmic bytes.",
-              "", "```json", json.dumps(blob, indent=1), "```", ""]
+        f"| `{kq['name']}` | {kq['grid']} | {blob['dispatches']} | {blob['read_bytes']} | {blob['write_bytes']} | "
+        f"{blob['algorithmic_bytes_per_launch']} | {blob['ratio']} |",
+        "", "```json", json.dumps(blob, indent=1), "```", ""]
     with open(TRAFFIC_PROFILE, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
 
 
-def make_inputs():
-    from synth import inputs as I
-    mats = []
-    for name, M, d in WORKLOAD:
-        x = I.make_activation(name)
-        f = I.make_factors(name)
-        scale = I.smoothquant_scale(x)
-        assert x.shape == (M, d)
-        mats.append((name, x, f, scale))
-    return mats
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
-def cpu_baseline(mats, min_seconds=10.0):
-    """The oracle, as it stands, over the whole step (every row of both
-    matrices), spread over host threads by row ranges (ctypes releases the
-    GIL), repeated until at least min_seconds of wall time."""
+def cpu_baseline(x_rows, f, tiny, min_seconds=10.0):
+    """The oracle, as it stands (single-threaded C, untuned), over a bounded
+    sample of the headline input (its first rows), spread over host threads
+    by row ranges (ctypes releases the GIL), repeated until at least
+    min_seconds of wall time; plus a one-thread figure on the tiny
+    configuration (256 x 1152, one shared factor set)."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import oracle as O
     O.lib()
-    threads = max(1, min(16, os.cpu_count() or 1))
-    jobs = []
-    for _, x, f, _ in mats:
-        rows = x.shape[0]
-        chunk = max(1, (rows + 4 * threads - 1) // (4 * threads))
-        for r0 in range(0, rows, chunk):
-            jobs.append((np.ascontiguousarray(x[r0:r0 + chunk]), f))
+    host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, host_cores))  # the box's CPU share is 16 threads
+    rows = x_rows.shape[0]
+    chunk = max(1, (rows + 4 * threads - 1) // (4 * threads))
+    jobs = [np.ascontiguousarray(x_rows[r0:r0 + chunk]) for r0 in range(0, rows, chunk)]
     passes = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
         while True:
-            list(ex.map(lambda a: O.kq_quantize(a[0], a[1]), jobs))
+            list(ex.map(lambda a: O.kq_quantize(a, f), jobs))
             passes += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
     dt = time.perf_counter() - t0
-    elems = sum(x.size for _, x, _, _ in mats)
+    elems = x_rows.size
+    xt, ft = tiny
+    n1, t1 = 0, time.perf_counter()
+    while True:
+        O.kq_quantize(xt, ft)
+        n1 += 1
+        if time.perf_counter() - t1 >= 2.0:
+            break
+    dt1 = time.perf_counter() - t1
+    name, M, d = HEADLINE
     return {
         "value": round(passes * elems * BYTES_PER_ELEM / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"the full step (both DiT matrices, all 8192 rows, per-block factor sets) {passes} times, "
-                  f"{passes * elems} elements in {dt:.1f} s wall on {threads} threads; same byte formula as the GPU value",
+        "sample": f"the first {rows} of the {M} rows of the {name} input ({rows} x {d}, Hadamard factors), "
+                  f"{passes} passes, {passes * elems} elements in {dt:.1f} s wall on {threads} threads over row "
+                  f"ranges; same byte formula as the GPU value",
+        "rows_per_s": round(passes * rows / dt, 1),
+        "host_cores": host_cores,
+        "cpu_model": cpu_model(),
+        "one_thread_tiny": {"value": round(n1 * xt.size * BYTES_PER_ELEM / dt1 / 1e9, 4), "unit": "GB/s",
+                            "rows_per_s": round(n1 * xt.shape[0] / dt1, 1),
+                            "sample": f"tiny configuration {xt.shape[0]} x {xt.shape[1]}, one shared factor set, "
+                                      f"{n1} passes on 1 thread"},
     }
+
+
+def _time_leg(fn, nsets, steps):
+    """Average time of one call of fn(set index): a graph of `steps` calls over
+    the rotating sets, captured on a side stream, replayed after the clocks
+    are up, timed with HIP events on that stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        fn(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(steps):
+                fn(i % nsets)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:  # clocks up
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        e0.record(cs)
+        g.replay()
+        e1.record(cs)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def best_copy(K, src_of, dst_of, nsets, steps):
+    """Every 4:1 copy form on the given buffers; (best seconds per call, best
+    form, {form: seconds})."""
+    import torch
+    per = {}
+    for form in range(K.KQ_COPY_FORMS):
+        per[form] = _time_leg(lambda i, form=form: K.measure_copy41(src_of(i), dst_of(i), form=form,
+                                                                     stream=torch.cuda.current_stream()),
+                              nsets, steps)
+    best = min(per, key=per.get)
+    return per[best], best, per
 
 
 def all_configs(args):
@@ -281,7 +331,6 @@ def all_configs(args):
             "fwht": lambda b: K.fwht_quantize(b["x"], b["q"], b["s"], stream=cur()),
             "kq16_perblock": lambda b: K.kq_quantize16(b["x"], f16, b["q"], b["s16"], stream=cur()),
             "smoothquant": lambda b: K.sq_quantize(b["x"], scale, b["q"], b["s"], stream=cur()),
-            "copy41": lambda b: K.measure_copy41(b["x"], b["q"], stream=cur()),
         }
         row = {"config": name, "M": M, "d": d, "algorithmic_bytes": int(alg)}
         for leg, fn in legs.items():
@@ -306,9 +355,12 @@ def all_configs(args):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps
             # copy: 2 + 0.5 B per element; 16-element blocks: 2 + 0.5 + 1/16
-            nbytes = elems * 2.5 if leg == "copy41" else (elems * (2.5 + 1.0 / 16) if leg == "kq16_perblock" else alg)
+            nbytes = elems * (2.5 + 1.0 / 16) if leg == "kq16_perblock" else alg
             row[leg] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                         "hbm_pct": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "rows/s": round(M / us * 1e6, 1)}
+        cp, cp_form, _ = best_copy(K, lambda i: bufs[i]["x"], lambda i: bufs[i]["q"], nsets, args.steps)
+        row["copy41"] = {"us": round(cp * 1e6, 2), "GB/s": round(elems * 2.5 / cp / 1e9, 1),
+                         "hbm_pct": round(100 * elems * 2.5 / cp / 1e9 / HBM_PEAK_GBS, 1), "form": cp_form}
         row["kq_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_perblock"]["us"], 4)
         row["kq_over_copy41_speed"] = round(row["copy41"]["us"] / row["kq_mfma_perblock"]["us"], 4)
         row["k2_lu_over_fwht_speed"] = round(row["fwht"]["us"] / row["kq_lu_perblock"]["us"], 4)
@@ -386,12 +438,8 @@ def gemm_bench(args):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
         # the per-tile kernel on the same operands, for comparison
-        K.set_tuning(7, 1)
-        try:
-            us_tile = _time_leg(lambda i: K.mx_gemm(*sets[i][:4], out=sets[i][4],
-                                                    stream=torch.cuda.current_stream()), nsets, args.steps) * 1e6
-        finally:
-            K.set_tuning(7, 0)
+        us_tile = _time_leg(lambda i: K.mx_gemm(*sets[i][:4], out=sets[i][4], stream=torch.cuda.current_stream(),
+                                                tuning={"gemm_kernel": 1}), nsets, args.steps) * 1e6
         # the activation quantizer followed by the product, as a layer runs them
         us_pipe = _time_leg(lambda i: (K.kq_quantize(sets[i][5], f, sets[i][0], sets[i][1],
                                                      stream=torch.cuda.current_stream()),
@@ -414,34 +462,6 @@ def gemm_bench(args):
     print(json.dumps({"gemm_block_us": round(tot_us, 2), "roofline_us": round(tot_roof, 2),
                       "frac": round(tot_roof / tot_us, 4),
                       "per_tile_kernel_block_us": round(sum(r["per_tile_kernel_us"] for r in rows), 2)}), flush=True)
-
-
-def _time_leg(fn, nsets, steps):
-    """Average time of one call of fn(set index): a graph of `steps` calls over
-    the rotating sets, captured on a side stream, replayed after the clocks
-    are up, timed with HIP events on that stream."""
-    import torch
-    g = torch.cuda.CUDAGraph()
-    cs = torch.cuda.Stream()
-    cs.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cs):
-        fn(0)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=cs):
-            for i in range(steps):
-                fn(i % nsets)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.1:  # clocks up
-        g.replay()
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(cs):
-        e0.record(cs)
-        g.replay()
-        e1.record(cs)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / steps
 
 
 ADALN_WORKLOADS = ("dit_1152", "mid_2240", "dbl_3072")  # the hidden widths AdaLN normalises
@@ -517,18 +537,14 @@ def adaln_bench(args):
 
         def fused_with(knobs):
             def run(i):
-                for key, val in knobs.items():
-                    K.set_tuning(key, val)
-                try:
-                    fused(i)
-                finally:
-                    for key in knobs:
-                        K.set_tuning(key, 0)
+                b = sets[i]
+                K.kq_adaln_quantize(b["h"], shift, scale, T, ADALN_EPS, f, b["q"], b["s"], stats=b["w"],
+                                    stream=cur(), tuning=knobs)
             return run
 
         t = {"fused": _time_leg(fused, nsets, args.steps),
-             "fused_butterfly_pass": _time_leg(fused_with({8: 2}), nsets, args.steps),
-             "fused_mfma_strip4": _time_leg(fused_with({8: 1, 9: 4}), nsets, args.steps),
+             "fused_butterfly_pass": _time_leg(fused_with({"adaln_pass": 2}), nsets, args.steps),
+             "fused_mfma_strip4": _time_leg(fused_with({"adaln_pass": 1, "adaln_strip": 4}), nsets, args.steps),
              "torch_layernorm_then_kq_mfma": _time_leg(torch_unfused, nsets, args.steps),
              "unfused_mfma": _time_leg(unfused(1), nsets, args.steps),
              "unfused_butterfly": _time_leg(unfused(2), nsets, args.steps),
@@ -554,9 +570,11 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
+              f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
+        sys.exit(2)
     if args.all_configs or args.gemm or args.adaln:
-        if args.gpus != 1:
-            sys.exit(2)
         if args.all_configs:
             all_configs(args)
         elif args.gemm:
@@ -564,44 +582,33 @@ def main():
         else:
             adaln_bench(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
-              f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
-        sys.exit(2)
     import torch
 
     import mxfp4_act_quantizer_amd as K
+    from synth import inputs as I
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    mats = make_inputs()
-    from synth import inputs as I
+    cur = torch.cuda.current_stream
 
-    # ---- device buffers, rotated so one cycle touches >= 1 GB
-    step_bytes = sum(x.size * BYTES_PER_ELEM for _, x, _, _ in mats)
+    # ---- the headline input, generated on the host from the seeded recipe
+    name, M, d = HEADLINE
+    t_gen = time.perf_counter()
+    x_bits = I.act_sweep_special(M, d, I.data_seed(name))[0]
+    print(f"[bench] {name} {M} x {d} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    f_h = I.hadamard_factors(1)
+    step_bytes = M * d * BYTES_PER_ELEM
     nsets = max(2, int(np.ceil(ROTATE_BYTES / step_bytes)))
-    sets = []
-    for _ in range(nsets):
-        one = []
-        for name, x, f, scale in mats:
-            M, d = x.shape
-            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-            lu = I.random_lu(d // 32, I.factor_seed(name) + 77)
-            one.append(dict(x=xd, f=torch.from_numpy(f).to(dev), scale=torch.from_numpy(scale).to(dev),
-                            lu=torch.from_numpy(lu).to(dev),
-                            q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
-                            s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)))
-        sets.append(one)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    sets = [dict(x=x0 if k == 0 else x0.clone(), q=torch.empty((M, d // 2), dtype=torch.uint8, device=dev),
+                 s=torch.empty((M, d // 32), dtype=torch.uint8, device=dev)) for k in range(nsets)]
+    fh_d = torch.from_numpy(f_h).to(dev)
     torch.cuda.synchronize()
 
-    def step_kq(i, variant):
-        for b in sets[i % nsets]:
-            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=torch.cuda.current_stream(), variant=variant)
-
-    def step_sq(i):
-        for b in sets[i % nsets]:
-            K.sq_quantize(b["x"], b["scale"], b["q"], b["s"], stream=torch.cuda.current_stream())
+    def step(i):
+        b = sets[i % nsets]
+        K.kq_quantize(b["x"], fh_d, b["q"], b["s"], stream=cur())
 
     def capture(fn, count):
         """A HIP graph of `count` calls fn(0..count-1), captured on a side stream."""
@@ -615,28 +622,8 @@ def main():
                 for i in range(count):
                     fn(i)
         torch.cuda.synchronize()
-        return g
+        return g, cs
 
-    def timed_graph(g, replays=1):
-        """Replay a graph: wall and event time of the replays, bracketed by synchronisation."""
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(replays):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
-
-    def clock_ramp(g):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < RAMP_S:
-            g.replay()
-            torch.cuda.synchronize()
-        return round(time.perf_counter() - t0, 3)
-
-    variant = args.variant
     if args.traffic_run:
         src = torch.randn(CAL_ELEMS, device=dev).to(torch.bfloat16)
         dst = torch.empty(CAL_ELEMS, dtype=torch.float32, device=dev)
@@ -645,51 +632,45 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         for i in range(args.warmup + args.steps):
-            step_kq(i, variant)
+            step(i)
         torch.cuda.synchronize()
         print(f"traffic run: {CAL_REPEAT} calibration copies, {args.warmup + args.steps} quantizer steps", flush=True)
         return
-    # the timed region: exactly K steps, launched as one graph (the launches
-    # themselves would otherwise leave the GPU idle between short kernels)
-    g_warm = capture(lambda i: step_kq(i, variant), max(1, args.warmup))
-    g_main = capture(lambda i: step_kq(i, variant), args.steps)
-    # the GPU idles in a low-power state: untimed replays until its clocks
-    # have ramped (about RAMP_S seconds), then the W warm-up steps, then K
-    ramp_s = clock_ramp(g_warm)
-    timed_graph(g_warm)
-    wall, ev = timed_graph(g_main)
-    ms_per_step = wall * 1e3 / args.steps
-    value = step_bytes / (wall / args.steps) / 1e9
 
-    # roofline of the quantizer kernel: per shape, a graph of back-to-back
-    # launches over the rotating buffers, timed with events on its stream
-    LAUNCHES = 40
-    launch_bytes = [x.size * BYTES_PER_ELEM for _, x, _, _ in mats]
-    per_shape = {}
-    for k, (name, x, _, _) in enumerate(mats):
-        def one(i, k=k):
-            b = sets[i % nsets][k]
-            K.kq_quantize(b["x"], b["f"], b["q"], b["s"], stream=torch.cuda.current_stream(), variant=variant)
-        g = capture(one, LAUNCHES)
-        timed_graph(g)
-        _, t = timed_graph(g, 3)
-        avg = t / (3 * LAUNCHES)
-        per_shape[name] = {"avg_us": round(avg * 1e6, 2), "GB/s": round(launch_bytes[k] / avg / 1e9, 1),
-                           "rows/s": round(x.shape[0] / avg, 1), "hbm_pct": round(100 * launch_bytes[k] / avg / 8e12, 2)}
-    # achieved: the timed region itself (its HIP events), per quantizer launch
-    n_launch = args.steps * len(mats)
-    achieved = step_bytes * args.steps / ev / 1e9
+    # ---- the timed region: exactly K steps, launched as one graph (launch
+    # gaps would otherwise show between kernels), bracketed by synchronisation
+    g_warm, _ = capture(step, max(1, args.warmup))
+    g_main, cs_main = capture(step, args.steps)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < RAMP_S:  # clocks out of their idle state
+        g_warm.replay()
+        torch.cuda.synchronize()
+    ramp_s = round(time.perf_counter() - t0, 3)
+    g_warm.replay()  # the W warm-up steps
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(cs_main):
+        e0.record(cs_main)  # HIP events on the stream the kernels run on
+        g_main.replay()
+        e1.record(cs_main)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = e0.elapsed_time(e1) * 1e-3
+    value = step_bytes * args.steps / wall / 1e9
+    avg_launch = ev / args.steps
+    achieved = step_bytes / avg_launch / 1e9
+    shape = K.kq_launch_shape(M, d)
     src_hash = kernel_source_hash()
-    traffic = load_traffic(src_hash)
+    strip = shape["strip"]
+    kname = f"kq_mfma_kernel<true, {strip}, false, {'true' if shape['nt_codes'] else 'false'}>"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": ("kq_mfma_kernel<true, kW> (kW = 8 at d=1152, 16 at d=4608)" if variant in (0, 1)
-                           else "stream_kernel<2>"),
-                "avg_launch_us": round(ev / n_launch * 1e6, 2), "launches_timed": n_launch,
-                "algorithmic_bytes_per_launch": round(step_bytes / len(mats)),
-                "timing": "HIP events on the launch stream around the timed graph of K steps",
-                "per_shape": per_shape, "per_shape_timing": f"graphs of {LAUNCHES} launches of one shape, replayed 3x"}
-
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(src_hash),
+                "kernel": kname, "avg_launch_us": round(avg_launch * 1e6, 2), "launches_timed": args.steps,
+                "algorithmic_bytes_per_launch": round(step_bytes),
+                "timing": "HIP events on the launch stream around the timed graph of K steps (one launch each)",
+                "launch_shape": shape}
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -697,70 +678,104 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "DiT CFG batch: 2x4096 tokens, d=1152 (36 factor sets) + d=4608 (144 factor sets), "
-                               "bf16 in, MXFP4 + E8M0 out, per-block Kronecker transforms",
-                   "M": 8192, "d": [1152, 4608], "nT": [36, 144], "variant": ["auto", "mfma", "butterfly"][variant],
-                   "rows_per_step": 2 * 8192, "rotating_sets": nsets, "accumulate": "fp32",
+        "config": {"workload": f"bandwidth sweep, largest single-GPU configuration: {M} x {d} bf16 activation "
+                               f"(N(0,1), 1% outlier channels x50, 0.1% each zero / subnormal / near-min-normal / "
+                               f"exact-tie blocks), [[1,1],[1,-1]]/sqrt(2) factors shared by all blocks "
+                               f"(normalised Walsh-Hadamard-32), MXFP4 + E8M0 out",
+                   "M": M, "d": d, "nT": 1, "factors": "hadamard", "rotating_sets": nsets, "accumulate": "fp32",
                    "launch": "HIP graph of the K timed steps", "clock_ramp_s": ramp_s,
                    "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
-                   "rows_per_s": round(2 * 8192 / (wall / args.steps), 1),
+                   "rows_per_s": round(M * args.steps / wall, 1),
                    "kernel_source_hash": src_hash},
         "roofline": roofline,
     }
 
     if not args.no_extras:
-        g_sq = capture(step_sq, args.steps)
-        timed_graph(capture(step_sq, max(1, args.warmup)))
-        sq_wall, _ = timed_graph(g_sq)
-        sq_value = step_bytes / (sq_wall / args.steps) / 1e9
-        other = 2 if variant in (0, 1) else 1
-        g_o = capture(lambda i: step_kq(i, other), args.steps)
-        timed_graph(capture(lambda i: step_kq(i, other), max(1, args.warmup)))
-        o_wall, _ = timed_graph(g_o)
-        def step_lu(i):
-            for b in sets[i % nsets]:
-                K.kq_quantize_lu(b["x"], b["lu"], b["q"], b["s"], stream=torch.cuda.current_stream())
+        steps = args.steps
+        scale_d = torch.from_numpy(I.smoothquant_scale(x_bits)).to(dev)
+        f_pb = torch.from_numpy(I.random_factors(d // 32, I.factor_seed(name))).to(dev)
+        f_id = torch.from_numpy(I.identity_factors(1)).to(dev)
+        lu_pb = torch.from_numpy(I.random_lu(d // 32, I.factor_seed(name) + 77)).to(dev)
 
-        def step_fwht(i):
-            for b in sets[i % nsets]:
-                K.fwht_quantize(b["x"], b["q"], b["s"], stream=torch.cuda.current_stream())
+        def leg(fn):
+            return _time_leg(fn, nsets, steps)
 
-        walls = {}
-        for nm, fn in (("lu", step_lu), ("fwht", step_fwht)):
-            g = capture(fn, args.steps)
-            timed_graph(capture(fn, max(1, args.warmup)))
-            walls[nm], _ = timed_graph(g)
-
-        def step_copy(i):
-            for b in sets[i % nsets]:
-                K.measure_copy41(b["x"], b["q"], stream=torch.cuda.current_stream())
-        g_c = capture(step_copy, args.steps)
-        timed_graph(capture(step_copy, max(1, args.warmup)))
-        c_wall, _ = timed_graph(g_c)
-        copy_bytes = sum(x.size * 2.5 for _, x, _, _ in mats)
-        out["comparison"] = {
-            "smoothquant_GB/s": round(sq_value, 1),
-            "smoothquant_hbm_pct": round(100 * sq_value / HBM_PEAK_GBS, 2),
-            "kroquant_over_smoothquant_speed": round(sq_wall / wall, 4),
-            ("butterfly_GB/s" if other == 2 else "mfma_GB/s"): round(step_bytes / (o_wall / args.steps) / 1e9, 1),
-            "k2_lu_GB/s": round(step_bytes / (walls["lu"] / args.steps) / 1e9, 1),
-            "fwht_GB/s": round(step_bytes / (walls["fwht"] / args.steps) / 1e9, 1),
-            "k2_lu_over_fwht_speed": round(walls["fwht"] / walls["lu"], 4),
-            "k2": "factor sets as 15 LU scalars per block, rebuilt in the kernel (kq_quantize_lu); "
-                  "fwht: fixed normalised Walsh-Hadamard-32 + MXFP4 (fwht_quantize)",
-            "copy41_ceiling_GB/s": round(copy_bytes / (c_wall / args.steps) / 1e9, 1),
-            "kroquant_over_copy41_speed": round(c_wall / wall, 4),
-            "copy41": "plain streaming copy of the same x (2 B read) into the q buffers (0.5 B written) per element",
+        b = lambda i: sets[i]
+        t = {
+            "kq_hadamard_shared": avg_launch,
+            "kq_perblock_384": leg(lambda i: K.kq_quantize(b(i)["x"], f_pb, b(i)["q"], b(i)["s"], stream=cur())),
+            "kq_identity": leg(lambda i: K.kq_quantize(b(i)["x"], f_id, b(i)["q"], b(i)["s"], stream=cur())),
+            "smoothquant": leg(lambda i: K.sq_quantize(b(i)["x"], scale_d, b(i)["q"], b(i)["s"], stream=cur())),
+            "kq_butterfly_perblock": leg(lambda i: K.kq_quantize(b(i)["x"], f_pb, b(i)["q"], b(i)["s"],
+                                                                 stream=cur(), variant=2)),
+            "k2_lu_perblock": leg(lambda i: K.kq_quantize_lu(b(i)["x"], lu_pb, b(i)["q"], b(i)["s"], stream=cur())),
+            "fwht": leg(lambda i: K.fwht_quantize(b(i)["x"], b(i)["q"], b(i)["s"], stream=cur())),
         }
+        c_best, c_form, c_per = best_copy(K, lambda i: sets[i]["x"], lambda i: sets[i]["q"], nsets, steps)
+        legs = {}
+        for k, sec in t.items():
+            legs[k] = {"us": round(sec * 1e6, 2), "GB/s": round(step_bytes / sec / 1e9, 1),
+                       "hbm_pct": round(100 * step_bytes / sec / 1e9 / HBM_PEAK_GBS, 2),
+                       "rows/s": round(M / sec, 1)}
+        copy_bytes = M * d * 2.5
+        legs["copy41_ceiling"] = {"us": round(c_best * 1e6, 2), "GB/s": round(copy_bytes / c_best / 1e9, 1),
+                                  "hbm_pct": round(100 * copy_bytes / c_best / 1e9 / HBM_PEAK_GBS, 2),
+                                  "form": c_form, "us_per_form": {f: round(s * 1e6, 2) for f, s in c_per.items()}}
+        sq = t["smoothquant"]
+        out["comparison"] = {
+            "legs": legs,
+            "smoothquant_GB/s": legs["smoothquant"]["GB/s"],
+            "smoothquant_rows/s": legs["smoothquant"]["rows/s"],
+            "smoothquant_hbm_pct": legs["smoothquant"]["hbm_pct"],
+            "kroquant_over_smoothquant_speed": round(sq / avg_launch, 4),
+            "kroquant_perblock_over_smoothquant_speed": round(sq / t["kq_perblock_384"], 4),
+            "k2_lu_over_fwht_speed": round(t["fwht"] / t["k2_lu_perblock"], 4),
+            "copy41_ceiling_GB/s": legs["copy41_ceiling"]["GB/s"],
+            "kroquant_over_copy41_speed": round(c_best / avg_launch, 4),
+            "notes": "every leg on the same input and buffers, graphs of K launches timed with HIP events; "
+                     "copy41: fastest of the 4:1 streaming copy forms (2 B read, 0.5 B written per element; "
+                     "GB/s at 2.5 B per element)",
+        }
+        del scale_d
+        # ---- per-shape entries: the DiT CFG batch and the double-stream 12288-wide input
+        per_shape = {}
+        for sname, sM, sd in PER_SHAPE:
+            xs = I.make_activation(sname)
+            fs = torch.from_numpy(I.make_factors(sname)).to(dev)
+            ss = torch.from_numpy(I.smoothquant_scale(xs)).to(dev)
+            sbytes = sM * sd * BYTES_PER_ELEM
+            ns = max(2, int(np.ceil(ROTATE_BYTES / sbytes)))
+            xd = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+            bufs = [dict(x=xd if k == 0 else xd.clone(), q=torch.empty((sM, sd // 2), dtype=torch.uint8, device=dev),
+                         s=torch.empty((sM, sd // 32), dtype=torch.uint8, device=dev)) for k in range(ns)]
+            torch.cuda.synchronize()
+            kq_t = _time_leg(lambda i: K.kq_quantize(bufs[i]["x"], fs, bufs[i]["q"], bufs[i]["s"], stream=cur()),
+                             ns, steps)
+            sq_t = _time_leg(lambda i: K.sq_quantize(bufs[i]["x"], ss, bufs[i]["q"], bufs[i]["s"], stream=cur()),
+                             ns, steps)
+            cp_t, cp_form, _ = best_copy(K, lambda i: bufs[i]["x"], lambda i: bufs[i]["q"], ns, steps)
+            per_shape[sname] = {
+                "M": sM, "d": sd, "nT": sd // 32, "launch_shape": K.kq_launch_shape(sM, sd),
+                "kq_us": round(kq_t * 1e6, 2), "kq_GB/s": round(sbytes / kq_t / 1e9, 1),
+                "kq_hbm_pct": round(100 * sbytes / kq_t / 1e9 / HBM_PEAK_GBS, 2), "kq_rows/s": round(sM / kq_t, 1),
+                "sq_us": round(sq_t * 1e6, 2), "sq_GB/s": round(sbytes / sq_t / 1e9, 1),
+                "sq_rows/s": round(sM / sq_t, 1), "kq_over_sq_speed": round(sq_t / kq_t, 4),
+                "copy41_us": round(cp_t * 1e6, 2), "copy41_form": cp_form,
+                "kq_over_copy41_speed": round(cp_t / kq_t, 4)}
+            print(f"[bench] {sname}: {per_shape[sname]}", file=sys.stderr, flush=True)
+            del bufs, xd
+            torch.cuda.empty_cache()
+        out["per_shape"] = per_shape
 
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(mats, args.cpu_seconds)
+        tiny = (I.make_activation("tiny"), I.make_factors("tiny"))
+        out["cpu_baseline"] = cpu_baseline(np.ascontiguousarray(x_bits[:CPU_ROWS]), f_h, tiny, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
 

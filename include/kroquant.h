@@ -44,7 +44,13 @@
  *     synchronisation.  Inputs are read-only; q and s are fully overwritten.
  *   - M == 0 is a successful no-op (pointers are not inspected).
  *   - Argument errors are reported before any HIP call and launch nothing.
- *   - Every entry point is stateless and reentrant.
+ *   - Every entry point is stateless and reentrant: a launch depends only on
+ *     its arguments and on the device it runs on (compute-unit count and
+ *     kernel occupancy, queried once per device under a lock).  Calls from
+ *     several host threads, on one stream or several, need no external
+ *     locking.  The library keeps no mutable settings; launch-shape overrides
+ *     exist only as an argument of the measurement entry points at the end of
+ *     this header.
  */
 #ifndef KROQUANT_H
 #define KROQUANT_H
@@ -88,12 +94,14 @@ int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors
 
 /*
  * kq_transform_f32: the transformed values y = x_blk . K_j (fp32) that
- * kq_quantize quantizes, written out for inspection.  Same transform code as
- * the quantizer for the chosen variant.
+ * kq_quantize quantizes, written out for inspection.  Same transform code and
+ * the same launch shape (strip width, token groups, workgroup order) as
+ * kq_quantize for the same (M, d); only the MX step is replaced by fp32
+ * stores of y.  kq_transform_tuned (below) selects the butterfly variant.
  *   y  dev, float32 [M, d], 16-byte aligned
  */
 int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
-                     int variant, void *stream);
+                     void *stream);
 
 /*
  * sq_quantize: SmoothQuant-style comparison quantizer (abstract: per-channel
@@ -262,6 +270,56 @@ int kq_fold_weight(const float *W, int64_t N, int64_t d, const float *factors, i
  * passed to kq_fold_weight, kq_factor_inverse or kq_quantize.  Returns
  * KQ_ERR_SINGULAR if some a is 0 or a scalar or result is not finite. */
 int kq_lu_factors(const float *lu, int64_t nT, float *factors);
+
+/* ---------------- measurement and test interface ----------------------- */
+/* Launch-shape overrides for benchmarks and for tests that pin a launch
+ * shape.  A field left 0 keeps the library's automatic choice; the product
+ * entry points above always use the automatic choices.  Out-of-range values
+ * are rejected with KQ_ERR_ARG. */
+typedef struct kq_tuning {
+    int32_t mfma_tiles_per_wg;     /* MFMA quantizer: 32-token tiles per workgroup, 1..256 */
+    int32_t mfma_groups;           /* 1 contiguous runs of tiles, 2 interleaved token groups */
+    int32_t mfma_strip;            /* 8 or 16 blocks (32-channel) per workgroup */
+    int32_t mfma_order;            /* 1 XCD-grouped workgroups, 2 flat order */
+    int32_t code_stores;           /* MFMA quantizer code stores: 1 default cache policy, 2 nontemporal */
+    int32_t stream_rows_per_wave;  /* butterfly, SmoothQuant, fp32, FWHT, 16-element kernels: rows per wave, 1..256 */
+    int32_t gemm_kernel;           /* mx_gemm: 1 per-tile, 2 persistent (k chunks of 256), 3 persistent (128) */
+    int32_t adaln_pass;            /* kq_adaln_quantize second pass: 1 matrix cores, 2 butterfly */
+    int32_t adaln_strip;           /* its matrix-core strip width: 4 or 8 blocks */
+    int32_t adaln_blocks_per_wave; /* butterfly / adaln_modulate pass: row blocks per wave, 1..256 */
+} kq_tuning;
+
+/* kq_quantize_ex / kq_transform_f32 / mx_gemm / kq_adaln_quantize with
+ * launch-shape overrides (tuning may be NULL: automatic).  variant is one of
+ * KQ_VARIANT_*.  Results do not depend on the launch shape: every shape
+ * computes the same values bit for bit (the tests check this). */
+int kq_quantize_tuned(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                      uint8_t *s, int variant, const kq_tuning *tuning, void *stream);
+int kq_transform_tuned(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                       int variant, const kq_tuning *tuning, void *stream);
+int mx_gemm_tuned(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+                  int64_t K, void *out, int out_bf16, const kq_tuning *tuning, void *stream);
+int kq_adaln_quantize_tuned(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                            int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
+                            uint8_t *q, uint8_t *s, const kq_tuning *tuning, void *stream);
+
+/* The launch shape the MFMA quantizer takes for an [M, d] input on the
+ * current device (adaln = 1: the AdaLN second pass), with the given overrides
+ * (NULL: automatic, as kq_quantize and kq_transform_f32).  shape receives
+ * {strip width in blocks, tiles per workgroup, interleaved (0/1), flat order
+ * (0/1), grid size in workgroups, nontemporal code stores (0/1)}.  Queries the
+ * device (occupancy); launches nothing.  Same argument errors as kq_quantize. */
+int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[6]);
+
+/* Copy kernels with the quantizer's 4:1 read:write footprint, timed by the
+ * benchmark as the practical HBM ceiling: src_bytes of src are read (16-byte
+ * loads) and src_bytes / 4 bytes of dst are written.  form 0 is the default
+ * (the fastest form measured); other forms are the alternatives the benchmark
+ * sweeps (1..KQ_COPY_FORMS-1).  src: dev, 16-byte aligned, src_bytes a
+ * multiple of 1024; dst: dev, 16-byte aligned, not overlapping src.  One
+ * launch on `stream`. */
+#define KQ_COPY_FORMS 6
+int kq_measure_copy41(const void *src, int64_t src_bytes, void *dst, int form, void *stream);
 
 /* Text for a status code (static storage). */
 const char *kq_status_string(int status);

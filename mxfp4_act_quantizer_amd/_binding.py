@@ -31,8 +31,17 @@ EXPORTS = (
     "kq_quantize", "kq_quantize_ex", "kq_transform_f32", "sq_quantize", "mx_quantize_f32",
     "kq_factor_inverse", "kq_block_matrix", "kq_block_inverse", "kq_fold_weight",
     "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize", "fwht_transform_f32", "kq_lu_factors", "mx_gemm",
-    "kq_adaln_quantize", "adaln_modulate", "kq_quantize16", "kq_transform16_f32", "kq_status_string", "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
+    "kq_adaln_quantize", "adaln_modulate", "kq_quantize16", "kq_transform16_f32", "kq_status_string",
+    "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
+    # measurement and test interface
+    "kq_quantize_tuned", "kq_transform_tuned", "mx_gemm_tuned", "kq_adaln_quantize_tuned", "kq_launch_shape",
+    "kq_measure_copy41",
 )
+KQ_COPY_FORMS = 6
+
+# launch-shape overrides (kq_tuning in kroquant.h); 0 keeps the automatic choice
+TUNING_FIELDS = ("mfma_tiles_per_wg", "mfma_groups", "mfma_strip", "mfma_order", "code_stores",
+                 "stream_rows_per_wave", "gemm_kernel", "adaln_pass", "adaln_strip", "adaln_blocks_per_wave")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mxfp4_act_quantizer_amd.build` "
@@ -43,9 +52,29 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 
+
+class Tuning(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in TUNING_FIELDS]
+
+
+def _tuning(tuning):
+    """A kq_tuning pointer from a dict of overrides (None: automatic)."""
+    if not tuning:
+        return None
+    unknown = set(tuning) - set(TUNING_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown tuning fields {sorted(unknown)}")
+    return ctypes.byref(Tuning(**{k: int(v) for k, v in tuning.items()}))
+
+
 _lib.kq_quantize.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
 _lib.kq_quantize_ex.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _INT, _P]
-_lib.kq_transform_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _INT, _P]
+_lib.kq_transform_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+_lib.kq_quantize_tuned.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _INT, _P, _P]
+_lib.kq_transform_tuned.argtypes = [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P]
+_lib.mx_gemm_tuned.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _P]
+_lib.kq_adaln_quantize_tuned.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P, _P, _P]
+_lib.kq_launch_shape.argtypes = [_I64, _I64, _INT, _P, _P]
 _lib.sq_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
 _lib.mx_quantize_f32.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.kq_quantize_lu.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
@@ -69,9 +98,8 @@ _lib.kq_build_info.restype = ctypes.c_char_p
 _lib.kq_last_hip_error.argtypes = []
 _lib.kq_hip_error_name.argtypes = [_INT]
 _lib.kq_hip_error_name.restype = ctypes.c_char_p
-_lib.kq_set_tuning.argtypes = [_INT, _INT]
-_lib.kq_measure_copy41.argtypes = [_P, _I64, _P, _P]
-for _name in EXPORTS + ("kq_set_tuning", "kq_measure_copy41"):
+_lib.kq_measure_copy41.argtypes = [_P, _I64, _P, _INT, _P]
+for _name in EXPORTS:
     if _name not in ("kq_status_string", "kq_build_info", "kq_hip_error_name"):
         getattr(_lib, _name).restype = _INT
 
@@ -157,14 +185,20 @@ def _nT(factors):
     return n // 20
 
 
-def kq_quantize(x, factors, q=None, s=None, stream=None, variant=KQ_VARIANT_AUTO):
-    """KroQuant quantizer: returns (q [M, d/2] u8, s [M, d/32] u8)."""
+def kq_quantize(x, factors, q=None, s=None, stream=None, variant=KQ_VARIANT_AUTO, tuning=None):
+    """KroQuant quantizer: returns (q [M, d/2] u8, s [M, d/32] u8).  `tuning`
+    (a dict of kq_tuning fields) pins the launch shape, for measurements."""
     torch = _torch()
     M, d = _md(x)
     q, s = _outputs(x, M, d, q, s)
-    st = _lib.kq_quantize_ex(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
-                             _nT(factors), _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"),
-                             int(variant), _stream_handle(stream))
+    args = (_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"), _nT(factors),
+            _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"))
+    if tuning:
+        st = _lib.kq_quantize_tuned(*args, int(variant), _tuning(tuning), _stream_handle(stream))
+    elif variant == KQ_VARIANT_AUTO:
+        st = _lib.kq_quantize(*args, _stream_handle(stream))
+    else:
+        st = _lib.kq_quantize_ex(*args, int(variant), _stream_handle(stream))
     _check(st, "kq_quantize")
     return q, s
 
@@ -173,16 +207,28 @@ def kq_quantize_ex(x, factors, q, s, variant, stream=None):
     return kq_quantize(x, factors, q, s, stream, variant)
 
 
-def kq_transform_f32(x, factors, y=None, stream=None, variant=KQ_VARIANT_AUTO):
+def kq_transform_f32(x, factors, y=None, stream=None, variant=KQ_VARIANT_AUTO, tuning=None):
     """Transformed values y = x_blk . K_j (fp32) as the quantizer computes them."""
     torch = _torch()
     M, d = _md(x)
     if y is None:
         y = torch.empty((M, d), dtype=torch.float32, device=x.device)
-    st = _lib.kq_transform_f32(_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"),
-                               _nT(factors), _dev(y, (torch.float32,), "y"), int(variant), _stream_handle(stream))
+    args = (_dev(x, _bf16_types(), "x"), M, d, _dev(factors, (torch.float32,), "factors"), _nT(factors),
+            _dev(y, (torch.float32,), "y"))
+    if tuning or variant != KQ_VARIANT_AUTO:
+        st = _lib.kq_transform_tuned(*args, int(variant), _tuning(tuning), _stream_handle(stream))
+    else:
+        st = _lib.kq_transform_f32(*args, _stream_handle(stream))
     _check(st, "kq_transform_f32")
     return y
+
+
+def kq_launch_shape(M, d, adaln=False, tuning=None):
+    """Launch shape of the MFMA quantizer for [M, d] on the current device:
+    dict of strip, tiles_per_wg, interleave, flat, grid, nt_codes."""
+    out = (ctypes.c_int64 * 6)()
+    _check(_lib.kq_launch_shape(int(M), int(d), 1 if adaln else 0, _tuning(tuning), out), "kq_launch_shape")
+    return dict(zip(("strip", "tiles_per_wg", "interleave", "flat", "grid", "nt_codes"), (int(v) for v in out)))
 
 
 def _nT_lu(lu):
@@ -236,7 +282,7 @@ def fwht_transform_f32(x, y=None, stream=None):
     return y
 
 
-def mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
+def mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None, tuning=None):
     """W4A4 product out = A . B^T of two MXFP4 matrices (codes [rows, K/2] u8,
     scales [rows, K/32] u8), accumulated in fp32; out float32 or bfloat16."""
     torch = _torch()
@@ -250,8 +296,12 @@ def mx_gemm(qa, sa, qb, sb, out=None, out_dtype=None, stream=None):
     if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (M, N):
         raise ValueError("out must be float32 or bfloat16 [M, N]")
     u8 = (torch.uint8,)
-    st = _lib.mx_gemm(_dev(qa, u8, "qa"), _dev(sa, u8, "sa"), M, _dev(qb, u8, "qb"), _dev(sb, u8, "sb"), N, K,
-                      _dev(out, (torch.float32, torch.bfloat16), "out"), bf, _stream_handle(stream))
+    args = (_dev(qa, u8, "qa"), _dev(sa, u8, "sa"), M, _dev(qb, u8, "qb"), _dev(sb, u8, "sb"), N, K,
+            _dev(out, (torch.float32, torch.bfloat16), "out"), bf)
+    if tuning:
+        st = _lib.mx_gemm_tuned(*args, _tuning(tuning), _stream_handle(stream))
+    else:
+        st = _lib.mx_gemm(*args, _stream_handle(stream))
     _check(st, "mx_gemm")
     return out
 
@@ -320,20 +370,24 @@ def _stats(h, M, stats):
     return stats
 
 
-def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, s=None, stats=None, stream=None):
+def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, s=None, stats=None, stream=None,
+                      tuning=None):
     """AdaLN front-end fused with the quantizer: x = LN(h) (1 + scale[b]) +
     shift[b] (b = row // tokens_per_sample) rounded to bf16, then the
-    butterfly transform and MXFP4.  `stats` is the [M, 2] float64 workspace
+    Kronecker transform and MXFP4.  `stats` is the [M, 2] float64 workspace
     (allocated here when not given).  Returns (q, s)."""
     torch = _torch()
     M, d = _md(h)
     q, s = _outputs(h, M, d, q, s)
     stats = _stats(h, M, stats)
-    st = _lib.kq_adaln_quantize(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
-                                _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
-                                _dev(factors, (torch.float32,), "factors"), _nT(factors),
-                                _dev(stats, (torch.float64,), "stats"), _dev(q, (torch.uint8,), "q"),
-                                _dev(s, (torch.uint8,), "s"), _stream_handle(stream))
+    args = (_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
+            _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
+            _dev(factors, (torch.float32,), "factors"), _nT(factors), _dev(stats, (torch.float64,), "stats"),
+            _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"))
+    if tuning:
+        st = _lib.kq_adaln_quantize_tuned(*args, _tuning(tuning), _stream_handle(stream))
+    else:
+        st = _lib.kq_adaln_quantize(*args, _stream_handle(stream))
     _check(st, "kq_adaln_quantize")
     return q, s
 
@@ -353,28 +407,16 @@ def adaln_modulate(h, shift, scale, tokens_per_sample, eps, x=None, stats=None, 
     return x
 
 
-def set_tuning(key, value):
-    """Launch-shape knobs for measurements (0 = automatic everywhere): 0 MFMA tiles
-    per workgroup, 1 butterfly rows/wave, 2 SmoothQuant/fp32 rows/wave, 3 MFMA
-    token groups (1 contiguous, 2 interleaved), 4 MFMA strip width (8 or 16
-    blocks), 5 MFMA workgroup order (1 XCD-grouped, 2 flat), 6 AdaLN row blocks
-    per wave (rounded up to 4), 7 W4A4 product kernel (1 per-tile, 2 persistent with k chunks of
-    256, 3 persistent with k chunks of 128; the persistent forms apply when K %
-    128 == 0 and the output rows split into 16-byte pieces), 8 AdaLN second pass of
-    kq_adaln_quantize (1 matrix cores, 2 butterfly), 9 its matrix-core strip width
-    (4 or 8 blocks)."""
-    _check(_lib.kq_set_tuning(int(key), int(value)), "kq_set_tuning")
-
-
-def measure_copy41(src, dst, stream=None):
-    """Measurement only: the plain 4:1 streaming copy (reads all of src, writes
-    src.nbytes / 4 bytes of dst) used as the benchmark's HBM ceiling."""
+def measure_copy41(src, dst, form=0, stream=None):
+    """Measurement only: a streaming copy with the quantizer's 4:1 footprint
+    (reads all of src, writes src.nbytes / 4 bytes of dst), the benchmark's
+    HBM ceiling; `form` picks one of the KQ_COPY_FORMS copy forms."""
     if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("src and dst must be contiguous GPU tensors")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes // 4:
         raise ValueError("dst must hold src.nbytes / 4 bytes")
-    _check(_lib.kq_measure_copy41(src.data_ptr(), nbytes, dst.data_ptr(), _stream_handle(stream)),
+    _check(_lib.kq_measure_copy41(src.data_ptr(), nbytes, dst.data_ptr(), int(form), _stream_handle(stream)),
            "kq_measure_copy41")
 
 

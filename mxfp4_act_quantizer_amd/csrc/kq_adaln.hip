@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void adaln_stream_kernel(const uint16_t *__res
 
 hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
                         float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
-                        uint16_t *x, hipStream_t stream)
+                        uint16_t *x, const Tuning &tn, hipStream_t stream)
 {
     // pass 1: row statistics
     const int64_t waves = (M + kStatRows - 1) / kStatRows;
@@ -276,7 +276,7 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
         g >>= 1; // gcd(nOct, 64): nOct is a multiple of 4
     const int Rb = 64 / g;
     const int Wb = Rb * nOct / 64;
-    int kIt = tuning().adaln_blocks_per_wave;
+    int kIt = tn.adaln_blocks_per_wave;
     if (kIt <= 0)
         kIt = kU; // blocks per wave: one pipeline stage (measured best of 4..16 on MI355X)
     kIt = (kIt + kU - 1) / kU * kU;
@@ -294,8 +294,8 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
     hipError_t e = hipLaunchKernel(fs, dim3((unsigned)grid1), dim3(256), args1, 0, stream);
     if (e != hipSuccess)
         return e;
-    if (x == nullptr && tuning().adaln_pass != 2)
-        return launch_adaln_mfma(h, M, d, stats, shift, scale, T, factors, nT, q, s, stream);
+    if (x == nullptr && tn.adaln_pass != 2)
+        return launch_adaln_mfma(h, M, d, stats, shift, scale, T, factors, nT, q, s, tn, stream);
     int per_block = nT > 1 ? 1 : 0;
     const double *cst = stats;
     int rb = Rb, wbn = Wb, kit = kIt;

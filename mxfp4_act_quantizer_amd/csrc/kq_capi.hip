@@ -19,15 +19,42 @@ bool overlap(const void *p, int64_t n, const void *r, int64_t m)
     return n > 0 && m > 0 && a0 < b1 && b0 < a1;
 }
 
-int check_md(int64_t M, int64_t d)
+// Shape check of a [M, d] activation with blocks of bw channels.  The block
+// count M * (d / bw) is bounded by comparing M with the quotient, so no
+// product is formed before the bound holds (afterwards M * d * 4 < 2^63).
+int check_md_bw(int64_t M, int64_t d, int64_t bw)
 {
     if (M < 0 || d <= 0)
         return KQ_ERR_ARG;
-    if (d % 32 != 0)
+    if (d % bw != 0 || d > kq::kMaxD)
         return KQ_ERR_SHAPE;
-    if (d > kq::kMaxD || (M > 0 && (M * (d / 32)) > kq::kMaxBlocksTotal))
+    if (M > kq::kMaxBlocksTotal / (d / bw))
         return KQ_ERR_SHAPE;
     return KQ_OK;
+}
+
+int check_md(int64_t M, int64_t d) { return check_md_bw(M, d, 32); }
+
+// Launch-shape overrides: NULL or every field in its documented range.
+int check_tuning(const kq_tuning *t)
+{
+    if (!t)
+        return KQ_OK;
+    auto in = [](int32_t v, int32_t lo, int32_t hi) { return v == 0 || (v >= lo && v <= hi); };
+    const bool ok = in(t->mfma_tiles_per_wg, 1, 256) && in(t->mfma_groups, 1, 2) &&
+                    (t->mfma_strip == 0 || t->mfma_strip == 8 || t->mfma_strip == 16) && in(t->mfma_order, 1, 2) &&
+                    in(t->code_stores, 1, 2) && in(t->stream_rows_per_wave, 1, 256) && in(t->gemm_kernel, 1, 3) &&
+                    in(t->adaln_pass, 1, 2) && (t->adaln_strip == 0 || t->adaln_strip == 4 || t->adaln_strip == 8) &&
+                    in(t->adaln_blocks_per_wave, 1, 256);
+    return ok ? KQ_OK : KQ_ERR_ARG;
+}
+
+kq::Tuning tuning_of(const kq_tuning *t)
+{
+    kq::Tuning r{};
+    if (t)
+        r = *t;
+    return r;
 }
 
 int check_sets(int64_t d, int64_t nT)
@@ -80,14 +107,16 @@ int check_param(const float *p, int64_t count, const void *x, int64_t xbytes, co
 
 extern "C" {
 
-int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                   uint8_t *s, int variant, void *stream)
+int kq_quantize_tuned(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                      uint8_t *s, int variant, const kq_tuning *tuning, void *stream)
 {
     int st = check_md(M, d);
     if (st)
         return st;
     if (variant != KQ_VARIANT_AUTO && variant != KQ_VARIANT_MFMA && variant != KQ_VARIANT_BUTTERFLY)
         return KQ_ERR_ARG;
+    if ((st = check_tuning(tuning)))
+        return st;
     if ((st = check_sets(d, nT)))
         return st;
     if (M == 0)
@@ -98,25 +127,34 @@ int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors
     if ((st = check_param(factors, nT * 20, x, xb, q, M * (d / 2), s, M * (d / 32))))
         return st;
     hipStream_t hs = (hipStream_t)stream;
+    const kq::Tuning tn = tuning_of(tuning);
     if (variant == KQ_VARIANT_BUTTERFLY)
-        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, q, s, nullptr, hs));
-    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, q, s, nullptr, 0, hs));
+        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, q, s, nullptr, tn, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, q, s, nullptr, 0, tn, hs));
+}
+
+int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                   uint8_t *s, int variant, void *stream)
+{
+    return kq_quantize_tuned(x, M, d, factors, nT, q, s, variant, nullptr, stream);
 }
 
 int kq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                 uint8_t *s, void *stream)
 {
-    return kq_quantize_ex(x, M, d, factors, nT, q, s, KQ_VARIANT_AUTO, stream);
+    return kq_quantize_tuned(x, M, d, factors, nT, q, s, KQ_VARIANT_AUTO, nullptr, stream);
 }
 
-int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
-                     int variant, void *stream)
+int kq_transform_tuned(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                       int variant, const kq_tuning *tuning, void *stream)
 {
     int st = check_md(M, d);
     if (st)
         return st;
     if (variant != KQ_VARIANT_AUTO && variant != KQ_VARIANT_MFMA && variant != KQ_VARIANT_BUTTERFLY)
         return KQ_ERR_ARG;
+    if ((st = check_tuning(tuning)))
+        return st;
     if ((st = check_sets(d, nT)))
         return st;
     if (M == 0)
@@ -131,9 +169,37 @@ int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *facto
     if ((st = check_param(factors, nT * 20, x, xb, y, yb, nullptr, 0)))
         return st;
     hipStream_t hs = (hipStream_t)stream;
+    const kq::Tuning tn = tuning_of(tuning);
     if (variant == KQ_VARIANT_BUTTERFLY)
-        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, nullptr, nullptr, y, hs));
-    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, nullptr, nullptr, y, 0, hs));
+        return hip_status(kq::launch_kq_butterfly(x, M, d, factors, nT, nullptr, nullptr, y, tn, hs));
+    return hip_status(kq::launch_kq_mfma(x, M, d, factors, nT, nullptr, nullptr, y, 0, tn, hs));
+}
+
+int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
+                     void *stream)
+{
+    return kq_transform_tuned(x, M, d, factors, nT, y, KQ_VARIANT_AUTO, nullptr, stream);
+}
+
+int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[6])
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if ((adaln != 0 && adaln != 1) || !shape)
+        return KQ_ERR_ARG;
+    if ((st = check_tuning(tuning)))
+        return st;
+    kq::MfmaShape sh{};
+    if ((st = hip_status(kq::mfma_launch_shape(M, d, tuning_of(tuning), adaln != 0, sh))))
+        return st;
+    shape[0] = sh.strip;
+    shape[1] = sh.tiles_per_wg;
+    shape[2] = sh.interleave;
+    shape[3] = sh.flat;
+    shape[4] = sh.grid;
+    shape[5] = sh.nt_codes;
+    return KQ_OK;
 }
 
 int kq_quantize_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, uint8_t *q, uint8_t *s,
@@ -151,7 +217,7 @@ int kq_quantize_lu(const uint16_t *x, int64_t M, int64_t d, const float *lu, int
         return st;
     if ((st = check_param(lu, nT * 15, x, xb, q, M * (d / 2), s, M * (d / 32))))
         return st;
-    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, q, s, nullptr, 1, (hipStream_t)stream));
+    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, q, s, nullptr, 1, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int kq_transform_lu_f32(const uint16_t *x, int64_t M, int64_t d, const float *lu, int64_t nT, float *y,
@@ -173,7 +239,7 @@ int kq_transform_lu_f32(const uint16_t *x, int64_t M, int64_t d, const float *lu
         return KQ_ERR_OVERLAP;
     if ((st = check_param(lu, nT * 15, x, xb, y, yb, nullptr, 0)))
         return st;
-    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, nullptr, nullptr, y, 1, (hipStream_t)stream));
+    return hip_status(kq::launch_kq_mfma(x, M, d, lu, nT, nullptr, nullptr, y, 1, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream)
@@ -185,7 +251,7 @@ int fwht_quantize(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *
         return KQ_OK;
     if ((st = check_quant_io(x, M * d * 2, q, s, M, d)))
         return st;
-    return hip_status(kq::launch_fwht(x, M, d, q, s, nullptr, (hipStream_t)stream));
+    return hip_status(kq::launch_fwht(x, M, d, q, s, nullptr, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *stream)
@@ -201,7 +267,7 @@ int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *
         return KQ_ERR_ALIGN;
     if (overlap(x, M * d * 2, y, M * d * 4))
         return KQ_ERR_OVERLAP;
-    return hip_status(kq::launch_fwht(x, M, d, nullptr, nullptr, y, (hipStream_t)stream));
+    return hip_status(kq::launch_fwht(x, M, d, nullptr, nullptr, y, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s, void *stream)
@@ -216,7 +282,7 @@ int sq_quantize(const uint16_t *x, int64_t M, int64_t d, const float *scale, uin
         return st;
     if ((st = check_param(scale, d, x, xb, q, M * (d / 2), s, M * (d / 32))))
         return st;
-    return hip_status(kq::launch_sq(x, M, d, scale, q, s, (hipStream_t)stream));
+    return hip_status(kq::launch_sq(x, M, d, scale, q, s, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, void *stream)
@@ -228,15 +294,19 @@ int mx_quantize_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s
         return KQ_OK;
     if ((st = check_quant_io(x, M * d * 4, q, s, M, d)))
         return st;
-    return hip_status(kq::launch_mx_f32(x, M, d, q, s, (hipStream_t)stream));
+    return hip_status(kq::launch_mx_f32(x, M, d, q, s, kq::Tuning{}, (hipStream_t)stream));
 }
 
-int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
-            int64_t K, void *out, int out_bf16, void *stream)
+int mx_gemm_tuned(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+                  int64_t K, void *out, int out_bf16, const kq_tuning *tuning, void *stream)
 {
     if (M < 0 || N < 0 || K <= 0 || (out_bf16 != 0 && out_bf16 != 1))
         return KQ_ERR_ARG;
-    if (K % 32 != 0 || K > kq::kMaxD || N > ((int64_t)1 << 21) || (M > 0 && N > 0 && M * N > ((int64_t)1 << 40)))
+    int st = check_tuning(tuning);
+    if (st)
+        return st;
+    // bounds by quotient: no product is formed before M * N <= 2^40 holds
+    if (K % 32 != 0 || K > kq::kMaxD || N > ((int64_t)1 << 21) || (N > 0 && M > ((int64_t)1 << 40) / N))
         return KQ_ERR_SHAPE;
     if (M == 0 || N == 0)
         return KQ_OK;
@@ -248,16 +318,22 @@ int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, 
     if (overlap(out, ob, qa, M * (K / 2)) || overlap(out, ob, sa, M * (K / 32)) || overlap(out, ob, qb, N * (K / 2)) ||
         overlap(out, ob, sb, N * (K / 32)))
         return KQ_ERR_OVERLAP;
-    return hip_status(kq::launch_mx_gemm(qa, sa, M, qb, sb, N, K, out, out_bf16, (hipStream_t)stream));
+    return hip_status(
+        kq::launch_mx_gemm(qa, sa, M, qb, sb, N, K, out, out_bf16, tuning_of(tuning), (hipStream_t)stream));
+}
+
+int mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb, int64_t N,
+            int64_t K, void *out, int out_bf16, void *stream)
+{
+    return mx_gemm_tuned(qa, sa, M, qb, sb, N, K, out, out_bf16, nullptr, stream);
 }
 
 // shape checks of the 16-element-block entry points
 static int check_md16(int64_t M, int64_t d, int64_t nT)
 {
-    if (M < 0 || d <= 0)
-        return KQ_ERR_ARG;
-    if (d % 16 != 0 || d > kq::kMaxD || (M > 0 && (M * (d / 16)) > kq::kMaxBlocksTotal))
-        return KQ_ERR_SHAPE;
+    const int st = check_md_bw(M, d, 16);
+    if (st)
+        return st;
     if (nT != 1 && nT != d / 16)
         return KQ_ERR_SHAPE;
     return KQ_OK;
@@ -280,7 +356,7 @@ int kq_quantize16(const uint16_t *x, int64_t M, int64_t d, const float *factors,
         return KQ_ERR_OVERLAP;
     if ((st = check_param(factors, nT * 16, x, xb, q, qb, s, sb)))
         return st;
-    return hip_status(kq::launch_kq16(x, M, d, factors, nT, q, s, nullptr, (hipStream_t)stream));
+    return hip_status(kq::launch_kq16(x, M, d, factors, nT, q, s, nullptr, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
@@ -300,21 +376,26 @@ int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *fac
         return KQ_ERR_OVERLAP;
     if ((st = check_param(factors, nT * 16, x, xb, y, yb, nullptr, 0)))
         return st;
-    return hip_status(kq::launch_kq16(x, M, d, factors, nT, nullptr, nullptr, y, (hipStream_t)stream));
+    return hip_status(kq::launch_kq16(x, M, d, factors, nT, nullptr, nullptr, y, kq::Tuning{}, (hipStream_t)stream));
 }
 
 // shared checks of the AdaLN entry points (h, shift, scale, T, eps, the
 // statistics workspace); out and out2 are the outputs, each with its byte count
+// (own_stats: the workspace is the library's own array, so `stats` is not
+// the caller's and is not checked)
 static int check_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
-                       float eps, const double *stats, const void *out, int64_t ob, const void *out2, int64_t ob2)
+                       float eps, const double *stats, const void *out, int64_t ob, const void *out2, int64_t ob2,
+                       bool own_stats = false)
 {
     if (T < 1 || !(eps > 0.0f) || eps > 3.0e38f)
         return KQ_ERR_ARG;
-    if (!h || !shift || !scale || !stats || !out)
+    if (!h || !shift || !scale || (!stats && !own_stats) || !out)
         return KQ_ERR_ARG;
     if (!aligned(h, 16) || !aligned(out, 16) || !aligned(shift, 4) || !aligned(scale, 4) || !aligned(stats, 8))
         return KQ_ERR_ALIGN;
-    const int64_t hb = M * d * 2, pb = ((M + T - 1) / T) * d * 4, wb = M * 16;
+    // samples: ceil(M / T) formed without M + T - 1 (T may be near INT64_MAX)
+    const int64_t samples = M > 0 ? (M - 1) / T + 1 : 0;
+    const int64_t hb = M * d * 2, pb = samples * d * 4, wb = M * 16;
     const void *in[3] = {h, shift, scale};
     const int64_t inb[3] = {hb, pb, pb};
     for (int i = 0; i < 3; ++i)
@@ -325,12 +406,14 @@ static int check_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shi
     return KQ_OK;
 }
 
-int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
-                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
-                      uint8_t *q, uint8_t *s, void *stream)
+int kq_adaln_quantize_tuned(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                            int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
+                            uint8_t *q, uint8_t *s, const kq_tuning *tuning, void *stream)
 {
     int st = check_md(M, d);
     if (st)
+        return st;
+    if ((st = check_tuning(tuning)))
         return st;
     if ((st = check_sets(d, nT)))
         return st;
@@ -346,7 +429,15 @@ int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shif
     if (overlap(factors, nT * 80, stats, M * 16))
         return KQ_ERR_OVERLAP;
     return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, stats, q, s,
-                                       nullptr, (hipStream_t)stream));
+                                       nullptr, tuning_of(tuning), (hipStream_t)stream));
+}
+
+int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                      int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
+                      uint8_t *q, uint8_t *s, void *stream)
+{
+    return kq_adaln_quantize_tuned(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, stats, q, s, nullptr,
+                                   stream);
 }
 
 int adaln_modulate(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
@@ -360,7 +451,7 @@ int adaln_modulate(const uint16_t *h, int64_t M, int64_t d, const float *shift, 
     if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, stats, x, M * d * 2, nullptr, 0)))
         return st;
     return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, nullptr, 1, stats, nullptr,
-                                       nullptr, x, (hipStream_t)stream));
+                                       nullptr, x, kq::Tuning{}, (hipStream_t)stream));
 }
 
 const char *kq_status_string(int status)
@@ -386,23 +477,5 @@ const char *kq_build_info(void)
 int kq_last_hip_error(void) { return (int)last_hip_error; }
 
 const char *kq_hip_error_name(int code) { return hipGetErrorName((hipError_t)code); }
-
-// Tuning knobs for measurements (not part of the stable header).
-int kq_set_tuning(int key, int value)
-{
-    switch (key) {
-    case 0: kq::tuning().mfma_tiles_per_wave = value; return KQ_OK;
-    case 1: kq::tuning().bfly_rows_per_wave = value; return KQ_OK;
-    case 2: kq::tuning().stream_rows_per_wave = value; return KQ_OK;
-    case 3: kq::tuning().mfma_interleave = value; return KQ_OK;
-    case 4: kq::tuning().mfma_strip = value; return KQ_OK;
-    case 5: kq::tuning().mfma_order = value; return KQ_OK;
-    case 6: kq::tuning().adaln_blocks_per_wave = value; return KQ_OK;
-    case 7: kq::tuning().gemm_variant = value; return KQ_OK;
-    case 8: kq::tuning().adaln_pass = value; return KQ_OK;
-    case 9: kq::tuning().adaln_strip = value; return KQ_OK;
-    default: return KQ_ERR_ARG;
-    }
-}
 
 } // extern "C"

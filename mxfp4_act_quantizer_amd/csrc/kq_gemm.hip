@@ -734,38 +734,6 @@ __global__ __launch_bounds__(G::T) __attribute__((amdgpu_waves_per_eu(G::OCC, G:
 
 namespace {
 
-int gemm_cus()
-{
-    static int n = 0;
-    if (!n) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-    }
-    return n;
-}
-
-// Resident workgroups per CU of a kernel (from the runtime), cached per kernel.
-int gemm_occupancy(const void *fn, int threads)
-{
-    static const void *keys[8] = {};
-    static int vals[8] = {};
-    for (int i = 0; i < 8; ++i)
-        if (keys[i] == fn)
-            return vals[i];
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu <= 0)
-        per_cu = 1;
-    for (int i = 0; i < 8; ++i)
-        if (!keys[i]) {
-            keys[i] = fn;
-            vals[i] = per_cu;
-            break;
-        }
-    return per_cu;
-}
-
 template <class G>
 hipError_t launch_persistent(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
                              int64_t N, int64_t K, void *out, int bf16, hipStream_t stream)
@@ -775,7 +743,7 @@ hipError_t launch_persistent(const uint8_t *qa, const uint8_t *sa, int64_t M, co
     if (tiles > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     const void *fn = bf16 ? (const void *)mx_gemm_persistent<G, true> : (const void *)mx_gemm_persistent<G, false>;
-    int64_t grid = (int64_t)gemm_cus() * gemm_occupancy(fn, G::T);
+    int64_t grid = (int64_t)device_cus() * occupancy_per_cu(fn, G::T);
     const int64_t tiles8 = (tiles + kGemmXcds - 1) / kGemmXcds * kGemmXcds;
     if (grid > tiles8)
         grid = tiles8;
@@ -799,13 +767,13 @@ using GemmP128 = PGeom<2, 2, 2, 2, 128, 4>;
 } // namespace
 
 hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const uint8_t *qb, const uint8_t *sb,
-                          int64_t N, int64_t K, void *out, int bf16, hipStream_t stream)
+                          int64_t N, int64_t K, void *out, int bf16, const Tuning &tune, hipStream_t stream)
 {
     // the persistent form stores whole 16-byte output pieces and reads whole
     // dwords of scales
     const bool persistent = K % 128 == 0 && N % (bf16 ? 8 : 4) == 0 && (uintptr_t)out % 16 == 0 &&
                             (uintptr_t)sa % 4 == 0 && (uintptr_t)sb % 4 == 0;
-    const int variant = tuning().gemm_variant;
+    const int variant = tune.gemm_kernel;
     if (persistent && variant != 1) {
         if (variant == 3)
             return launch_persistent<GemmP128>(qa, sa, M, qb, sb, N, K, out, bf16, stream);

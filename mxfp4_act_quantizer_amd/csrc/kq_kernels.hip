@@ -31,6 +31,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "kq_device.h"
 #include "kq_internal.h"
 
@@ -40,12 +44,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-Tuning &tuning()
-{
-    static Tuning t{0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    return t;
-}
 
 // ---------------------------------------------------------------------------
 // MFMA variant
@@ -250,12 +248,15 @@ __device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<k
 // workgroup (kW consecutive bytes per token).  rq and rs cover the tile's own
 // rows, so rows past M fall outside them; blocks past the row end, the spare
 // scale lanes, and every lane when `valid` is false set bit 31 of their
-// offsets, which the range check drops.  Both stores keep the default cache
-// policy, so that the codes are still in the caches when the W4A4 product
-// reads them right after: nontemporal code stores made the quantizer alone
-// 3-6% faster but quantize-then-product at the DiT qkv shape (8192 x 1152 by
-// 3456) 8% slower (41.7 against 38.4 us).
-template <int kW>
+// offsets, which the range check drops.  With kNT the code stores are
+// nontemporal (streamed past the caches), otherwise they keep the default
+// cache policy; the launcher takes nontemporal stores when the launch's whole
+// footprint exceeds the last-level cache, so that codes a following W4A4
+// product could still read from the caches keep the default policy: at the
+// DiT qkv shape (8192 x 1152 by 3456) nontemporal code stores made the
+// quantizer alone 3-6% faster but quantize-then-product 8% slower (41.7
+// against 38.4 us).  Scale bytes always keep the default policy.
+template <int kW, bool kNT>
 __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool valid, int bg, int nB, int d, int wave,
                                            int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
 {
@@ -266,7 +267,7 @@ __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool 
     const unsigned drop_q = (unsigned)(bg * kW + (c8 >> 1) >= nB || !valid) << 31;
     const u32x2 v = *(const u32x2 *)&st.q[par][tq][c8 * 8];
     __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * kW * 16 + c8 * 8) | drop_q), 0,
-                                          0);
+                                          kNT ? kAuxNT : 0);
     const int f = wave * 64 + lane; // flat lane of the workgroup
     const int ts = (f / kW) % kTileT;
     const int cs = f % kW;
@@ -308,7 +309,7 @@ struct AdArgs {
 // compiler spills, and that measured no faster).
 constexpr int kAdOcc = 2;
 
-template <bool kQuant, int kW, bool kAd = false>
+template <bool kQuant, int kW, bool kAd = false, bool kNT = false>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? kAdOcc : 4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
     auto store_prev = [&](int kp) {
         const int64_t r0 = trow(kp < 0 ? 0 : kp);
         const int64_t rows = (M - r0) < kTileT ? (M - r0) : kTileT;
-        store_tile(st, kp & 1, kp >= 0, bg, nB, d, wave, lane, out_buffer(q + r0 * (d >> 1), rows * (d >> 1)),
+        store_tile<kW, kNT>(st, kp & 1, kp >= 0, bg, nB, d, wave, lane, out_buffer(q + r0 * (d >> 1), rows * (d >> 1)),
                    out_buffer(s + r0 * nB, rows * nB));
     };
     // Each prologue load is followed by a store pair with every lane dropped
@@ -644,61 +645,91 @@ __global__ __launch_bounds__(256) void stream_kernel(const void *__restrict__ xi
         process_rows<kMode>(bufA, m, m0, m1, d, nB, oct, cok, qp, r, B, B16, rq, rs, y);
 }
 
+
 // ---------------------------------------------------------------------------
-// launchers
+// device queries (thread-safe, cached per device and kernel)
 // ---------------------------------------------------------------------------
-static int num_cus()
+namespace {
+std::mutex g_info_mu;
+std::map<int, int> g_cus;
+std::map<std::pair<int, const void *>, int> g_occ;
+
+int current_device()
 {
-    static int n = 0;
-    if (!n) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = 0;
+    return dev;
+}
+} // namespace
+
+int device_cus()
+{
+    const int dev = current_device();
+    std::lock_guard<std::mutex> lock(g_info_mu);
+    const auto it = g_cus.find(dev);
+    if (it != g_cus.end())
+        return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    g_cus[dev] = n;
     return n;
 }
 
-// Resident workgroups of an MFMA kernel per XCD (occupancy from the runtime),
-// cached per kernel instance.
-static int mfma_wgs_per_xcd(const void *fn, int threads)
+int occupancy_per_cu(const void *fn, int threads)
 {
-    static const void *keys[4] = {nullptr, nullptr, nullptr, nullptr};
-    static int vals[4] = {0, 0, 0, 0};
-    for (int i = 0; i < 4; ++i)
-        if (keys[i] == fn)
-            return vals[i];
+    const int dev = current_device();
+    std::lock_guard<std::mutex> lock(g_info_mu);
+    const auto key = std::make_pair(dev, fn);
+    const auto it = g_occ.find(key);
+    if (it != g_occ.end())
+        return it->second;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu <= 0)
         per_cu = 1;
-    int v = per_cu * num_cus() / (int)kXcds;
-    if (v < 1)
-        v = 1;
-    for (int i = 0; i < 4; ++i)
-        if (!keys[i]) {
-            keys[i] = fn;
-            vals[i] = v;
-            break;
-        }
-    return v;
+    g_occ[key] = per_cu;
+    return per_cu;
 }
 
-template <int kW, bool kAd = false>
-static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                                   uint8_t *q, uint8_t *s, float *y, int lu, hipStream_t stream, AdArgs ad = {})
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+// Resident workgroups per XCD of an MFMA quantizer instance (at least 1).
+int64_t mfma_wgs_per_xcd(const void *fn, int threads)
 {
-    const int nB = (int)(d / 32);
-    const int nBG = (nB + kW - 1) / kW;
+    const int64_t v = (int64_t)occupancy_per_cu(fn, threads) * device_cus() / (int64_t)kXcds;
+    return v < 1 ? 1 : v;
+}
+
+// The quantizing instance of a strip width: the launch shape of every form
+// (quantizer, transform export, nontemporal stores) is taken from its occupancy.
+const void *mfma_shape_fn(int w, bool adaln)
+{
+    if (adaln)
+        return w == 4 ? (const void *)kq_mfma_kernel<true, 4, true> : (const void *)kq_mfma_kernel<true, 8, true>;
+    return w == 16 ? (const void *)kq_mfma_kernel<true, 16> : (const void *)kq_mfma_kernel<true, 8>;
+}
+
+// The last-level cache (MALL) of MI355X.  A launch whose x, q and s together
+// exceed it streams its codes past the caches (nontemporal stores): no later
+// kernel could find them there anyway.
+constexpr int64_t kMallBytes = (int64_t)256 << 20;
+
+// Token grouping for strip width w: tiles per workgroup, interleaved or
+// contiguous groups, flat or XCD-grouped order.
+void mfma_groups(int64_t M, int64_t d, int w, bool adaln, const Tuning &tn, MfmaShape &sh)
+{
+    const int64_t nB = d / 32;
+    const int64_t nBG = (nB + w - 1) / w;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const void *fn;
-    if constexpr (kAd)
-        fn = (const void *)kq_mfma_kernel<true, kW, true>;
-    else
-        fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW>;
-    const int64_t resident = mfma_wgs_per_xcd(fn, 64 * kW); // per XCD
-    int tpw = tuning().mfma_tiles_per_wave > 256 ? 256 : tuning().mfma_tiles_per_wave;
-    int interleave = tuning().mfma_interleave == 2 ? 1 : 0;
-    bool flat = tuning().mfma_order == 2;
-    if (tpw <= 0 && tuning().mfma_order == 0 && tuning().mfma_interleave != 1) {
+    const int64_t resident = mfma_wgs_per_xcd(mfma_shape_fn(w, adaln), 64 * w);
+    int64_t tpw = tn.mfma_tiles_per_wg;
+    int interleave = tn.mfma_groups == 2 ? 1 : 0;
+    bool flat = tn.mfma_order == 2;
+    if (tpw <= 0 && tn.mfma_order == 0 && tn.mfma_groups != 1) {
         // When XCD-grouped token groups would fill under 80% of the resident
         // workgroup slots (strips per row not a good divisor of the slots per
         // XCD: e.g. 35 strips against 64 slots), deal (group, strip) pairs in
@@ -710,7 +741,7 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
         if (groups_f >= 1 && 5 * (gx < 1 ? 1 : gx) * nBG < 4 * resident) {
             const int64_t t1f = (nTiles + groups_f - 1) / groups_f;
             if (t1f >= 3 && t1f <= 16) {
-                tpw = (int)t1f;
+                tpw = t1f;
                 interleave = 1;
                 flat = true;
             }
@@ -736,11 +767,11 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
             gx = 1;
         const int64_t t1 = (nTiles + gx * kXcds - 1) / (gx * kXcds);
         const int64_t wgs6 = ((nTiles + 5) / 6 + kXcds - 1) / kXcds * kXcds * nBG;
-        if (tuning().mfma_interleave != 1 && t1 == 3 && 10 * wgs6 >= 9 * (int64_t)num_cus()) {
+        if (tn.mfma_groups != 1 && t1 == 3 && 10 * wgs6 >= 9 * (int64_t)device_cus()) {
             tpw = 6;
             interleave = 0;
-        } else if (tuning().mfma_interleave != 1 && t1 >= 3 && t1 <= 12) {
-            tpw = (int)t1;
+        } else if (tn.mfma_groups != 1 && t1 >= 3 && t1 <= 12) {
+            tpw = t1;
             interleave = 1;
         } else if (t1 < 3) {
             tpw = 3;
@@ -751,83 +782,123 @@ static hipError_t launch_kq_mfma_w(const uint16_t *x, int64_t M, int64_t d, cons
             tpw = rounds4 >= 4 ? 4 : 6;
             interleave = 0;
         }
-        if (tuning().mfma_interleave == 2)
+        if (tn.mfma_groups == 2)
             interleave = 1;
     }
     const int64_t nG = (nTiles + tpw - 1) / tpw;
     // XCD-grouped: token groups dealt to the XCDs in turn, padded to a multiple of 8
     const int64_t nGpad = flat ? nG : (nG + kXcds - 1) / kXcds * kXcds;
-    const int64_t grid = nGpad * nBG;
-    if (grid > 0x7FFFFFFF)
+    sh.strip = w;
+    sh.tiles_per_wg = (int)tpw;
+    sh.interleave = interleave;
+    sh.flat = flat ? 1 : 0;
+    sh.grid = nGpad * nBG;
+}
+
+template <int kW, bool kAd, bool kNT>
+hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
+                                uint8_t *q, uint8_t *s, float *y, int lu, const MfmaShape &sh, hipStream_t stream,
+                                AdArgs ad)
+{
+    if (sh.grid > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
+    const void *fn;
+    if constexpr (kAd)
+        fn = (const void *)kq_mfma_kernel<true, kW, true>;
+    else
+        fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW, false, kNT>;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
-    int nbg = nBG;
-    int order = (interleave ? 1 : 0) | (flat ? 2 : 0);
-    void *args_q[] = {(void *)&x,   (void *)&M,   (void *)&di,  (void *)&factors, (void *)&per_block, (void *)&q,
-                      (void *)&s,   (void *)&y,   (void *)&nbg, (void *)&tpw,     (void *)&order,     (void *)&lu,
-                      (void *)&ad};
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64 * kW), args_q, 0, stream);
+    int nbg = (int)((d / 32 + kW - 1) / kW);
+    int tpw = sh.tiles_per_wg;
+    int order = (sh.interleave ? 1 : 0) | (sh.flat ? 2 : 0);
+    void *args[] = {(void *)&x,   (void *)&M,   (void *)&di,  (void *)&factors, (void *)&per_block, (void *)&q,
+                    (void *)&s,   (void *)&y,   (void *)&nbg, (void *)&tpw,     (void *)&order,     (void *)&lu,
+                    (void *)&ad};
+    return hipLaunchKernel(fn, dim3((unsigned)sh.grid), dim3(64 * kW), args, 0, stream);
+}
+
+} // namespace
+
+hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln, MfmaShape &sh)
+{
+    const int64_t nB = d / 32;
+    int w;
+    if (adaln) {
+        // The normalisation takes the registers of a lane to about 180 VGPRs
+        // (two waves per SIMD), so 16-block strips (1024 threads, at most 128
+        // VGPRs) are not offered.  Strips of 4 blocks when they divide the row
+        // and strips of 8 do not (measured at 8192 x 1152: 18.95 against 19.83
+        // us for the whole front-end; strips of 8 were as fast or faster at
+        // 2048 x 2240 and 4608 x 3072).
+        w = tn.adaln_strip;
+        if (w != 4 && w != 8)
+            w = (nB % 4 == 0 && nB % 8 != 0) ? 4 : 8;
+    } else {
+        // Strips of 16 blocks (16 waves, 1 KB of each row per workgroup, 85 KB
+        // of LDS, one workgroup per CU) read and write HBM in longer runs than
+        // strips of 8, which pays when the whole launch is one resident round
+        // of interleaved token groups (measured: 8192 x 4608, 18.3 us against
+        // 19.8).  Over several rounds the lone workgroup per CU leaves its CU
+        // idle between workgroups, and strips of 8 (two per CU) win.  They are
+        // used only when they divide the row exactly, so no wave idles.
+        w = tn.mfma_strip;
+        if (w != 8 && w != 16) {
+            w = 8;
+            if (nB % 16 == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups != 1) {
+                int64_t gx = mfma_wgs_per_xcd(mfma_shape_fn(16, false), 64 * 16) / (nB / 16);
+                if (gx < 1)
+                    gx = 1;
+                const int64_t nTiles = (M + kTileT - 1) / kTileT;
+                const int64_t t1 = (nTiles + gx * kXcds - 1) / (gx * kXcds);
+                if (t1 >= 3 && t1 <= 12)
+                    w = 16;
+            }
+        }
+    }
+    mfma_groups(M, d, w, adaln, tn, sh);
+    const double footprint = (double)M * (double)d * (2.0 + 0.5 + 1.0 / 32.0);
+    sh.nt_codes = !adaln && (tn.code_stores == 2 || (tn.code_stores == 0 && footprint > (double)kMallBytes));
+    return sh.grid > 0x7FFFFFFF ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                          uint8_t *s, float *y, int lu, hipStream_t stream)
+                          uint8_t *s, float *y, int lu, const Tuning &tn, hipStream_t stream)
 {
-    // Strips of 16 blocks (16 waves, 1 KB of each row per workgroup, 85 KB of
-    // LDS, one workgroup per CU) read and write HBM in longer runs than strips
-    // of 8, which pays when the whole launch is one resident round of
-    // interleaved token groups (measured: 8192 x 4608, 18.3 us against 19.8).
-    // Over several rounds the lone workgroup per CU leaves its CU idle
-    // between workgroups, and strips of 8 (two per CU) win.  They are used
-    // only when they divide the row exactly, so no wave idles.
-    const int64_t nB = d / 32;
-    int w = tuning().mfma_strip;
-    if (w != 8 && w != 16) {
-        w = 8;
-        if (nB % 16 == 0 && tuning().mfma_tiles_per_wave <= 0 && tuning().mfma_interleave != 1) {
-            const void *fn16 = y ? (const void *)kq_mfma_kernel<false, 16> : (const void *)kq_mfma_kernel<true, 16>;
-            int64_t gx = mfma_wgs_per_xcd(fn16, 64 * 16) / (nB / 16);
-            if (gx < 1)
-                gx = 1;
-            const int64_t nTiles = (M + kTileT - 1) / kTileT;
-            const int64_t t1 = (nTiles + gx * kXcds - 1) / (gx * kXcds);
-            if (t1 >= 3 && t1 <= 12)
-                w = 16;
-        }
-    }
-    if (w == 16)
-        return launch_kq_mfma_w<16>(x, M, d, factors, nT, q, s, y, lu, stream);
-    return launch_kq_mfma_w<8>(x, M, d, factors, nT, q, s, y, lu, stream);
+    MfmaShape sh;
+    hipError_t e = mfma_launch_shape(M, d, tn, false, sh);
+    if (e != hipSuccess)
+        return e;
+    const AdArgs ad{};
+    if (sh.strip == 16)
+        return sh.nt_codes && !y ? launch_mfma_instance<16, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                                 : launch_mfma_instance<16, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+    return sh.nt_codes && !y ? launch_mfma_instance<8, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                             : launch_mfma_instance<8, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
 }
 
 // Second pass of the AdaLN front-end on the matrix cores: the quantizer's
 // launch shape with h in place of x, normalised at staging.
 hipError_t launch_adaln_mfma(const uint16_t *h, int64_t M, int64_t d, const double *stats, const float *shift,
                              const float *scale, int64_t T, const float *factors, int64_t nT, uint8_t *q, uint8_t *s,
-                             hipStream_t stream)
+                             const Tuning &tn, hipStream_t stream)
 {
-    // The normalisation takes the registers of a lane to about 180 VGPRs (two
-    // waves per SIMD), so 16-block strips (1024 threads, at most 128 VGPRs)
-    // are not offered.  Strips of 4 blocks when they divide the row and
-    // strips of 8 do not (measured at 8192 x 1152: 18.95 against 19.83 us for
-    // the whole front-end; strips of 8 were as fast or faster at 2048 x 2240
-    // and 4608 x 3072).
+    MfmaShape sh;
+    hipError_t e = mfma_launch_shape(M, d, tn, true, sh);
+    if (e != hipSuccess)
+        return e;
     const AdArgs ad{stats, shift, scale, T};
-    const int64_t nB = d / 32;
-    int w = tuning().adaln_strip;
-    if (w != 4 && w != 8)
-        w = (nB % 4 == 0 && nB % 8 != 0) ? 4 : 8;
-    if (w == 4)
-        return launch_kq_mfma_w<4, true>(h, M, d, factors, nT, q, s, nullptr, 0, stream, ad);
-    return launch_kq_mfma_w<8, true>(h, M, d, factors, nT, q, s, nullptr, 0, stream, ad);
+    if (sh.strip == 4)
+        return launch_mfma_instance<4, true, false>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
+    return launch_mfma_instance<8, true, false>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,
-                                uint8_t *q, uint8_t *s, float *y, int rows_knob, hipStream_t stream)
+                                uint8_t *q, uint8_t *s, float *y, const Tuning &tn, hipStream_t stream)
 {
     const int nOct = (int)(d / 8);
     const int nCT = (nOct + 63) / 64;
-    int R = rows_knob > 256 ? 256 : rows_knob;
+    int R = tn.stream_rows_per_wave > 256 ? 256 : tn.stream_rows_per_wave;
     if (R <= 0)
         R = 4; // short-lived waves (one pipeline stage of rows each) keep the most loads in flight
 
@@ -854,33 +925,33 @@ static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, c
 }
 
 hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
-                               uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
+                               uint8_t *q, uint8_t *s, float *y, const Tuning &tn, hipStream_t stream)
 {
-    return launch_stream(y ? kBflyT : kBflyQ, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y,
-                         tuning().bfly_rows_per_wave, stream);
+    return launch_stream(y ? kBflyT : kBflyQ, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 
 hipError_t launch_kq16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
-                       uint8_t *s, float *y, hipStream_t stream)
+                       uint8_t *s, float *y, const Tuning &tn, hipStream_t stream)
 {
-    return launch_stream(y ? kBfly16T : kBfly16Q, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y,
-                         tuning().bfly_rows_per_wave, stream);
+    return launch_stream(y ? kBfly16T : kBfly16Q, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 
 hipError_t launch_sq(const uint16_t *x, int64_t M, int64_t d, const float *scale, uint8_t *q, uint8_t *s,
-                     hipStream_t stream)
+                     const Tuning &tn, hipStream_t stream)
 {
-    return launch_stream(kSQ, x, M, d, scale, 0, q, s, nullptr, tuning().stream_rows_per_wave, stream);
+    return launch_stream(kSQ, x, M, d, scale, 0, q, s, nullptr, tn, stream);
 }
 
-hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, hipStream_t stream)
+hipError_t launch_mx_f32(const float *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, const Tuning &tn,
+                         hipStream_t stream)
 {
-    return launch_stream(kMXF32, x, M, d, nullptr, 0, q, s, nullptr, tuning().stream_rows_per_wave, stream);
+    return launch_stream(kMXF32, x, M, d, nullptr, 0, q, s, nullptr, tn, stream);
 }
 
-hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, hipStream_t stream)
+hipError_t launch_fwht(const uint16_t *x, int64_t M, int64_t d, uint8_t *q, uint8_t *s, float *y, const Tuning &tn,
+                       hipStream_t stream)
 {
-    return launch_stream(y ? kFwhtT : kFwhtQ, x, M, d, nullptr, 0, q, s, y, tuning().stream_rows_per_wave, stream);
+    return launch_stream(y ? kFwhtT : kFwhtQ, x, M, d, nullptr, 0, q, s, y, tn, stream);
 }
 
 } // namespace kq

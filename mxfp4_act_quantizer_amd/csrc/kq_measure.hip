@@ -1,11 +1,19 @@
-// Measurement-only export (not part of the quantizer API in kroquant.h): a
-// plain streaming copy with the quantizer's 4:1 read:write footprint, which
-// the benchmark times next to the quantizer as the practical HBM ceiling of
-// a kernel that reads 2 bytes and writes 0.5 bytes per element.
+// Measurement-only export (declared in the measurement section of
+// kroquant.h): streaming copies with the quantizer's 4:1 read:write footprint
+// (2 bytes read and 0.5 byte written per activation element), which the
+// benchmark times next to the quantizer as the practical HBM ceiling of such
+// a kernel.  Each 16-byte piece read yields one 4-byte word written (the xor of
+// its four words, so no read can be optimised away).
 //
-// Each lane reads 16 bytes (nontemporal) and writes one 4-byte word (the xor
-// of the four words read, nontemporal), grid-stride, four reads in flight per
-// lane.  src_bytes / 4 bytes are written to dst.
+// Forms (all read with nontemporal 16-byte loads; P = 16-byte pieces):
+//   chunked:  wave w owns pieces [w*64*U, (w+1)*64*U): U loads of 1 KB per
+//             wave in flight, then U stores of 256 B (4 bytes per lane); the
+//             grid covers the input once (short-lived waves, like the
+//             streaming quantizers)
+//   wide:     a lane reads 4 consecutive pieces (64 bytes) per step and
+//             writes one 16-byte word, so the stores are 1 KB per wave
+//   stride:   grid-stride loop over 2048 workgroups, U pieces in flight per lane
+//   persist:  one wave per resident slot walks chunks chunk = wave + k * waves
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,41 +22,108 @@
 namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kUnroll = 4;
-constexpr int kGrid = 2048; // workgroups of 256 lanes (a sweep of 1024..8192 on MI355X put 2048 at the top)
 
-__global__ __launch_bounds__(256) void copy41_kernel(const u32x4 *__restrict__ in, int64_t n16,
+__device__ __forceinline__ unsigned fold(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
+
+template <bool kNT>
+__device__ __forceinline__ void put(unsigned *p, unsigned v)
+{
+    if constexpr (kNT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+// chunked / persistent: U loads of 1 KB per wave, then U stores of 256 B
+template <int U, bool kNT, bool kPersist>
+__global__ __launch_bounds__(256) void copy41_chunked(const u32x4 *__restrict__ in, int64_t n16,
+                                                      unsigned *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t waves = kPersist ? (int64_t)gridDim.x * 4 : 1;
+    const int64_t chunk = 64 * U;
+    for (int64_t w = wave0; w * chunk < n16; w += waves) {
+        const int64_t base = w * chunk + lane;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = base + 64 * u;
+            v[u] = p < n16 ? __builtin_nontemporal_load(&in[p]) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = base + 64 * u;
+            if (p < n16)
+                put<kNT>(&out[p], fold(v[u]));
+        }
+        if (!kPersist)
+            break;
+    }
+}
+
+// wide: lane reads pieces 4j .. 4j+3 (64 contiguous bytes) and writes word j of
+// 16 bytes; U such steps per wave
+template <int U>
+__global__ __launch_bounds__(256) void copy41_wide(const u32x4 *__restrict__ in, int64_t n16, u32x4 *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n64 = n16 / 4; // n16 is a multiple of 64
+    u32x4 v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t j = (w * U + u) * 64 + lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[u][k] = j < n64 ? __builtin_nontemporal_load(&in[4 * j + k]) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t j = (w * U + u) * 64 + lane;
+        if (j < n64)
+            __builtin_nontemporal_store(u32x4{fold(v[u][0]), fold(v[u][1]), fold(v[u][2]), fold(v[u][3])}, &out[j]);
+    }
+}
+
+// grid-stride: 2048 workgroups, U pieces in flight per lane
+template <int U>
+__global__ __launch_bounds__(256) void copy41_stride(const u32x4 *__restrict__ in, int64_t n16,
                                                      unsigned *__restrict__ out)
 {
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-        u32x4 v[kUnroll];
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             v[u] = __builtin_nontemporal_load(&in[i + u * stride]);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            __builtin_nontemporal_store(v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3], &out[i + u * stride]);
+        for (int u = 0; u < U; ++u)
+            __builtin_nontemporal_store(fold(v[u]), &out[i + u * stride]);
     }
-    for (; i < n16; i += stride) {
-        const u32x4 v = __builtin_nontemporal_load(&in[i]);
-        __builtin_nontemporal_store(v[0] ^ v[1] ^ v[2] ^ v[3], &out[i]);
-    }
+    for (; i < n16; i += stride)
+        __builtin_nontemporal_store(fold(__builtin_nontemporal_load(&in[i])), &out[i]);
+}
+
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+        n = 256;
+    return n;
 }
 
 } // namespace
 
 extern "C" {
 
-// src: device, 16-byte aligned, src_bytes a multiple of 16; dst: device,
-// 4-byte aligned, src_bytes / 4 bytes, not overlapping src.  One launch on
-// `stream`.  Returns KQ_OK, KQ_ERR_ARG, KQ_ERR_ALIGN, KQ_ERR_OVERLAP or KQ_ERR_HIP.
-int kq_measure_copy41(const void *src, int64_t src_bytes, void *dst, void *stream)
+int kq_measure_copy41(const void *src, int64_t src_bytes, void *dst, int form, void *stream)
 {
-    if (!src || !dst || src_bytes < 0 || src_bytes % 16)
+    if (!src || !dst || src_bytes < 0 || src_bytes % 1024 || form < 0 || form >= KQ_COPY_FORMS)
         return KQ_ERR_ARG;
-    if (((uintptr_t)src & 15) || ((uintptr_t)dst & 3))
+    if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
         return KQ_ERR_ALIGN;
     const uintptr_t a0 = (uintptr_t)src, a1 = a0 + (uintptr_t)src_bytes;
     const uintptr_t b0 = (uintptr_t)dst, b1 = b0 + (uintptr_t)(src_bytes / 4);
@@ -57,15 +132,39 @@ int kq_measure_copy41(const void *src, int64_t src_bytes, void *dst, void *strea
     if (src_bytes == 0)
         return KQ_OK;
     const int64_t n16 = src_bytes / 16;
-    const int64_t need = (n16 + 255) / 256;
-    const unsigned grid = (unsigned)(need < kGrid ? need : kGrid);
     const u32x4 *in = (const u32x4 *)src;
     unsigned *out = (unsigned *)dst;
+    u32x4 *out16 = (u32x4 *)dst;
+    hipStream_t hs = (hipStream_t)stream;
+    auto waves_for = [&](int64_t pieces_per_wave) { return (n16 + pieces_per_wave - 1) / pieces_per_wave; };
+    auto grid_for = [&](int64_t waves) { return (waves + 3) / 4; };
+    int64_t grid = 0;
+    const void *fn = nullptr;
+    switch (form) {
+    case 0: fn = (const void *)copy41_chunked<8, true, false>; grid = grid_for(waves_for(64 * 8)); break;
+    case 1: fn = (const void *)copy41_chunked<8, false, false>; grid = grid_for(waves_for(64 * 8)); break;
+    case 2: fn = (const void *)copy41_chunked<4, true, false>; grid = grid_for(waves_for(64 * 4)); break;
+    case 3: fn = (const void *)copy41_wide<2>; grid = grid_for(waves_for(64 * 4 * 2)); break;
+    case 4: {
+        fn = (const void *)copy41_chunked<8, true, true>;
+        const int64_t slots = (int64_t)device_cus() * 8; // 8 workgroups of 4 waves per CU
+        const int64_t need = grid_for(waves_for(64 * 8));
+        grid = need < slots ? need : slots;
+        break;
+    }
+    default: {
+        fn = (const void *)copy41_stride<4>;
+        const int64_t need = (n16 + 255) / 256;
+        grid = need < 2048 ? need : 2048;
+        break;
+    }
+    }
+    if (grid > 0x7FFFFFFF)
+        return KQ_ERR_SHAPE;
+    void *args_w[] = {(void *)&in, (void *)&n16, (void *)&out16};
     void *args[] = {(void *)&in, (void *)&n16, (void *)&out};
-    return hipLaunchKernel((const void *)copy41_kernel, dim3(grid), dim3(256), args, 0, (hipStream_t)stream) ==
-                   hipSuccess
-               ? KQ_OK
-               : KQ_ERR_HIP;
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), form == 3 ? args_w : args, 0, hs);
+    return e == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
 } // extern "C"

@@ -7,6 +7,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from oracle import oracle as O
+from tests import parity as P
 
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
@@ -113,3 +114,53 @@ def fwht_z(x):
 
     _run(M, job)
     return z
+
+
+def compare_kq_rows(x, f, qg, sg, rows=1024, progress=None, lu=False):
+    """Every row of a GPU result (qg, sg) against the oracle under the flag
+    rules of tests/parity.py, in row chunks on host threads (memory stays
+    bounded at any M).  Returns the summed counts of parity.compare."""
+    M = x.shape[0]
+    chunks = [(a, min(M, a + rows)) for a in range(0, M, rows)]
+    quant = O.kq_quantize_lu if lu else O.kq_quantize
+    transform = O.kq_transform_lu if lu else O.kq_transform
+
+    def job(rr):
+        a, b = rr
+        xc = np.ascontiguousarray(x[a:b])
+        qr, sr, y32 = quant(xc, f, want_y32=True)
+        z = transform(xc, f)[1]
+        ef, bf = P.boundary_flags(z, y32)
+        return P.compare(qg[a:b], sg[a:b], qr, sr, ef, bf)
+
+    tot = None
+    done = 0
+    with ThreadPoolExecutor(THREADS) as ex:
+        for r in ex.map(job, chunks):
+            if tot is None:
+                tot = dict(r)
+            else:
+                for k, v in r.items():
+                    tot[k] = (tot[k] and v) if k == "ok" else tot[k] + v
+            done += 1
+            if progress and done % 16 == 0:
+                progress(f"    {done}/{len(chunks)} chunks")
+    return tot
+
+
+def transform_rows_error(x, f, y_gpu, rows=1024):
+    """(max |y_gpu - y| / z, elements outside 2e-6 z + TOL_ABS) over every row,
+    y the oracle's exact transform, in row chunks on host threads."""
+    M = x.shape[0]
+    chunks = [(a, min(M, a + rows)) for a in range(0, M, rows)]
+
+    def job(rr):
+        a, b = rr
+        y, z = O.kq_transform(np.ascontiguousarray(x[a:b]), f)
+        return P.transform_error(y_gpu[a:b], y, z)
+
+    worst, bad = 0.0, 0
+    with ThreadPoolExecutor(THREADS) as ex:
+        for w, n in ex.map(job, chunks):
+            worst, bad = max(worst, w), bad + n
+    return worst, bad

@@ -42,14 +42,16 @@ def test_status_strings():
 
 
 def test_copy_ceiling_validation():
-    # the benchmark's measurement copy checks its arguments before any HIP call
+    # the benchmark's measurement copies check their arguments before any HIP call
     L = K.lib()
-    assert L.kq_measure_copy41(FAKE, 0, FAKE + (1 << 30), None) == K.KQ_OK
-    assert L.kq_measure_copy41(None, 64, FAKE, None) == K.KQ_ERR_ARG
-    assert L.kq_measure_copy41(FAKE, 24, FAKE + (1 << 30), None) == K.KQ_ERR_ARG
-    assert L.kq_measure_copy41(FAKE + 4, 64, FAKE + (1 << 30), None) == K.KQ_ERR_ALIGN
-    assert L.kq_measure_copy41(FAKE, 64, FAKE + (1 << 30) + 1, None) == K.KQ_ERR_ALIGN
-    assert L.kq_measure_copy41(FAKE, 64, FAKE + 32, None) == K.KQ_ERR_OVERLAP
+    assert L.kq_measure_copy41(FAKE, 0, FAKE + (1 << 30), 0, None) == K.KQ_OK
+    assert L.kq_measure_copy41(None, 1024, FAKE, 0, None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE, 1000, FAKE + (1 << 30), 0, None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE, 1024, FAKE + (1 << 30), -1, None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE, 1024, FAKE + (1 << 30), K.KQ_COPY_FORMS, None) == K.KQ_ERR_ARG
+    assert L.kq_measure_copy41(FAKE + 4, 1024, FAKE + (1 << 30), 0, None) == K.KQ_ERR_ALIGN
+    assert L.kq_measure_copy41(FAKE, 1024, FAKE + (1 << 30) + 4, 0, None) == K.KQ_ERR_ALIGN
+    assert L.kq_measure_copy41(FAKE, 1024, FAKE + 32, 0, None) == K.KQ_ERR_OVERLAP
 
 
 def test_hip_error_detail_without_gpu():
@@ -99,10 +101,11 @@ def test_kq_validation():
 def test_transform_and_sq_mx_validation():
     y, f, x, sc = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
     q, s = FAKE + (4 << 30), FAKE + (5 << 30)
-    assert raw("kq_transform_f32", x, 4, 64, f, 2, y + 4, 1, None) == K.KQ_ERR_ALIGN
-    assert raw("kq_transform_f32", x, 4, 64, f, 5, y, 1, None) == K.KQ_ERR_SHAPE
-    assert raw("kq_transform_f32", x, 4, 64, f, 2, x + 16, 1, None) == K.KQ_ERR_OVERLAP
-    assert raw("kq_transform_f32", x, 4, 64, f, 2, y, 9, None) == K.KQ_ERR_ARG
+    assert raw("kq_transform_f32", x, 4, 64, f, 2, y + 4, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_transform_f32", x, 4, 64, f, 5, y, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_transform_f32", x, 4, 64, f, 2, x + 16, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_transform_tuned", x, 4, 64, f, 2, y, 9, None, None) == K.KQ_ERR_ARG  # variant
+    assert raw("kq_transform_tuned", x, 4, 64, f, 2, y + 4, 1, None, None) == K.KQ_ERR_ALIGN
     assert raw("sq_quantize", x, 4, 96, None, q, s, None) == K.KQ_ERR_ARG
     assert raw("sq_quantize", x, 4, 96, sc + 1, q, s, None) == K.KQ_ERR_ALIGN
     assert raw("sq_quantize", x, 4, 100, sc, q, s, None) == K.KQ_ERR_SHAPE
@@ -353,13 +356,60 @@ def test_kq16_validation():
     assert raw("kq_transform16_f32", x, 4, 48, f, 3, y + 4, None) == K.KQ_ERR_ALIGN
 
 
-def test_tuning_keys():
-    # the launch-shape knobs: keys 0..9 are accepted (and reset to automatic),
-    # anything else is refused; no HIP call is made
-    L = K.lib()
-    for key in range(10):
-        assert L.kq_set_tuning(key, 0) == K.KQ_OK
-    for key in (-1, 10, 100):
-        assert L.kq_set_tuning(key, 0) == K.KQ_ERR_ARG
-    with pytest.raises(K.KQError):
-        K.set_tuning(10, 1)
+def test_tuning_validation():
+    # launch-shape overrides travel as an argument; out-of-range fields are
+    # refused before any HIP call, and nothing is kept between calls
+    import ctypes
+    x, q, s, f, y = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+    bad = [("mfma_tiles_per_wg", 257), ("mfma_tiles_per_wg", -1), ("mfma_groups", 3), ("mfma_strip", 12),
+           ("mfma_order", 3), ("code_stores", 3), ("stream_rows_per_wave", 300), ("gemm_kernel", 4),
+           ("adaln_pass", 3), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000)]
+    for field, val in bad:
+        t = ctypes.byref(K.Tuning(**{field: val}))
+        assert raw("kq_quantize_tuned", x, 4, 64, f, 1, q, s, 0, t, None) == K.KQ_ERR_ARG, field
+        assert raw("kq_transform_tuned", x, 4, 64, f, 1, y, 0, t, None) == K.KQ_ERR_ARG, field
+        assert raw("mx_gemm_tuned", q, s, 4, q, s, 4, 64, y, 0, t, None) == K.KQ_ERR_ARG, field
+        shape = (ctypes.c_int64 * 6)()
+        assert raw("kq_launch_shape", 4, 64, 0, t, shape) == K.KQ_ERR_ARG, field
+    ok = ctypes.byref(K.Tuning(mfma_strip=16, code_stores=2, gemm_kernel=3))
+    # a valid override still fails the other checks first (no GPU is touched)
+    assert raw("kq_quantize_tuned", x + 2, 4, 64, f, 1, q, s, 0, ok, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_quantize_tuned", x, 0, 64, f, 1, q, s, 0, ok, None) == K.KQ_OK
+    assert raw("kq_launch_shape", 4, 48, 0, None, (ctypes.c_int64 * 6)()) == K.KQ_ERR_SHAPE
+    assert raw("kq_launch_shape", 4, 64, 2, None, (ctypes.c_int64 * 6)()) == K.KQ_ERR_ARG
+    assert raw("kq_launch_shape", 4, 64, 0, None, None) == K.KQ_ERR_ARG
+    with pytest.raises(ValueError):
+        K.kq_launch_shape(4, 64, tuning={"no_such_field": 1})
+    assert not hasattr(K.lib(), "kq_set_tuning")
+
+
+def test_sizes_near_int64_max_are_shape_errors():
+    # block counts and byte sizes are bounded by quotient, so huge M is a shape
+    # error, never a wrapped product that reaches the launch
+    big = (1 << 63) - 1
+    x, q, s, f, y = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+    for M in (big, big // 2, (1 << 40) // 36 + 1, 1 << 62):
+        assert raw("kq_quantize", x, M, 1152, f, 1, q, s, None) == K.KQ_ERR_SHAPE, M
+        assert raw("sq_quantize", x, M, 1152, f, q, s, None) == K.KQ_ERR_SHAPE, M
+        assert raw("mx_quantize_f32", x, M, 1152, q, s, None) == K.KQ_ERR_SHAPE, M
+        assert raw("kq_transform_f32", x, M, 1152, f, 1, y, None) == K.KQ_ERR_SHAPE, M
+        assert raw("kq_quantize16", x, M, 1152, f, 1, q, s, None) == K.KQ_ERR_SHAPE, M
+        assert raw("fwht_quantize", x, M, 1152, q, s, None) == K.KQ_ERR_SHAPE, M
+        assert raw("mx_gemm", q, s, M, q, s, 64, 64, y, 0, None) == K.KQ_ERR_SHAPE, M
+        assert raw("kq_adaln_quantize", x, M, 1152, f, f, 1, ctypes_float(1e-6), f, 1, y, q, s, None) \
+            == K.KQ_ERR_SHAPE, M
+    # the largest accepted block count still passes the shape check (it then
+    # fails on the null pointer, before any HIP call)
+    M = (1 << 40) // 36
+    assert raw("kq_quantize", None, M, 1152, f, 1, q, s, None) == K.KQ_ERR_ARG
+    # tokens_per_sample near INT64_MAX: ceil(M / T) is formed without
+    # overflow, so the [1, d] modulation rows still have their true size and a
+    # workspace placed inside them is caught
+    h, sh, sc, q2, s2 = (FAKE + (i << 32) for i in range(5))
+    assert raw("kq_adaln_quantize", h, 4, 64, sh, sc, big, ctypes_float(1e-6), f, 1, sh + 128, q2, s2,
+               None) == K.KQ_ERR_OVERLAP
+
+
+def ctypes_float(v):
+    import ctypes
+    return ctypes.c_float(v)

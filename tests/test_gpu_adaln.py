@@ -140,10 +140,11 @@ def test_adaln_special_rows(K):
     assert np.array_equal(xg[0], xb[0])
 
 
-# launch knobs of kq_adaln_quantize: 8 selects the second pass (1 matrix
-# cores, 2 butterfly), 9 the matrix-core strip width (4 or 8 blocks)
-PASS_FORMS = [("mfma_strip4", {8: 1, 9: 4}, None), ("mfma_strip8", {8: 1, 9: 8}, None),
-              ("butterfly", {8: 2}, "KQ_VARIANT_BUTTERFLY")]
+# launch-shape overrides of kq_adaln_quantize: the second pass (1 matrix
+# cores, 2 butterfly) and the matrix-core strip width (4 or 8 blocks)
+PASS_FORMS = [("mfma_strip4", {"adaln_pass": 1, "adaln_strip": 4}, None),
+              ("mfma_strip8", {"adaln_pass": 1, "adaln_strip": 8}, None),
+              ("butterfly", {"adaln_pass": 2}, "KQ_VARIANT_BUTTERFLY")]
 FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300, 96, 1), (4100, 3072, 2048)]
 
 
@@ -151,10 +152,8 @@ FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300
 def test_adaln_second_pass_forms(K, form, knobs, variant):
     # every second-pass form equals the unfused pipeline through the matching
     # quantizer bit for bit, on ragged rows, sample boundaries inside tiles and
-    # several widths; the knobs are reset afterwards
-    try:
-        for key, val in knobs.items():
-            K.set_tuning(key, val)
+    # several widths
+    if True:
         for M, d, T in FORM_CASES:
             seed = 8400 + M + d
             say(f"[adaln form {form}] M={M} d={d} T={T} seed={seed}")
@@ -162,7 +161,7 @@ def test_adaln_second_pass_forms(K, form, knobs, variant):
             shift, scale = I.adaln_modulation((M + T - 1) // T, d, seed + 1)
             hd, sh, sc = dev_bf16(h), dev_f32(shift), dev_f32(scale)
             fd = dev_f32(I.random_factors(d // 32, seed + 2))
-            q, s = K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd)
+            q, s = K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd, tuning=knobs)
             x = K.adaln_modulate(hd, sh, sc, T, EPS)
             if variant is None:
                 q2, s2 = K.kq_quantize(x, fd)
@@ -170,9 +169,6 @@ def test_adaln_second_pass_forms(K, form, knobs, variant):
                 q2, s2 = K.kq_quantize(x, fd, variant=getattr(K, variant))
             torch.cuda.synchronize()
             assert torch.equal(q, q2) and torch.equal(s, s2), f"{form} {M}x{d}: fused != unfused"
-    finally:
-        for key in knobs:
-            K.set_tuning(key, 0)
 
 
 def test_adaln_stats_workspace(K):

@@ -1,11 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (the library's automatic launch shapes).
 
-Configurations 1-4 and the 4096-row sweep are compared against the oracle on
-every row (the oracle runs on host threads over row chunks).  The 16384- and
-65536-row sweeps compare sampled rows against the oracle, plus properties that
-hold at any size: identity factors give exactly the plain MXFP4 of the input,
-and a replicated per-block factor layout gives exactly the shared-set result.
+Every configuration, the 16384- and 65536-row sweeps included, is compared
+against the oracle on every row (the oracle runs on host threads over row
+chunks).  Properties that hold at any size are checked as well: identity
+factors give exactly the plain MXFP4 of the input, a replicated per-block
+factor layout gives exactly the shared-set result, and the transform export
+(same launch shape as the quantizer) re-encoded by the fp32 quantizer gives
+exactly the quantizer's codes and scales.
 """
 import sys
 
@@ -85,27 +87,27 @@ def test_sq_full_config_bit_exact(K, name):
     assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0
 
 
+@pytest.mark.timeout(1800)
 @pytest.mark.parametrize("name", ["sweep_4096", "sweep_16384", "sweep_65536"])
 def test_sweep_identity_hadamard(K, name):
     M, d, _ = I.CONFIGS[name]
     say(f"[sweep {name}] generating M={M} d={d}")
     x, _, specials = I.act_sweep_special(M, d, I.data_seed(name))
     xd = to_dev(x)
-    del x
-    rng = np.random.default_rng(M)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(M - 8, M), rng.choice(M, 112, replace=False),
-                                     specials[rng.choice(len(specials), 64, replace=False), 0]]))
-    xs = xd[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    say(f"[sweep {name}] launch shape {K.kq_launch_shape(M, d)}")
 
-    # identity: bit-exact plain MXFP4, at full size against the fp32 quantizer on the GPU
+    # identity: bit-exact plain MXFP4, against the fp32 quantizer on the GPU
+    # and against the oracle on every row
     say(f"[sweep {name}] identity nT=1 and nT={d // 32}")
     qi, si = kq_gpu(K, xd, I.identity_factors(1))
     q32, s32 = K.mx_quantize_f32(xd.float())
     torch.cuda.synchronize()
     assert np.array_equal(qi, q32.cpu().numpy()) and np.array_equal(si, s32.cpu().numpy())
     del q32, s32
-    qir, sir = O.kq_quantize(xs, I.identity_factors(1))
-    assert np.array_equal(qi[rows], qir) and np.array_equal(si[rows], sir)
+    torch.cuda.empty_cache()
+    res = OM.compare_kq_rows(x, I.identity_factors(1), qi, si, progress=say)
+    say(f"    identity, every row: {res}")
+    assert res["code_mismatch"] == 0 and res["scale_mismatch"] == 0
     qb, sb = kq_gpu(K, xd, I.identity_factors(d // 32))
     assert np.array_equal(qb, qi) and np.array_equal(sb, si)
     del qb, sb, qi, si
@@ -116,25 +118,106 @@ def test_sweep_identity_hadamard(K, name):
     qh, sh = kq_gpu(K, xd, h)
     qhb, shb = kq_gpu(K, xd, I.hadamard_factors(d // 32))
     assert np.array_equal(qh, qhb) and np.array_equal(sh, shb)
-    qr, sr, y32 = O.kq_quantize(xs, h, want_y32=True)
-    _, z = O.kq_transform(xs, h)
-    ef, bf = P.boundary_flags(z, y32)
-    res = P.compare(qh[rows], sh[rows], qr, sr, ef, bf)
-    say(f"    sampled {len(rows)} rows: {res}")
+    del qhb, shb
+    res = OM.compare_kq_rows(x, h, qh, sh, progress=say)
+    say(f"    hadamard, every row: {res}")
     assert res["ok"], res
+    del qh, sh
 
-    # learned-style per-block factors, sampled rows
+    # learned-style per-block factors, every row
     f = I.random_factors(d // 32, I.factor_seed(name))
     say(f"[sweep {name}] random per-block factors")
     qg, sg = kq_gpu(K, xd, f)
-    qr, sr, y32 = O.kq_quantize(xs, f, want_y32=True)
-    _, z = O.kq_transform(xs, f)
-    ef, bf = P.boundary_flags(z, y32)
-    res = P.compare(qg[rows], sg[rows], qr, sr, ef, bf)
-    say(f"    sampled {len(rows)} rows: {res}")
+    res = OM.compare_kq_rows(x, f, qg, sg, progress=say)
+    say(f"    per-block, every row: {res}")
     assert res["ok"], res
     del xd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["dit_4608", "dbl_12288", "sweep_65536"])
+def test_transform_export_in_timed_launch_shape(K, name):
+    # kq_transform_f32 runs the quantizer's transform in the quantizer's own
+    # launch shape (strip width, token groups, workgroup order: one shape
+    # function serves both); its values are within tolerance of the exact
+    # transform on every row (sampled rows at 65536 x 12288), and the fp32
+    # quantizer applied to them gives the quantizer's codes and scales bit for bit
+    M, d, _ = I.CONFIGS[name]
+    if name.startswith("sweep"):
+        x = I.act_sweep_special(M, d, I.data_seed(name))[0]
+        f = I.hadamard_factors(1)
+    else:
+        x = I.make_activation(name)
+        f = I.make_factors(name)
+    shape = K.kq_launch_shape(M, d)
+    say(f"[transform full {name}] M={M} d={d} nT={f.shape[0]} launch shape {shape}")
+    xd = to_dev(x)
+    fd = torch.from_numpy(f).cuda()
+    y = K.kq_transform_f32(xd, fd)
+    q, s = K.kq_quantize(xd, fd)
+    q2, s2 = K.mx_quantize_f32(y)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2), "quantizer != MXFP4 of its own exported transform"
+    del q, s, q2, s2, xd
+    if name.startswith("sweep"):
+        rng = np.random.default_rng(M + 1)
+        rows = np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), rng.choice(M, 896, replace=False)]))
+        yh = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+        xs = np.ascontiguousarray(x[rows])
+        worst, bad = OM.transform_rows_error(xs, f, yh)
+        say(f"    {len(rows)} sampled rows: max |y_gpu - y| / z = {worst:.3e}, outside the bound: {bad}")
+    else:
+        worst, bad = OM.transform_rows_error(x, f, y.cpu().numpy())
+        say(f"    every row: max |y_gpu - y| / z = {worst:.3e}, outside the bound: {bad}")
+    assert bad == 0
+    del y
+    torch.cuda.empty_cache()
+
+
+def test_concurrent_host_threads_match_single_thread(K):
+    # two host threads, each on its own stream, quantizing different shapes at
+    # the same time (the first launches of their kernel instances included)
+    # give exactly the single-thread results
+    import threading
+    cases = [("dit_1152", 8192, 1152), ("sweep_16384", 16384, 12288)]
+    inputs = []
+    for name, M, d in cases:
+        x = I.make_activation(name) if not name.startswith("sweep") else \
+            I.act_sweep_special(M, d, I.data_seed(name))[0]
+        f = I.make_factors(name) if not name.startswith("sweep") else I.random_factors(d // 32, 9300)
+        inputs.append((to_dev(x), torch.from_numpy(f).cuda()))
+    say("[concurrency] two threads, two streams, 12 launches each")
+    results = [None, None]
+    errors = []
+    barrier = threading.Barrier(2)
+
+    def run(k):
+        try:
+            xd, fd = inputs[k]
+            st = torch.cuda.Stream()
+            barrier.wait()
+            outs = []
+            with torch.cuda.stream(st):
+                for _ in range(12):
+                    outs.append(K.kq_quantize(xd, fd, stream=st))
+            st.synchronize()
+            results[k] = outs
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    ths = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    assert not errors, errors
+    for k, (xd, fd) in enumerate(inputs):
+        q0, s0 = K.kq_quantize(xd, fd)
+        torch.cuda.synchronize()
+        for q, s in results[k]:
+            assert torch.equal(q, q0) and torch.equal(s, s0), cases[k]
+    say("    all launches equal the single-thread result")
 
 
 @pytest.mark.parametrize("name", ["dit_4608", "mid_8960", "dbl_12288"])

@@ -53,17 +53,17 @@ def dev_f32(a):
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
 
 
-def run_kq(K, x_bits, f, variant):
+def run_kq(K, x_bits, f, variant, tuning=None):
     x = dev_bf16(x_bits)
-    q, s = K.kq_quantize(x, dev_f32(f), variant=variant)
+    q, s = K.kq_quantize(x, dev_f32(f), variant=variant, tuning=tuning)
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def check_kq(K, name, x_bits, f, variant, exact=False):
+def check_kq(K, name, x_bits, f, variant, exact=False, tuning=None):
     M, d = x_bits.shape
-    say(f"[kq {name}] M={M} d={d} nT={f.shape[0]} variant={variant}")
-    qg, sg = run_kq(K, x_bits, f, variant)
+    say(f"[kq {name}] M={M} d={d} nT={f.shape[0]} variant={variant} tuning={tuning}")
+    qg, sg = run_kq(K, x_bits, f, variant, tuning)
     qr, sr, y32 = O.kq_quantize(x_bits, f, want_y32=True)
     if exact:
         res = P.compare(qg, sg, qr, sr)
@@ -354,17 +354,21 @@ def test_graph_replay_matches_eager(K):
 
 
 def test_copy_ceiling_kernel_output(K):
-    # the benchmark's 4:1 measurement copy: word i of dst = xor of the four words of src chunk i
-    for n16 in (1, 255, 256 * 2048 * 4 + 77):
-        say(f"[copy41] chunks={n16}")
+    # the benchmark's 4:1 measurement copies, every form: word i of dst = xor
+    # of the four words of src piece i; nothing past dst's n16 words is written
+    for n16 in (64, 64 * 255, 64 * (2048 * 4 + 77)):
         rng = np.random.default_rng(n16)
         src = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
         s_dev = torch.from_numpy(src.view(np.int32)).cuda()
-        d_dev = torch.zeros(n16, dtype=torch.int32, device="cuda")
-        K.measure_copy41(s_dev, d_dev)
-        torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(src.reshape(n16, 4), axis=1)
-        assert np.array_equal(d_dev.cpu().numpy().view(np.uint32), want)
+        for form in range(K.KQ_COPY_FORMS):
+            say(f"[copy41] pieces={n16} form={form}")
+            d_dev = torch.zeros(n16 + 64, dtype=torch.int32, device="cuda")
+            K.measure_copy41(s_dev, d_dev[:n16], form=form)
+            torch.cuda.synchronize()
+            got = d_dev.cpu().numpy().view(np.uint32)
+            assert np.array_equal(got[:n16], want), form
+            assert not got[n16:].any(), form
 
 
 @pytest.mark.parametrize("strip", [8, 16])
@@ -374,13 +378,11 @@ def test_kq_mfma_strip_widths(K, strip, M, d, shared):
     # (blocks past the row end inside a strip, rows past M inside a tile)
     x, _ = I.act_gaussian_outliers(M, d, 7000 + M + d, max(1, d // 100), 50.0)
     f = I.random_factors(1 if shared else d // 32, 7100 + d)
-    K.set_tuning(4, strip)
-    try:
-        check_kq(K, f"strip={strip} shared={shared}", x, f, VARIANTS["mfma"])
-        y = K.kq_transform_f32(dev_bf16(x), dev_f32(f), variant=VARIANTS["mfma"])
-        torch.cuda.synchronize()
-    finally:
-        K.set_tuning(4, 0)
+    tn = {"mfma_strip": strip}
+    assert K.kq_launch_shape(M, d, tuning=tn)["strip"] == strip
+    check_kq(K, f"strip={strip} shared={shared}", x, f, VARIANTS["mfma"], tuning=tn)
+    y = K.kq_transform_f32(dev_bf16(x), dev_f32(f), variant=VARIANTS["mfma"], tuning=tn)
+    torch.cuda.synchronize()
     yr, z = O.kq_transform(x, f)
     err = np.abs(y.cpu().numpy().astype(np.float64) - yr)
     assert np.all(err <= P.TOL * z + P.TOL_ABS), float((err / (z + 1e-300)).max())
@@ -589,19 +591,15 @@ def test_mx_gemm_kernels_agree(K_lib, M, N, Kd):
     qa, sa = _mx_operand(M, Kd, 9900 + M)
     qb, sb = _mx_operand(N, Kd, 9901 + N)
     d = [torch.from_numpy(a).cuda() for a in (qa, sa, qb, sb)]
-    try:
-        for dt in (torch.float32, torch.bfloat16):
-            outs = []
-            for v in (1, 2, 3):
-                say(f"[mx_gemm kernels] M={M} N={N} K={Kd} dtype={dt} variant={v}")
-                K_lib.set_tuning(7, v)
-                outs.append(K_lib.mx_gemm(*d, out_dtype=dt))
-            torch.cuda.synchronize()
-            iv = torch.int32 if dt == torch.float32 else torch.int16
-            for o in outs[1:]:
-                assert torch.equal(o.view(iv), outs[0].view(iv))
-    finally:
-        K_lib.set_tuning(7, 0)
+    for dt in (torch.float32, torch.bfloat16):
+        outs = []
+        for v in (1, 2, 3):
+            say(f"[mx_gemm kernels] M={M} N={N} K={Kd} dtype={dt} variant={v}")
+            outs.append(K_lib.mx_gemm(*d, out_dtype=dt, tuning={"gemm_kernel": v}))
+        torch.cuda.synchronize()
+        iv = torch.int32 if dt == torch.float32 else torch.int16
+        for o in outs[1:]:
+            assert torch.equal(o.view(iv), outs[0].view(iv))
 
 
 def test_mx_gemm_output_alignment_and_guards(K_lib):
