@@ -216,6 +216,26 @@ int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shif
                       uint8_t *q, uint8_t *s, void *stream);
 
 /*
+ * kq_adaln_quantize_noalloc: kq_adaln_quantize for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  The row-statistics workspace is a fixed
+ * device array inside the library instead of the caller's `stats`:
+ * KQ_NOALLOC_MAX_ROWS rows of 16 bytes (2 MiB), one copy per GPU the library
+ * runs on, held until the process ends; its device address is looked up
+ * once per device on the first call there.  M > KQ_NOALLOC_MAX_ROWS returns
+ * KQ_ERR_SHAPE and launches nothing.  The call allocates and frees nothing.
+ * Every call on one GPU shares that array and leaves its statistics in it:
+ * calls that overlap in time on the same GPU (different streams, or threads
+ * without ordering) race on it and must be ordered by the caller.  Calls on
+ * one stream are ordered.  Arguments, results and errors are otherwise those
+ * of kq_adaln_quantize.
+ */
+#define KQ_NOALLOC_MAX_ROWS 131072
+int kq_adaln_quantize_noalloc(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                              int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, uint8_t *q,
+                              uint8_t *s, void *stream);
+
+/*
  * adaln_modulate: the same normalisation alone (the unfused front-end): x as
  * kq_adaln_quantize computes it, written as bf16.
  *   x  dev, bf16 [M, d], 16-byte aligned, not overlapping h, shift, scale or stats

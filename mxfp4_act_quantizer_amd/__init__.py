@@ -17,7 +17,7 @@ _BINDING_NAMES = (
     "kq_quantize_ex", "kq_status_string", "kq_transform_f32", "lib", "mx_quantize_f32", "kq_launch_shape", "Tuning", "TUNING_FIELDS", "KQ_COPY_FORMS",
     "sq_quantize", "measure_copy41", "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize",
     "fwht_transform_f32", "kq_lu_factors", "mx_gemm", "kq_adaln_quantize", "adaln_modulate",
-    "kq_quantize16", "kq_transform16_f32",
+    "kq_quantize16", "kq_transform16_f32", "kq_adaln_quantize_noalloc", "KQ_NOALLOC_MAX_ROWS",
 )
 __all__ = list(_BINDING_NAMES)
 

@@ -36,7 +36,10 @@ EXPORTS = (
     # measurement and test interface
     "kq_quantize_tuned", "kq_transform_tuned", "mx_gemm_tuned", "kq_adaln_quantize_tuned", "kq_launch_shape",
     "kq_measure_copy41",
+    # for callers that cannot allocate
+    "kq_adaln_quantize_noalloc",
 )
+KQ_NOALLOC_MAX_ROWS = 131072
 KQ_COPY_FORMS = 6
 
 # launch-shape overrides (kq_tuning in kroquant.h); 0 keeps the automatic choice
@@ -86,6 +89,7 @@ _lib.mx_gemm.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P]
 _lib.kq_quantize16.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
 _lib.kq_transform16_f32.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
 _lib.kq_adaln_quantize.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P, _P]
+_lib.kq_adaln_quantize_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P]
 _lib.adaln_modulate.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _P, _P]
 _lib.kq_factor_inverse.argtypes = [_P, _I64, _P]
 _lib.kq_block_matrix.argtypes = [_P, _I64, _P]
@@ -389,6 +393,21 @@ def kq_adaln_quantize(h, shift, scale, tokens_per_sample, eps, factors, q=None, 
     else:
         st = _lib.kq_adaln_quantize(*args, _stream_handle(stream))
     _check(st, "kq_adaln_quantize")
+    return q, s
+
+
+def kq_adaln_quantize_noalloc(h, shift, scale, tokens_per_sample, eps, factors, q, s, stream=None):
+    """kq_adaln_quantize with the library's own fixed row-statistics array
+    (at most KQ_NOALLOC_MAX_ROWS rows; calls overlapping in time on one GPU
+    race on it): q and s are the caller's, nothing is allocated."""
+    torch = _torch()
+    M, d = _md(h)
+    st = _lib.kq_adaln_quantize_noalloc(_dev(h, _bf16_types(), "h"), M, d, _dev(shift, (torch.float32,), "shift"),
+                                        _dev(scale, (torch.float32,), "scale"), int(tokens_per_sample), float(eps),
+                                        _dev(factors, (torch.float32,), "factors"), _nT(factors),
+                                        _dev(q, (torch.uint8,), "q"), _dev(s, (torch.uint8,), "s"),
+                                        _stream_handle(stream))
+    _check(st, "kq_adaln_quantize_noalloc")
     return q, s
 
 

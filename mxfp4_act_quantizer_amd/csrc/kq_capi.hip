@@ -4,10 +4,47 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+
 #include "../../include/kroquant.h"
 #include "kq_internal.h"
 
+// Row-statistics workspace of kq_adaln_quantize_noalloc: (mean,
+// 1/sqrt(var + eps)) per row, KQ_NOALLOC_MAX_ROWS rows.  Each GPU holds its
+// own copy; host code reaches it only through the device address looked up
+// per device (noalloc_stats), never through this name.
+static __device__ __align__(256) double scratch[2 * KQ_NOALLOC_MAX_ROWS];
+
 namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, double *> g_scratch_ptr;
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+hipError_t noalloc_stats(double **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    const auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+        return e;
+    if (p == nullptr)
+        return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (double *)p;
+    *out = (double *)p;
+    return hipSuccess;
+}
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -438,6 +475,33 @@ int kq_adaln_quantize(const uint16_t *h, int64_t M, int64_t d, const float *shif
 {
     return kq_adaln_quantize_tuned(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, stats, q, s, nullptr,
                                    stream);
+}
+
+int kq_adaln_quantize_noalloc(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                              int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, uint8_t *q,
+                              uint8_t *s, void *stream)
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if ((st = check_sets(d, nT)))
+        return st;
+    if (M > KQ_NOALLOC_MAX_ROWS)
+        return KQ_ERR_SHAPE;
+    if (M == 0)
+        return KQ_OK;
+    if (!s)
+        return KQ_ERR_ARG;
+    const int64_t qb = M * (d / 2), sb = M * (d / 32);
+    if ((st = check_adaln(h, M, d, shift, scale, tokens_per_sample, eps, nullptr, q, qb, s, sb, true)))
+        return st;
+    if ((st = check_param(factors, nT * 20, h, M * d * 2, q, qb, s, sb)))
+        return st;
+    double *stats = nullptr;
+    if ((st = hip_status(noalloc_stats(&stats))))
+        return st;
+    return hip_status(kq::launch_adaln(h, M, d, shift, scale, tokens_per_sample, eps, factors, nT, stats, q, s,
+                                       nullptr, kq::Tuning{}, (hipStream_t)stream));
 }
 
 int adaln_modulate(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,

@@ -413,3 +413,21 @@ def test_sizes_near_int64_max_are_shape_errors():
 def ctypes_float(v):
     import ctypes
     return ctypes.c_float(v)
+
+
+def test_noalloc_validation():
+    # the allocation-free AdaLN entry point refuses rows beyond its fixed
+    # workspace before any HIP call, and checks the other arguments as
+    # kq_adaln_quantize does
+    import ctypes
+    h, sh, sc, f, q, s = (FAKE + (i << 32) for i in range(6))
+    eps = ctypes.c_float(1e-6)
+    big = K.KQ_NOALLOC_MAX_ROWS + 1
+    assert raw("kq_adaln_quantize_noalloc", h, big, 64, sh, sc, 1, eps, f, 1, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_adaln_quantize_noalloc", h, 1 << 62, 64, sh, sc, 1, eps, f, 1, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_adaln_quantize_noalloc", h, 4, 48, sh, sc, 1, eps, f, 1, q, s, None) == K.KQ_ERR_SHAPE
+    assert raw("kq_adaln_quantize_noalloc", h, 4, 64, sh, sc, 0, eps, f, 1, q, s, None) == K.KQ_ERR_ARG
+    assert raw("kq_adaln_quantize_noalloc", h, 4, 64, sh, sc, 1, eps, f, 1, q, None, None) == K.KQ_ERR_ARG
+    assert raw("kq_adaln_quantize_noalloc", h + 2, 4, 64, sh, sc, 1, eps, f, 1, q, s, None) == K.KQ_ERR_ALIGN
+    assert raw("kq_adaln_quantize_noalloc", h, 4, 64, sh, sc, 1, eps, f, 1, h + 64, s, None) == K.KQ_ERR_OVERLAP
+    assert raw("kq_adaln_quantize_noalloc", None, 0, 64, None, None, 1, eps, None, 1, None, None, None) == K.KQ_OK
