@@ -551,6 +551,56 @@ def test_adaln_flags_a_value_on_a_midpoint(oracle_lib):
     assert np.all(xb[1] == 0x3F81) and not fl[1].any()
 
 
+def test_adaln_margin_flags_near_midpoints_only(oracle_lib):
+    # Rows alternating +half and -half: n = +-half / sqrt(half^2 + eps) =
+    # +-(1 - delta) with delta about eps / (2 half^2).  With scale = 0 and
+    # shift = 2^-8, x = 1 + 2^-8 - delta sits delta below the bf16 midpoint
+    # between 1 and 1 + 2^-7 (the other half of the row sits near -1 + 2^-8,
+    # far from any midpoint).  delta = 4.8e-13 (half = 1024) is inside the
+    # margin, so those elements are flagged (and round down, to 1);
+    # delta = 2e-9 (half = 16) is far outside it and nothing is flagged.
+    d, T, eps = 32, 1, 1e-6
+    for half, flagged in ((1024.0, True), (16.0, False)):
+        h = _bf16_bits(np.tile(np.array([half, -half] * (d // 2), np.float32), (1, 1)))
+        shift = np.full((1, d), 2.0 ** -8, np.float32)
+        scale = np.zeros((1, d), np.float32)
+        x, xb, fl = oracle_lib.adaln(h, shift, scale, T, eps)
+        delta = 1.0 + 2.0 ** -8 - x[0, 0]
+        assert 0.0 < delta < (1e-12 if flagged else 1e-8)
+        assert bool(fl[0, 0::2].all()) == flagged and not fl[0, 1::2].any()
+        assert np.all(xb[0, 0::2] == 0x3F80)
+
+
+def test_adaln_margin_against_high_precision(oracle_lib):
+    # x recomputed in 60-digit decimal arithmetic (exact sums of the bf16
+    # inputs, then one high-precision square root): the oracle's double x is
+    # within its margin of it (so the margin bounds a double evaluation), and
+    # every element the oracle does not flag rounds to the same bf16 from the
+    # high-precision value
+    import decimal
+    decimal.getcontext().prec = 60
+    D = decimal.Decimal
+    M, d, T, eps = 24, 64, 5, 1e-6
+    h, shift, scale = _adaln_inputs(M, d, T, 740)
+    x, xb, fl = oracle_lib.adaln(h, shift, scale, T, eps)
+    hv = (h.astype(np.uint32) << 16).view(np.float32)
+    e32 = D(float(np.float32(eps)))
+    worst = 0.0
+    for m in range(M):
+        vals = [D(float(v)) for v in hv[m]]
+        mu = sum(vals) / d
+        var = sum((v - mu) ** 2 for v in vals) / d
+        r = 1 / (var + e32).sqrt()
+        b = m // T
+        for c in range(d):
+            xe = (vals[c] - mu) * r * (1 + D(float(scale[b, c]))) + D(float(shift[b, c]))
+            err = abs(float(D(float(x[m, c])) - xe))
+            worst = max(worst, err / max(abs(float(xe)), 1e-300))
+            if not fl[m, c]:
+                assert oracle_lib.double_to_bf16(float(xe)) == int(xb[m, c]), (m, c)
+    assert worst < 2.0 ** -40, worst
+
+
 # ---------------------------------------------------------------------------
 # 16-element blocks with four factors (the verdict record's pith_inferences:
 # the construction carries over to 16-element blocks by changing the number of
