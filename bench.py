@@ -692,7 +692,8 @@ def main():
                    "launch": "HIP graph of the K timed steps", "clock_ramp_s": ramp_s,
                    "hbm_pct": round(100 * value / HBM_PEAK_GBS, 2),
                    "rows_per_s": round(M * args.steps / wall, 1),
-                   "kernel_source_hash": src_hash},
+                   "kernel_source_hash": src_hash,
+                   "library_sources": K.kq_build_info().rsplit(" ", 1)[-1]},
         "roofline": roofline,
     }
 

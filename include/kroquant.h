@@ -299,7 +299,7 @@ int kq_lu_factors(const float *lu, int64_t nT, float *factors);
 typedef struct kq_tuning {
     int32_t mfma_tiles_per_wg;     /* MFMA quantizer: 32-token tiles per workgroup, 1..256 */
     int32_t mfma_groups;           /* 1 contiguous runs of tiles, 2 interleaved token groups */
-    int32_t mfma_strip;            /* 8 or 16 blocks (32-channel) per workgroup */
+    int32_t mfma_strip;            /* 4, 8 or 16 blocks (32-channel) per workgroup */
     int32_t mfma_order;            /* 1 XCD-grouped workgroups, 2 flat order */
     int32_t code_stores;           /* MFMA quantizer code stores: 1 default cache policy, 2 nontemporal */
     int32_t stream_rows_per_wave;  /* butterfly, SmoothQuant, fp32, FWHT, 16-element kernels: rows per wave, 1..256 */

@@ -3,6 +3,7 @@
     python -m mxfp4_act_quantizer_amd.build            # build
     python -m mxfp4_act_quantizer_amd.build --resources  # also print VGPR/LDS use per kernel
 """
+import hashlib
 import os
 import subprocess
 import sys
@@ -27,9 +28,23 @@ FLAGS = [
 ]
 
 
+def source_hash():
+    """sha256 (first 16 hex digits) of every source the library is built from:
+    csrc/* and include/*, in name order.  Compiled into kq_build_info(), so a
+    loaded library can be checked against the tree it should come from."""
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h", ".cpp")):
+                h.update(f.encode())
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def build(resources=False, verbose=False):
     srcs = [os.path.join(CSRC, f) for f in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-o", LIB + ".tmp", *srcs]
+    cmd = [HIPCC, *FLAGS, f'-DKQ_SOURCE_HASH="{source_hash()}"', "-o", LIB + ".tmp", *srcs]
     if resources:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

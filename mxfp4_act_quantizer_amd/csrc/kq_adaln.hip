@@ -44,81 +44,31 @@ namespace kq {
 namespace {
 
 constexpr int kAuxNTa = 2;   // nontemporal: the second pass reads h for the last time
-// Statistics kernel: one row per wave; kChunks 16-byte pieces per lane
-// loaded at a time, 3 for rows of up to 192 pieces (d <= 1536) and 6 above
-// (measured against two rows per wave and 4 pieces: 17.9 / 12.8 / 23.3 us
-// against 18.8 / 13.9 / 25.3 for the whole front-end at d 1152 / 2240 /
-// 3072).  A lane sums its pieces in increasing order whatever kChunks is, so
-// the statistics do not depend on it.
-constexpr int kStatRows = 1; // rows per wave of the statistics kernel
 constexpr int kU = 4;        // row blocks per pipeline stage of the streaming pass
 
-__device__ __forceinline__ double wave_sum(double v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
-}
-
 // ---------------------------------------------------------------------------
-// Row statistics: wave w of the grid takes rows kStatRows w .. + kStatRows-1,
-// kChunks 16-byte pieces of each row per lane in flight at a time.
+// Row statistics: one row per wave (adaln_row_stats), kChunks 16-byte pieces
+// per lane loaded at a time, 3 for rows of up to 192 pieces (d <= 1536) and 6
+// above (measured against two rows per wave and 4 pieces: 17.9 / 12.8 / 23.3
+// us against 18.8 / 13.9 / 25.3 for the whole front-end at d 1152 / 2240 /
+// 3072).  A lane sums its pieces in increasing order whatever kChunks is, so
+// the statistics do not depend on it.
 // ---------------------------------------------------------------------------
 template <int kChunks>
 __global__ __launch_bounds__(256) void adaln_stats_kernel(const uint16_t *__restrict__ h, int64_t M, int d, float eps,
                                                           double *__restrict__ stats)
 {
-    constexpr int kStatChunks = kChunks;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t m0 = wave * kStatRows;
-    if (m0 >= M)
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M)
         return; // wave-uniform; no barrier in this kernel
-    const int64_t rows = (M - m0) < kStatRows ? (M - m0) : kStatRows;
-    const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + m0 * d), rows * d * 2);
-    const int nOct = d >> 3;
-    double s1[kStatRows], s2[kStatRows];
-#pragma unroll
-    for (int j = 0; j < kStatRows; ++j)
-        s1[j] = s2[j] = 0.0;
-    // lane-strided over the row's 16-byte pieces; rows past the run and
-    // pieces past the row end fall outside the range and read as zeros
-    for (int base = 0; base < nOct; base += 64 * kStatChunks) {
-        u32x4 v[kStatRows][kStatChunks];
-#pragma unroll
-        for (int j = 0; j < kStatRows; ++j)
-#pragma unroll
-            for (int c = 0; c < kStatChunks; ++c) {
-                const int o = base + 64 * c + lane;
-                const unsigned drop = (unsigned)(o >= nOct) << 31;
-                v[j][c] = __builtin_bit_cast(
-                    u32x4,
-                    __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)(j * d * 2 + o * 16) | drop), 0, 0));
-            }
-#pragma unroll
-        for (int j = 0; j < kStatRows; ++j)
-#pragma unroll
-            for (int c = 0; c < kStatChunks; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const double a = (double)bf16lo(v[j][c][i]), e = (double)bf16hi(v[j][c][i]);
-                    s1[j] += a;
-                    s2[j] = __builtin_fma(a, a, s2[j]);
-                    s1[j] += e;
-                    s2[j] = __builtin_fma(e, e, s2[j]);
-                }
-    }
-#pragma unroll
-    for (int j = 0; j < kStatRows; ++j) {
-        const double t1 = wave_sum(s1[j]), t2 = wave_sum(s2[j]);
-        if (j < rows && lane == j) {
-            const double mu = t1 / (double)d;
-            double var = t2 / (double)d - mu * mu;
-            var = var > 0.0 ? var : 0.0;
-            stats[2 * (m0 + j)] = mu;
-            stats[2 * (m0 + j) + 1] = 1.0 / sqrt(var + (double)eps);
-        }
+    const __amdgpu_buffer_rsrc_t rh = out_buffer((void *)(h + m * d), (int64_t)d * 2);
+    const unsigned off[1] = {0u};
+    double mu[1], rstd[1];
+    adaln_row_stats<1, kChunks>(rh, off, d, eps, lane, mu, rstd);
+    if (lane == 0) {
+        stats[2 * m] = mu[0];
+        stats[2 * m + 1] = rstd[0];
     }
 }
 
@@ -129,14 +79,6 @@ __global__ __launch_bounds__(256) void adaln_stats_kernel(const uint16_t *__rest
 struct HRows {
     u32x4 v[kU];
 };
-
-__device__ __forceinline__ void load_rows(HRows &in, __amdgpu_buffer_rsrc_t rh, int mr, int d, unsigned lane_off)
-{
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-        in.v[u] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)((unsigned)((mr + u) * d * 2) + lane_off), 0, kAuxNTa));
-}
 
 // Flat row blocks.  Rb = 64 / gcd(nOct, 64) rows of nOct octets (8 channels
 // each) are a whole number Wb = Rb nOct / 64 of waves with every lane busy
@@ -266,9 +208,8 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
                         float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
                         uint16_t *x, const Tuning &tn, hipStream_t stream)
 {
-    // pass 1: row statistics
-    const int64_t waves = (M + kStatRows - 1) / kStatRows;
-    const int64_t grid1 = (waves + 3) / 4;
+    // pass 1: row statistics, one row per wave
+    const int64_t grid1 = (M + 3) / 4;
     // pass 2: flat row blocks of Rb rows = Wb full waves; kIt blocks per wave
     const int nOct = (int)(d / 8);
     int g = 64;

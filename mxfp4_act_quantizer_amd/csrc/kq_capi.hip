@@ -79,7 +79,7 @@ int check_tuning(const kq_tuning *t)
         return KQ_OK;
     auto in = [](int32_t v, int32_t lo, int32_t hi) { return v == 0 || (v >= lo && v <= hi); };
     const bool ok = in(t->mfma_tiles_per_wg, 1, 256) && in(t->mfma_groups, 1, 2) &&
-                    (t->mfma_strip == 0 || t->mfma_strip == 8 || t->mfma_strip == 16) && in(t->mfma_order, 1, 2) &&
+                    (t->mfma_strip == 0 || t->mfma_strip == 4 || t->mfma_strip == 8 || t->mfma_strip == 16) && in(t->mfma_order, 1, 2) &&
                     in(t->code_stores, 1, 2) && in(t->stream_rows_per_wave, 1, 256) && in(t->gemm_kernel, 1, 3) &&
                     in(t->adaln_pass, 1, 2) && (t->adaln_strip == 0 || t->adaln_strip == 4 || t->adaln_strip == 8) &&
                     in(t->adaln_blocks_per_wave, 1, 256);
@@ -532,10 +532,14 @@ const char *kq_status_string(int status)
     }
 }
 
+#ifndef KQ_SOURCE_HASH
+#define KQ_SOURCE_HASH "unknown"
+#endif
+
 const char *kq_build_info(void)
 {
     return "kroquant gfx950: default variant=mfma (v_mfma_f32_32x32x16_bf16, 3-term bf16 split of K), "
-           "butterfly=DPP quad stages; FP4 via v_cvt_scalef32_pk_fp4_f32";
+           "butterfly=DPP quad stages; FP4 via v_cvt_scalef32_pk_fp4_f32; sources " KQ_SOURCE_HASH;
 }
 
 int kq_last_hip_error(void) { return (int)last_hip_error; }

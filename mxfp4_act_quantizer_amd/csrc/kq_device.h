@@ -255,6 +255,67 @@ __device__ __forceinline__ void adaln_bf16x8(const u32x4 &hv, double mu, double 
     }
 }
 
+// Row statistics of the AdaLN front-end, one wave per row.  Lane l sums the
+// row's 16-byte pieces l, l + 64, l + 128, ... in increasing order (each
+// piece's eight values in order), the sum and the sum of squares in fp64
+// (bf16 values and their squares are exact in double), kChunks pieces in
+// flight per lane; pieces past the row end (bit 31 of their offset) read as
+// zeros and add nothing.  Then a butterfly reduction over the 64 lanes.
+// Every kernel that needs the statistics calls this routine, so they agree
+// bit for bit whatever their launch shape.
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// kRows rows at once (their loads in flight together), row r at byte offset
+// row_off[r] of the buffer; every row is summed exactly as a row alone.
+template <int kRows, int kChunks>
+__device__ __forceinline__ void adaln_row_stats(__amdgpu_buffer_rsrc_t rh, const unsigned (&row_off)[kRows], int d,
+                                                float eps, int lane, double (&mu)[kRows], double (&rstd)[kRows])
+{
+    const int nOct = d >> 3;
+    double s1[kRows], s2[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+        s1[r] = s2[r] = 0.0;
+    for (int base = 0; base < nOct; base += 64 * kChunks) {
+        u32x4 v[kRows][kChunks];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) {
+                const int o = base + 64 * c + lane;
+                const unsigned drop = (unsigned)(o >= nOct) << 31;
+                v[r][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rh, (int)((row_off[r] + (unsigned)o * 16u) | drop), 0, 0));
+            }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const double a = (double)bf16lo(v[r][c][i]), e = (double)bf16hi(v[r][c][i]);
+                    s1[r] += a;
+                    s2[r] = __builtin_fma(a, a, s2[r]);
+                    s1[r] += e;
+                    s2[r] = __builtin_fma(e, e, s2[r]);
+                }
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const double t1 = wave_sum_f64(s1[r]), t2 = wave_sum_f64(s2[r]);
+        mu[r] = t1 / (double)d;
+        double var = t2 / (double)d - mu[r] * mu[r];
+        var = var > 0.0 ? var : 0.0;
+        rstd[r] = 1.0 / sqrt(var + (double)eps);
+    }
+}
+
 struct Modulation {
     double g[8], t[8]; // 1 + scale and shift of the lane's channels for the current sample
     int64_t next;      // first row of the next sample

@@ -710,6 +710,8 @@ const void *mfma_shape_fn(int w, bool adaln)
 {
     if (adaln)
         return w == 4 ? (const void *)kq_mfma_kernel<true, 4, true> : (const void *)kq_mfma_kernel<true, 8, true>;
+    if (w == 4)
+        return (const void *)kq_mfma_kernel<true, 4>;
     return w == 16 ? (const void *)kq_mfma_kernel<true, 16> : (const void *)kq_mfma_kernel<true, 8>;
 }
 
@@ -877,7 +879,7 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
         // idle between workgroups, and strips of 8 (two per CU) win.  They are
         // used only when they divide the row exactly, so no wave idles.
         w = tn.mfma_strip;
-        if (w != 8 && w != 16) {
+        if (w != 4 && w != 8 && w != 16) {
             w = 8;
             if (nB % 16 == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups != 1) {
                 int64_t gx = mfma_wgs_per_xcd(mfma_shape_fn(16, false), 64 * 16) / (nB / 16);
@@ -908,6 +910,9 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
     if (sh.strip == 16)
         return sh.nt_codes && !y ? launch_mfma_instance<16, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
                                  : launch_mfma_instance<16, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+    if (sh.strip == 4)
+        return sh.nt_codes && !y ? launch_mfma_instance<4, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                                 : launch_mfma_instance<4, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
     return sh.nt_codes && !y ? launch_mfma_instance<8, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
                              : launch_mfma_instance<8, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
 }

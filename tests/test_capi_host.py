@@ -35,6 +35,13 @@ def test_library_is_the_in_tree_build():
     assert "gfx950" in K.kq_build_info()
 
 
+def test_library_is_built_from_the_current_sources():
+    # the library carries the hash of the sources it was compiled from; a
+    # stale build (sources changed since) fails here
+    from mxfp4_act_quantizer_amd import build as B
+    assert K.kq_build_info().endswith("sources " + B.source_hash()), (K.kq_build_info(), B.source_hash())
+
+
 def test_status_strings():
     for st in range(7):
         assert K.kq_status_string(st) != "unknown status"
@@ -361,7 +368,7 @@ def test_tuning_validation():
     # refused before any HIP call, and nothing is kept between calls
     import ctypes
     x, q, s, f, y = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
-    bad = [("mfma_tiles_per_wg", 257), ("mfma_tiles_per_wg", -1), ("mfma_groups", 3), ("mfma_strip", 12),
+    bad = [("mfma_tiles_per_wg", 257), ("mfma_tiles_per_wg", -1), ("mfma_groups", 3), ("mfma_strip", 12), ("mfma_strip", 2),
            ("mfma_order", 3), ("code_stores", 3), ("stream_rows_per_wave", 300), ("gemm_kernel", 4),
            ("adaln_pass", 3), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000)]
     for field, val in bad:

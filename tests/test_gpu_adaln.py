@@ -93,8 +93,13 @@ def check(K, h, shift, scale, T, f, label):
 # (M, d, tokens per sample): ragged row counts against runs of 8 rows and
 # pipeline stages of 4, samples that end inside a run, widths from one block
 # to past several 512-channel column tiles
+# Also samples of 32 tokens and more: sample boundaries inside 32-row tiles
+# (T = 40, 35, 33), a ragged last tile, one sample for all rows, and widths
+# from 96 to 12288 channels.
 ADALN_CASES = [(1, 32, 1), (5, 64, 2), (37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (19, 3072, 7),
-               (9, 8192, 4), (24, 544, 5), (3, 8960, 2), (6, 12288, 3)]
+               (9, 8192, 4), (24, 544, 5), (3, 8960, 2), (6, 12288, 3),
+               (33, 1152, 32), (97, 1152, 40), (70, 8192, 35), (300, 96, 100), (64, 3072, 64),
+               (5, 12288, 64), (130, 1152, 1000), (200, 544, 33), (161, 2240, 80)]
 
 
 @pytest.mark.parametrize("M,d,T", ADALN_CASES, ids=[f"{m}x{d}_T{t}" for m, d, t in ADALN_CASES])
@@ -145,7 +150,8 @@ def test_adaln_special_rows(K):
 PASS_FORMS = [("mfma_strip4", {"adaln_pass": 1, "adaln_strip": 4}, None),
               ("mfma_strip8", {"adaln_pass": 1, "adaln_strip": 8}, None),
               ("butterfly", {"adaln_pass": 2}, "KQ_VARIANT_BUTTERFLY")]
-FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300, 96, 1), (4100, 3072, 2048)]
+FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300, 96, 1), (4100, 3072, 2048),
+              (97, 1152, 40), (70, 8192, 35), (200, 544, 33)]
 
 
 @pytest.mark.parametrize("form,knobs,variant", PASS_FORMS, ids=[p[0] for p in PASS_FORMS])
@@ -174,7 +180,11 @@ def test_adaln_second_pass_forms(K, form, knobs, variant):
 def test_adaln_stats_workspace(K):
     # the caller's workspace holds each row's mean and 1/sqrt(var + eps) in
     # double after the call (numpy's float64 statistics of the same bf16 rows)
-    M, d, T = 21, 2240, 4
+    for M, d, T in ((21, 2240, 4), (75, 1152, 40)):
+        _check_stats(K, M, d, T)
+
+
+def _check_stats(K, M, d, T):
     say(f"[adaln stats] M={M} d={d} T={T}")
     h = I.act_dit_lognormal(M, d, 8300)[0]
     shift, scale = I.adaln_modulation((M + T - 1) // T, d, 8301)

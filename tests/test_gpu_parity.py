@@ -371,7 +371,7 @@ def test_copy_ceiling_kernel_output(K):
             assert not got[n16:].any(), form
 
 
-@pytest.mark.parametrize("strip", [8, 16])
+@pytest.mark.parametrize("strip", [4, 8, 16])
 @pytest.mark.parametrize("M,d,shared", [(67, 1152, False), (33, 160, True), (130, 4608, False), (5, 544, False)])
 def test_kq_mfma_strip_widths(K, strip, M, d, shared):
     # both workgroup strip widths of the MFMA quantizer, forced, on ragged shapes
