@@ -879,7 +879,12 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
         // idle between workgroups, and strips of 8 (two per CU) win.  They are
         // used only when they divide the row exactly, so no wave idles.
         w = tn.mfma_strip;
-        if (w != 4 && w != 8 && w != 16) {
+        if (w != 4 && w != 8 && w != 16 && nB % 8 != 0 && nB % 4 == 0) {
+            // Strips of 4 blocks when they divide the row and strips of 8 do
+            // not, so no wave idles (measured at 8192 x 1152, contiguous
+            // groups of 6 tiles: 7.93 against 8.23 us for strips of 8).
+            w = 4;
+        } else if (w != 4 && w != 8 && w != 16) {
             w = 8;
             if (nB % 16 == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups != 1) {
                 int64_t gx = mfma_wgs_per_xcd(mfma_shape_fn(16, false), 64 * 16) / (nB / 16);
