@@ -73,6 +73,8 @@ def parse():
                     help="AdaLN front-end fused with the quantizer against the unfused pipeline, hidden widths")
     ap.add_argument("--gemm", action="store_true",
                     help="W4A4 consumer (mx_gemm) on the DiT layer shapes, against its roofline")
+    ap.add_argument("--gemm-library", action="store_true",
+                    help="mx_gemm against torch's MXFP4 scaled_mm (hipBLASLt) on the qkv and proj layer shapes")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic profile from two rocprofv3 --pmc output folders (no GPU needed)")
     return ap.parse_args()
@@ -464,6 +466,61 @@ def gemm_bench(args):
                       "per_tile_kernel_block_us": round(sum(r["per_tile_kernel_us"] for r in rows), 2)}), flush=True)
 
 
+def gemm_library_bench(args):
+    """mx_gemm against the library MXFP4 product this image offers
+    (torch.nn.functional.scaled_mm with 1x32 E8M0 block scales, which runs
+    hipBLASLt), on the same operands: the quantizer's codes and scales as they
+    are, viewed as float4_e2m1fn_x2 and float8_e8m0fnu.  Both timed eagerly,
+    back to back, with HIP events.  Only the qkv and proj shapes: at the MLP
+    shapes the library's kernel generator fails in this build and retries
+    for minutes."""
+    import torch
+    import torch.nn.functional as F
+
+    import mxfp4_act_quantizer_amd as K
+    from synth import inputs as I
+    dev = torch.device("cuda:0")
+
+    def eager_us(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for name, M, N, Kd in GEMM_SHAPES[:2]:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(M + N + Kd)
+        f = torch.from_numpy(I.hadamard_factors(Kd // 32)).to(dev)
+        x = torch.randn(M, Kd, generator=gen, device=dev).to(torch.bfloat16)
+        qa, sa = K.kq_quantize(x, f)
+        qb, sb = K.mx_quantize_f32(torch.randn(N, Kd, generator=gen, device=dev) / math.sqrt(Kd))
+        ref = K.mx_gemm(qa, sa, qb, sb, out_dtype=torch.float32)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ours = eager_us(lambda: K.mx_gemm(qa, sa, qb, sb, out=out), args.steps)
+        a4, b4 = qa.view(torch.float4_e2m1fn_x2), qb.view(torch.float4_e2m1fn_x2)
+        ea, eb = sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu)
+
+        def lib():
+            return F.scaled_mm(a4, b4.t(), ea, F.ScalingType.BlockWise1x32, eb, F.ScalingType.BlockWise1x32,
+                               F.SwizzleType.NO_SWIZZLE, F.SwizzleType.NO_SWIZZLE, output_dtype=torch.bfloat16)
+        row = {"layer": name, "M": M, "N": N, "K": Kd, "mx_gemm_us": round(ours, 2)}
+        try:
+            got = lib()
+            torch.cuda.synchronize()
+            row["library_us"] = round(eager_us(lib, args.steps), 2)
+            row["library_max_rel_diff"] = float(((got.float() - ref).abs().max() / ref.abs().max()).item())
+            row["mx_gemm_max_rel_diff"] = float(((out.float() - ref).abs().max() / ref.abs().max()).item())
+        except (RuntimeError, TypeError, AttributeError) as e:
+            row["library_error"] = f"{type(e).__name__}: {str(e)[:200]}"
+        print(json.dumps(row), flush=True)
+
+
 ADALN_WORKLOADS = ("dit_1152", "mid_2240", "dbl_3072")  # the hidden widths AdaLN normalises
 ADALN_EPS = 1e-6
 
@@ -473,8 +530,10 @@ def adaln_bench(args):
     the unfused pipeline (adaln_modulate writing bf16 x, then kq_quantize with
     the MFMA or the butterfly transform) and against torch's layer_norm and
     modulation (bf16 out) followed by kq_quantize, at the hidden widths, two samples
-    (CFG) per batch.  Two more fused legs select the butterfly second pass and
-    the matrix-core second pass in strips of 4 blocks.  Fused algorithmic bytes: 2.53125 B per element (h read,
+    (CFG) per batch.  The fused call runs its automatic form (two launches,
+    second pass on the matrix cores); more fused legs force the one-launch form
+    (whole rows in LDS), the matrix-core second pass in strips of 4 blocks and
+    the butterfly second pass.  Fused algorithmic bytes: 2.53125 B per element (h read,
     codes and scales written) plus the modulation; unfused: 6.53125 (x
     written and read back).  Per-block factor sets; h drawn on the GPU as
     N(0,1) with 1% outlier channels x50 (the time does not depend on the
@@ -543,6 +602,7 @@ def adaln_bench(args):
             return run
 
         t = {"fused": _time_leg(fused, nsets, args.steps),
+             "fused_one_launch": _time_leg(fused_with({"adaln_pass": 3}), nsets, args.steps),
              "fused_butterfly_pass": _time_leg(fused_with({"adaln_pass": 2}), nsets, args.steps),
              "fused_mfma_strip4": _time_leg(fused_with({"adaln_pass": 1, "adaln_strip": 4}), nsets, args.steps),
              "torch_layernorm_then_kq_mfma": _time_leg(torch_unfused, nsets, args.steps),
@@ -574,11 +634,13 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
               f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
         sys.exit(2)
-    if args.all_configs or args.gemm or args.adaln:
+    if args.all_configs or args.gemm or args.adaln or args.gemm_library:
         if args.all_configs:
             all_configs(args)
         elif args.gemm:
             gemm_bench(args)
+        elif args.gemm_library:
+            gemm_library_bench(args)
         else:
             adaln_bench(args)
         return

@@ -304,7 +304,9 @@ typedef struct kq_tuning {
     int32_t code_stores;           /* MFMA quantizer code stores: 1 default cache policy, 2 nontemporal */
     int32_t stream_rows_per_wave;  /* butterfly, SmoothQuant, fp32, FWHT, 16-element kernels: rows per wave, 1..256 */
     int32_t gemm_kernel;           /* mx_gemm: 1 per-tile, 2 persistent (k chunks of 256), 3 persistent (128) */
-    int32_t adaln_pass;            /* kq_adaln_quantize second pass: 1 matrix cores, 2 butterfly */
+    int32_t adaln_pass;            /* kq_adaln_quantize form: 1 two launches, second pass on the matrix
+                                      cores; 2 two launches, butterfly second pass; 3 one launch (whole
+                                      rows in LDS; KQ_ERR_HIP when they do not fit) */
     int32_t adaln_strip;           /* its matrix-core strip width: 4 or 8 blocks */
     int32_t adaln_blocks_per_wave; /* butterfly / adaln_modulate pass: row blocks per wave, 1..256 */
 } kq_tuning;

@@ -208,6 +208,10 @@ hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *sh
                         float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
                         uint16_t *x, const Tuning &tn, hipStream_t stream)
 {
+    // the one-launch form when the tuning selects it (measured slower than the
+    // two launches at every width tried, so never chosen by itself)
+    if (x == nullptr && tn.adaln_pass == 3)
+        return launch_adaln_rows(h, M, d, shift, scale, T, eps, factors, nT, stats, q, s, stream);
     // pass 1: row statistics, one row per wave
     const int64_t grid1 = (M + 3) / 4;
     // pass 2: flat row blocks of Rb rows = Wb full waves; kIt blocks per wave

@@ -81,7 +81,7 @@ int check_tuning(const kq_tuning *t)
     const bool ok = in(t->mfma_tiles_per_wg, 1, 256) && in(t->mfma_groups, 1, 2) &&
                     (t->mfma_strip == 0 || t->mfma_strip == 4 || t->mfma_strip == 8 || t->mfma_strip == 16) && in(t->mfma_order, 1, 2) &&
                     in(t->code_stores, 1, 2) && in(t->stream_rows_per_wave, 1, 256) && in(t->gemm_kernel, 1, 3) &&
-                    in(t->adaln_pass, 1, 2) && (t->adaln_strip == 0 || t->adaln_strip == 4 || t->adaln_strip == 8) &&
+                    in(t->adaln_pass, 1, 3) && (t->adaln_strip == 0 || t->adaln_strip == 4 || t->adaln_strip == 8) &&
                     in(t->adaln_blocks_per_wave, 1, 256);
     return ok ? KQ_OK : KQ_ERR_ARG;
 }

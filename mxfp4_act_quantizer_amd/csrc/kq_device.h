@@ -261,14 +261,62 @@ __device__ __forceinline__ void adaln_bf16x8(const u32x4 &hv, double mu, double 
 // (bf16 values and their squares are exact in double), kChunks pieces in
 // flight per lane; pieces past the row end (bit 31 of their offset) read as
 // zeros and add nothing.  Then a butterfly reduction over the 64 lanes.
-// Every kernel that needs the statistics calls this routine, so they agree
-// bit for bit whatever their launch shape.
+// Every kernel that needs the statistics sums through adaln_piece_sums in
+// this order and ends in adaln_row_finish, so they agree bit for bit whatever
+// their launch shape or where the row is read from.
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1)
         v += __shfl_xor(v, m, 64);
     return v;
+}
+
+// One 16-byte piece (eight bf16 values, in order) into a lane's running sums.
+__device__ __forceinline__ void adaln_piece_sums(const u32x4 &v, double &s1, double &s2)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = (double)bf16lo(v[i]), e = (double)bf16hi(v[i]);
+        s1 += a;
+        s2 = __builtin_fma(a, a, s2);
+        s1 += e;
+        s2 = __builtin_fma(e, e, s2);
+    }
+}
+
+// The wave reduction of the lanes' sums, then mean and 1/sqrt(var + eps)
+// (biased variance, clamped at 0).  Every lane of the wave takes part.
+__device__ __forceinline__ void adaln_row_finish(double s1, double s2, int d, float eps, double &mu, double &rstd)
+{
+    const double t1 = wave_sum_f64(s1), t2 = wave_sum_f64(s2);
+    mu = t1 / (double)d;
+    double var = t2 / (double)d - mu * mu;
+    var = var > 0.0 ? var : 0.0;
+    rstd = 1.0 / sqrt(var + (double)eps);
+}
+
+// adaln_row_finish of two rows at once, their reductions interleaved; each
+// row's values are those adaln_row_finish gives it alone.
+__device__ __forceinline__ void adaln_row_finish2(const double (&s1)[2], const double (&s2)[2], int d, float eps,
+                                                  double (&mu)[2], double (&rstd)[2])
+{
+    double t1[2] = {s1[0], s1[1]}, t2[2] = {s2[0], s2[1]};
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            t1[k] += __shfl_xor(t1[k], m, 64);
+            t2[k] += __shfl_xor(t2[k], m, 64);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        mu[k] = t1[k] / (double)d;
+        double var = t2[k] / (double)d - mu[k] * mu[k];
+        var = var > 0.0 ? var : 0.0;
+        rstd[k] = 1.0 / sqrt(var + (double)eps);
+    }
 }
 
 // kRows rows at once (their loads in flight together), row r at byte offset
@@ -297,23 +345,11 @@ __device__ __forceinline__ void adaln_row_stats(__amdgpu_buffer_rsrc_t rh, const
         for (int r = 0; r < kRows; ++r)
 #pragma unroll
             for (int c = 0; c < kChunks; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const double a = (double)bf16lo(v[r][c][i]), e = (double)bf16hi(v[r][c][i]);
-                    s1[r] += a;
-                    s2[r] = __builtin_fma(a, a, s2[r]);
-                    s1[r] += e;
-                    s2[r] = __builtin_fma(e, e, s2[r]);
-                }
+                adaln_piece_sums(v[r][c], s1[r], s2[r]);
     }
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        const double t1 = wave_sum_f64(s1[r]), t2 = wave_sum_f64(s2[r]);
-        mu[r] = t1 / (double)d;
-        double var = t2 / (double)d - mu[r] * mu[r];
-        var = var > 0.0 ? var : 0.0;
-        rstd[r] = 1.0 / sqrt(var + (double)eps);
-    }
+    for (int r = 0; r < kRows; ++r)
+        adaln_row_finish(s1[r], s2[r], d, eps, mu[r], rstd[r]);
 }
 
 struct Modulation {

@@ -17,6 +17,7 @@ using Tuning = kq_tuning;
 // Thread-safe per-device queries, filled once per (device, kernel) under a lock.
 int device_cus();                                  // compute units of the current device
 int occupancy_per_cu(const void *fn, int threads); // resident workgroups per CU of fn on the current device
+hipError_t allow_dynamic_lds(const void *fn, int bytes); // raise fn's dynamic LDS limit (once per device)
 
 // Launch shape the MFMA quantizer picks for (M, d): strip width, tiles per
 // workgroup, interleaved token groups, flat workgroup order, grid.  The
@@ -52,10 +53,32 @@ hipError_t launch_mx_gemm(const uint8_t *qa, const uint8_t *sa, int64_t M, const
 // workspace stats [M, 2], then x = LayerNorm(h) (1 + scale[m / T]) +
 // shift[m / T] rounded to bf16 and either (x null) the transform and MXFP4
 // into q, s (the matrix-core second pass, or the butterfly one when the
-// tuning selects it), or (x given) x written out.  Two launches on `stream`.
+// tuning selects it), or (x given) x written out.  Two launches on `stream`,
+// or one (x null) when the tuning selects the one-launch form.
 hipError_t launch_adaln(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale, int64_t T,
                         float eps, const float *factors, int64_t nT, double *stats, uint8_t *q, uint8_t *s,
                         uint16_t *x, const Tuning &tn, hipStream_t stream);
+// The AdaLN front-end in one launch (x null only): workgroups own whole token
+// rows, R at a time, held in LDS (statistics, normalisation, transform and
+// MXFP4 from there; stats written as by the two-launch form).  LDS layout of a
+// workgroup: x rows (pitch xrow), staged codes at qoff (pitch qrow), scale
+// bytes at soff (pitch srow), per-row (mean, 1/sqrt(var + eps)) at toff, the
+// factor sets at foff, and at moff the shift rows then (mbytes later) the
+// scale rows of up to nmod samples.
+struct AdRowsLayout {
+    int xrow, qrow, srow;
+    int qoff, soff, toff, foff, moff, mbytes, nmod, bytes;
+};
+struct AdRowsShape {
+    int R, nmod, bytes;
+    int64_t grid;
+};
+// Rows per tile, staged samples and grid of the one-launch form for (M, d,
+// nT); false when too few rows fit the LDS (the two-launch form then runs).
+bool adaln_rows_shape(int64_t M, int64_t d, int64_t nT, AdRowsShape &sh);
+hipError_t launch_adaln_rows(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                             int64_t T, float eps, const float *factors, int64_t nT, double *stats, uint8_t *q,
+                             uint8_t *s, hipStream_t stream);
 // Second pass of the AdaLN front-end on the matrix cores: h normalised with
 // the statistics workspace and modulated while it is staged, then the MFMA
 // transform and MXFP4 into q, s.  One launch on `stream`.

@@ -450,6 +450,231 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
 }
 
 // ---------------------------------------------------------------------------
+// AdaLN front-end in one launch, for rows that fit the LDS (selected by the
+// tuning; the two-launch form is the default).  A workgroup of kRowsWaves waves
+// owns R <= 32 whole token rows at a time (one matrix-core tile of tokens), so
+// h is read from HBM once:
+//   0. the factor sets go into LDS once; each tile's rows of h, and the
+//      modulation rows of its samples when there are at most nmod of them,
+//      go into LDS by LDS-DMA loads (padded rows: a 16-byte read at the same
+//      column of 16 consecutive rows hits every bank once);
+//   1. each wave computes the statistics of two rows from LDS at a time,
+//      summing a row's pieces in the statistics kernel's order
+//      (adaln_piece_sums, adaln_row_finish2), so the values agree with it bit
+//      for bit; they go to `stats` and to LDS;
+//   2. the waves walk the row's blocks: lane (h, t) normalises and modulates
+//      its 8 channels of token t from LDS (adaln_bf16x8, per lane, since a
+//      tile can straddle two samples), the block is transformed on the matrix
+//      cores exactly as in kq_mfma_kernel and quantized into an LDS staging
+//      tile;
+//   3. the codes and scales leave as whole rows, 16 bytes per lane, while the
+//      next tile's loads are in flight.
+// Lanes of tokens past the tile's last row compute on a copy of that row and
+// store nothing.  With one tile per workgroup nothing overlaps the load, the
+// statistics and the blocks of a tile, and the two-launch form, whose many
+// workgroups per CU overlap them, measured faster at every width.
+// ---------------------------------------------------------------------------
+constexpr int kRowsWaves = 16;
+
+// LDS layout for R rows of width d, nsets staged factor sets and the
+// modulation rows of up to nmod samples (shift, then scale, fp32).  Regions
+// filled by LDS-DMA are whole 1 KB instructions long, so the lanes past their
+// data (which write zeros) stay inside them.
+__host__ __device__ inline AdRowsLayout adaln_rows_layout(int R, int d, int nsets, int nmod)
+{
+    AdRowsLayout L;
+    L.xrow = 2 * d + 16;
+    L.qrow = d / 2 + 16;
+    L.srow = (d / 32 + 15) / 16 * 16;
+    const int round = 1024 * kRowsWaves; // one DMA instruction of every wave
+    L.qoff = (R * L.xrow + round - 1) / round * round;
+    L.soff = L.qoff + R * L.qrow;
+    L.toff = L.soff + R * L.srow;
+    L.foff = (L.toff + R * 16 + 1023) / 1024 * 1024;
+    L.moff = L.foff + (nsets * 80 + 1023) / 1024 * 1024;
+    L.nmod = nmod;
+    L.mbytes = (nmod * d * 4 + 1023) / 1024 * 1024;
+    L.bytes = L.moff + 2 * L.mbytes;
+    return L;
+}
+
+// bytes (a multiple of 16) from rsrc into LDS at dst by 16-byte LDS-DMA loads,
+// 1 KB per instruction, instructions dealt to the waves in turn
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsigned char *dst, int bytes, int wave,
+                                           int lane)
+{
+    const int n = (bytes + 1023) >> 10;
+    for (int k = wave; k < n; k += kRowsWaves) {
+        const int o = (k << 10) + lane * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void *)(dst + (k << 10)), 16,
+            (int)(o < bytes ? (unsigned)o : 0x80000000u), 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(64 * kRowsWaves) void adaln_rows_kernel(
+    const uint16_t *__restrict__ h, int64_t M, int d, const float *__restrict__ shift,
+    const float *__restrict__ scale, int64_t T, float eps, const float *__restrict__ factors, int per_block,
+    double *__restrict__ stats, uint8_t *__restrict__ q, uint8_t *__restrict__ s, int R, int nmod)
+{
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int nB = d >> 5, nOct = d >> 3;
+    const AdRowsLayout L = adaln_rows_layout(R, d, per_block ? nB : 1, nmod);
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int slots = nOct + 1; // 16-byte slots of a padded LDS row
+    const int h2 = lane >> 5, tl = lane & 31;
+    const int64_t nTiles = (M + R - 1) / R;
+    const int64_t nS = (M + T - 1) / T;
+    constexpr unsigned kVm0 = 0x0F70u; // s_waitcnt vmcnt(0) alone
+
+    // Loads of tile `tile`: its rows of h into the x region (instruction k of
+    // wave w fills slots 64 (w + kRowsWaves k) .. +63; pad slots, rows past R
+    // and rows past M fetch nothing and write zeros) and, when its rows span
+    // at most nmod samples, those samples' modulation rows.
+    auto load_tile = [&](int64_t tile) {
+        const int64_t r0 = tile * R;
+        const int rows = (int)((M - r0) < R ? (M - r0) : R);
+        const __amdgpu_buffer_rsrc_t rh =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(h + r0 * d), 0, rows * d * 2, kBufWord3);
+        for (int base = wave * 64; base < L.qoff / 16; base += 64 * kRowsWaves) {
+            const int p = base + lane;
+            const int row = p / slots, slot = p - row * slots;
+            const unsigned off = (row < R && slot < nOct) ? (unsigned)(row * d + slot * 8) * 2u : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (__attribute__((address_space(3))) void *)(lds + base * 16),
+                                                     16, (int)off, 0, 0, 0);
+        }
+        const int64_t b0 = r0 / T, ns = (r0 + rows - 1) / T - b0 + 1;
+        if (ns <= nmod) {
+            const int bytes = (int)ns * d * 4;
+            dma_to_lds(__builtin_amdgcn_make_buffer_rsrc((void *)(shift + b0 * d), 0, bytes, kBufWord3),
+                       lds + L.moff, bytes, wave, lane);
+            dma_to_lds(__builtin_amdgcn_make_buffer_rsrc((void *)(scale + b0 * d), 0, bytes, kBufWord3),
+                       lds + L.moff + L.mbytes, bytes, wave, lane);
+        }
+    };
+
+    // the factor sets, staged once
+    const int fbytes = (per_block ? nB : 1) * 80;
+    dma_to_lds(__builtin_amdgcn_make_buffer_rsrc((void *)factors, 0, fbytes, kBufWord3), lds + L.foff, fbytes, wave,
+               lane);
+    const float *fl = (const float *)(lds + L.foff);
+    bf16x8 A[3][2];
+    if ((int64_t)blockIdx.x < nTiles)
+        load_tile(blockIdx.x);
+    bool built = false;
+    for (int64_t tile = blockIdx.x; tile < nTiles; tile += gridDim.x) {
+        const int64_t r0 = tile * R;
+        const int rows = (int)((M - r0) < R ? (M - r0) : R);
+        // this wave's loads (and earlier stores) done, then everyone's
+        __builtin_amdgcn_s_waitcnt(kVm0);
+        __syncthreads();
+        asm volatile("" ::: "memory");
+        if (!per_block && !built) {
+            build_a_operands(A, fl, 0, lane);
+            built = true;
+        }
+
+        // statistics: wave w takes rows w and w + kRowsWaves together (their
+        // reductions interleave), each summed as a row alone
+        for (int r = wave; r < rows; r += 2 * kRowsWaves) {
+            const bool two = r + kRowsWaves < rows;
+            const unsigned char *xa = lds + r * L.xrow;
+            const unsigned char *xb = lds + (two ? r + kRowsWaves : r) * L.xrow;
+            double s1[2] = {0.0, 0.0}, s2[2] = {0.0, 0.0};
+            for (int o = lane; o < nOct; o += 64) {
+                adaln_piece_sums(*(const u32x4 *)(xa + o * 16), s1[0], s2[0]);
+                adaln_piece_sums(*(const u32x4 *)(xb + o * 16), s1[1], s2[1]);
+            }
+            double mu[2], rstd[2];
+            adaln_row_finish2(s1, s2, d, eps, mu, rstd);
+            if (lane < (two ? 2 : 1)) {
+                const int rr = r + lane * kRowsWaves;
+                const double m = lane ? mu[1] : mu[0], rs = lane ? rstd[1] : rstd[0];
+                *(double *)(lds + L.toff + rr * 16) = m;
+                *(double *)(lds + L.toff + rr * 16 + 8) = rs;
+                stats[2 * (r0 + rr)] = m;
+                stats[2 * (r0 + rr) + 1] = rs;
+            }
+        }
+        __syncthreads();
+
+        // blocks: normalise, transform, quantize into the staging tile
+        const int tr = tl < rows ? tl : rows - 1; // the lane's row (a copy of the last for tokens past it)
+        const double mu = *(const double *)(lds + L.toff + tr * 16);
+        const double rstd = *(const double *)(lds + L.toff + tr * 16 + 8);
+        const int64_t b0 = r0 / T;
+        const bool staged = (r0 + rows - 1) / T - b0 + 1 <= nmod;
+        const int64_t b = (r0 + tr) / T; // the lane's sample
+        const float *msh = staged ? (const float *)(lds + L.moff) + (b - b0) * d : shift + (b < nS ? b : nS - 1) * d;
+        const float *msc =
+            staged ? (const float *)(lds + L.moff + L.mbytes) + (b - b0) * d : scale + (b < nS ? b : nS - 1) * d;
+        const unsigned char *xrow = lds + tr * L.xrow;
+        for (int jb = wave; jb < nB; jb += kRowsWaves) {
+            if (per_block)
+                build_a_operands(A, fl + jb * 20, 0, lane);
+            bf16x8 bv[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int oct = jb * 4 + 2 * j + h2; // channels 32 jb + 16 j + 8 h .. +7
+                double g[8], sh[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    g[e] = 1.0 + (double)msc[oct * 8 + e];
+                    sh[e] = (double)msh[oct * 8 + e];
+                }
+                unsigned xw[4];
+                adaln_bf16x8(*(const u32x4 *)(xrow + oct * 16), mu, rstd, g, sh, xw);
+                bv[j] = __builtin_bit_cast(bf16x8, u32x4{xw[0], xw[1], xw[2], xw[3]});
+            }
+            f32x16 acc = {};
+            // smallest terms first: lo, mid, hi (as kq_mfma_kernel)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][j], bv[j], acc, 0, 0, 0);
+            float m = __builtin_fabsf(acc[0]);
+#pragma unroll
+            for (int v = 1; v < 16; ++v)
+                m = amax_step(m, acc[v]);
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            m = vmax(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+            const unsigned bs = e8m0_byte(m);
+            const float sc = scale_operand(bs);
+            unsigned w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
+            unsigned w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
+            if (bs == 0xFFu)
+                w0 = w1 = 0u;
+            if (tl < rows) {
+                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                *(u32x2 *)(lds + L.qoff + tl * L.qrow + jb * 16 + 8 * h2) = u32x2{w0, w1};
+                if (h2 == 0)
+                    lds[L.soff + tl * L.srow + jb] = (unsigned char)bs;
+            }
+        }
+        __syncthreads();
+
+        // the next tile's loads go out while this tile's codes and scales leave
+        if (tile + gridDim.x < nTiles)
+            load_tile(tile + gridDim.x);
+        const int pieces = d >> 5; // 16-byte code pieces per row
+        const __amdgpu_buffer_rsrc_t rq = out_buffer(q + r0 * (d >> 1), (int64_t)rows * (d >> 1));
+        for (int c = t; c < rows * pieces; c += 64 * kRowsWaves) {
+            const int row = c / pieces, pc = c - row * pieces;
+            const u32x4 v = *(const u32x4 *)(lds + L.qoff + row * L.qrow + pc * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rq, row * (d >> 1) + pc * 16, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rs = out_buffer(s + r0 * nB, (int64_t)rows * nB);
+        for (int c = t; c < rows * nB; c += 64 * kRowsWaves) {
+            const int row = c / nB, k = c - row * nB;
+            __builtin_amdgcn_raw_buffer_store_b8(lds[L.soff + row * L.srow + k], rs, row * nB + k, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming variants: one lane per 8 channels, a wave covers 512 channels
 // (16 blocks) of U rows at a time and walks a run of rows.
 // ---------------------------------------------------------------------------
@@ -692,6 +917,25 @@ int occupancy_per_cu(const void *fn, int threads)
     return per_cu;
 }
 
+namespace {
+std::map<std::pair<int, const void *>, hipError_t> g_lds_attr;
+} // namespace
+
+// Raise fn's dynamic LDS limit to `bytes` on the current device, once per
+// (device, kernel); later calls return the first call's result.
+hipError_t allow_dynamic_lds(const void *fn, int bytes)
+{
+    const int dev = current_device();
+    std::lock_guard<std::mutex> lock(g_info_mu);
+    const auto key = std::make_pair(dev, fn);
+    const auto it = g_lds_attr.find(key);
+    if (it != g_lds_attr.end())
+        return it->second;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    g_lds_attr[key] = e;
+    return e;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -920,6 +1164,62 @@ hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *
                                  : launch_mfma_instance<4, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
     return sh.nt_codes && !y ? launch_mfma_instance<8, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
                              : launch_mfma_instance<8, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+}
+
+// One-launch AdaLN form.  Rows per tile R: enough for every CU to take at most
+// one tile (at most 32, one matrix-core tile of tokens), fewer (down to 8) when
+// the LDS cannot hold that many.  Staged modulation: the most samples (2, 1, 0)
+// whose rows still fit beside them.  Grid: one resident round.
+constexpr int kAdRowsLds = 160 * 1024; // LDS of one CU (gfx950), all of it for one workgroup at most
+bool adaln_rows_shape(int64_t M, int64_t d, int64_t nT, AdRowsShape &sh)
+{
+    if (M < 1 || d > 65536)
+        return false;
+    const int nsets = nT > 1 ? (int)(d / 32) : 1;
+    const int64_t cus = device_cus();
+    int64_t need = (M + cus - 1) / cus;
+    if (need > 32)
+        need = 32;
+    const int floor_r = need < 8 ? (int)need : 8;
+    for (int r = (int)need; r >= floor_r; --r)
+        for (int nm = 2; nm >= 0; --nm) {
+            const AdRowsLayout L = adaln_rows_layout(r, (int)d, nsets, nm);
+            if (L.bytes > kAdRowsLds)
+                continue;
+            sh.R = r;
+            sh.nmod = nm;
+            sh.bytes = L.bytes;
+            const int64_t nTiles = (M + r - 1) / r;
+            int per_cu = kAdRowsLds / L.bytes;
+            const int occ = occupancy_per_cu((const void *)adaln_rows_kernel, 64 * kRowsWaves);
+            if (per_cu > occ)
+                per_cu = occ;
+            const int64_t slots = cus * (int64_t)(per_cu < 1 ? 1 : per_cu);
+            sh.grid = nTiles < slots ? nTiles : slots;
+            return true;
+        }
+    return false;
+}
+
+hipError_t launch_adaln_rows(const uint16_t *h, int64_t M, int64_t d, const float *shift, const float *scale,
+                             int64_t T, float eps, const float *factors, int64_t nT, double *stats, uint8_t *q,
+                             uint8_t *s, hipStream_t stream)
+{
+    AdRowsShape sh{};
+    if (!adaln_rows_shape(M, d, nT, sh))
+        return hipErrorInvalidConfiguration;
+    // above the default dynamic LDS limit the launch needs the attribute
+    hipError_t e = allow_dynamic_lds((const void *)adaln_rows_kernel, kAdRowsLds);
+    if (e != hipSuccess)
+        return e;
+    int di = (int)d;
+    int per_block = nT > 1 ? 1 : 0;
+    int R = sh.R, nmod = sh.nmod;
+    void *args[] = {(void *)&h,     (void *)&M,       (void *)&di,        (void *)&shift, (void *)&scale,
+                    (void *)&T,     (void *)&eps,     (void *)&factors,   (void *)&per_block,
+                    (void *)&stats, (void *)&q,       (void *)&s,         (void *)&R,     (void *)&nmod};
+    return hipLaunchKernel((const void *)adaln_rows_kernel, dim3((unsigned)sh.grid), dim3(64 * kRowsWaves), args,
+                           (unsigned)sh.bytes, stream);
 }
 
 // Second pass of the AdaLN front-end on the matrix cores: the quantizer's

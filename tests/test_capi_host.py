@@ -370,7 +370,7 @@ def test_tuning_validation():
     x, q, s, f, y = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
     bad = [("mfma_tiles_per_wg", 257), ("mfma_tiles_per_wg", -1), ("mfma_groups", 3), ("mfma_strip", 12), ("mfma_strip", 2),
            ("mfma_order", 3), ("code_stores", 3), ("stream_rows_per_wave", 300), ("gemm_kernel", 4),
-           ("adaln_pass", 3), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000)]
+           ("adaln_pass", 4), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000)]
     for field, val in bad:
         t = ctypes.byref(K.Tuning(**{field: val}))
         assert raw("kq_quantize_tuned", x, 4, 64, f, 1, q, s, 0, t, None) == K.KQ_ERR_ARG, field

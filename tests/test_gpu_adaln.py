@@ -9,7 +9,9 @@ Bars:
     transform of that x under tests/parity.py's rules, with every block that
     holds a flagged x element flagged as well;
   - kq_adaln_quantize equals kq_quantize(adaln_modulate(h)) bit for bit (the
-    fused kernels compute what the unfused pipeline stores and reads back);
+    fused kernels compute what the unfused pipeline stores and reads back),
+    in the two-launch forms (the default) and in the one-launch form (whole
+    rows in LDS, selected by the tuning);
     with the butterfly second pass selected it equals
     kq_quantize_ex(adaln_modulate(h), BUTTERFLY) bit for bit.
 Every case prints its name, shape and seed before it touches the GPU.
@@ -145,11 +147,13 @@ def test_adaln_special_rows(K):
     assert np.array_equal(xg[0], xb[0])
 
 
-# launch-shape overrides of kq_adaln_quantize: the second pass (1 matrix
-# cores, 2 butterfly) and the matrix-core strip width (4 or 8 blocks)
+# launch-shape overrides of kq_adaln_quantize: two launches with the second
+# pass on the matrix cores (strips of 4 or 8 blocks) or the butterfly one, or
+# one launch with whole rows in LDS (every case here fits it)
 PASS_FORMS = [("mfma_strip4", {"adaln_pass": 1, "adaln_strip": 4}, None),
               ("mfma_strip8", {"adaln_pass": 1, "adaln_strip": 8}, None),
-              ("butterfly", {"adaln_pass": 2}, "KQ_VARIANT_BUTTERFLY")]
+              ("butterfly", {"adaln_pass": 2}, "KQ_VARIANT_BUTTERFLY"),
+              ("one_launch", {"adaln_pass": 3}, None)]
 FORM_CASES = [(37, 1152, 16), (130, 1152, 3), (67, 2240, 32), (9, 8192, 4), (300, 96, 1), (4100, 3072, 2048),
               (97, 1152, 40), (70, 8192, 35), (200, 544, 33)]
 
@@ -175,6 +179,25 @@ def test_adaln_second_pass_forms(K, form, knobs, variant):
                 q2, s2 = K.kq_quantize(x, fd, variant=getattr(K, variant))
             torch.cuda.synchronize()
             assert torch.equal(q, q2) and torch.equal(s, s2), f"{form} {M}x{d}: fused != unfused"
+
+
+def test_adaln_stats_agree_across_forms(K):
+    # the one-launch form sums each row from LDS in the statistics kernel's
+    # order, so the workspace holds the same doubles bit for bit as after the
+    # two-launch form and after adaln_modulate
+    for M, d, T in ((37, 1152, 16), (300, 2240, 64), (130, 3072, 40), (5, 12288, 2)):
+        say(f"[adaln stats forms] M={M} d={d} T={T}")
+        h = I.act_dit_lognormal(M, d, 8350 + M)[0]
+        shift, scale = I.adaln_modulation((M + T - 1) // T, d, 8351 + M)
+        hd, sh, sc = dev_bf16(h), dev_f32(shift), dev_f32(scale)
+        fd = dev_f32(I.random_factors(d // 32, 8352 + M))
+        ws = [torch.full((M, 2), float("nan"), dtype=torch.float64, device="cuda") for _ in range(3)]
+        K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd, stats=ws[0], tuning={"adaln_pass": 3})
+        K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd, stats=ws[1], tuning={"adaln_pass": 1})
+        K.adaln_modulate(hd, sh, sc, T, EPS, stats=ws[2])
+        torch.cuda.synchronize()
+        a, b, c = (w.cpu().numpy().view(np.uint64) for w in ws)
+        assert np.array_equal(a, b) and np.array_equal(a, c), f"{M}x{d}: statistics differ between forms"
 
 
 def test_adaln_stats_workspace(K):
