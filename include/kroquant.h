@@ -196,8 +196,10 @@ int kq_transform16_f32(const uint16_t *x, int64_t M, int64_t d, const float *fac
  * of every 32-channel block and MXFP4 as kq_quantize.  The normalised x is
  * never written: one pass writes the row statistics into `stats`, a second
  * reads h again, normalises it while staging it for the matrix cores, and
- * quantizes.  The transform is the default (KQ_VARIANT_MFMA) form; the result
- * equals kq_quantize(adaln_modulate(h), ...) bit for bit.
+ * quantizes (kq_adaln_quantize_tuned can select a one-launch form instead,
+ * which holds whole rows in LDS; same results and statistics, bit for bit).
+ * The transform is the default (KQ_VARIANT_MFMA) form; the result equals
+ * kq_quantize(adaln_modulate(h), ...) bit for bit.
  *   h      dev, bf16 [M, d] (the residual stream), 16-byte aligned
  *   shift  dev, float32 [ceil(M / tokens_per_sample), d], 4-byte aligned
  *   scale  dev, float32, same shape and alignment as shift
