@@ -1095,6 +1095,45 @@ bool mfma_long_run(int64_t M, int64_t d, MfmaShape &sh)
     return true;
 }
 
+// Mid-size runs: one resident round of at most one workgroup per CU, whose
+// interleaved token groups (flat order) each walk 6..16 tiles.  Of strips of
+// 16 and 8 blocks (whichever divide the row) the one that gives the longer
+// runs inside that range is taken.  Used when the shape above would put more
+// than one workgroup on a CU or walk fewer than 8 tiles per workgroup
+// (measured on two boxes against that shape: 4608 x 3072 10.1 against 11.2
+// us, 2048 x 8960 12.0 against 12.8, 4608 x 12288 27.3 against 29.3, 4096 x
+// 12288 24.7 against 25.5, 2048 x 12288 14.4 against 15.0; at 8192 x 4608,
+// where that shape already is one round of 11 tiles per workgroup, this one
+// was 2% slower, so it is not taken there).  Leaves sh unchanged when no
+// strip gives such a round.
+void mfma_one_per_cu(int64_t M, int64_t d, MfmaShape &sh)
+{
+    const int64_t nB = d / 32;
+    const int64_t nTiles = (M + kTileT - 1) / kTileT;
+    const int64_t cus = device_cus();
+    int best_w = 0;
+    int64_t best_t = 0;
+    for (const int w : {16, 8}) {
+        if (nB % w != 0)
+            continue;
+        const int64_t groups = cus / (nB / w);
+        if (groups < 1)
+            continue;
+        const int64_t tpw = (nTiles + groups - 1) / groups;
+        if (tpw >= 6 && tpw <= 16 && tpw > best_t) {
+            best_w = w;
+            best_t = tpw;
+        }
+    }
+    if (best_w == 0)
+        return;
+    sh.strip = best_w;
+    sh.tiles_per_wg = (int)best_t;
+    sh.interleave = 1;
+    sh.flat = 1;
+    sh.grid = (nTiles + best_t - 1) / best_t * (nB / best_w);
+}
+
 hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln, MfmaShape &sh)
 {
     const int64_t nB = d / 32;
@@ -1141,8 +1180,11 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
             }
         }
     }
-    if (!long_run)
+    if (!long_run) {
         mfma_groups(M, d, w, adaln, tn, sh);
+        if (!adaln && automatic && (sh.grid > device_cus() || sh.tiles_per_wg < 8))
+            mfma_one_per_cu(M, d, sh);
+    }
     const double footprint = (double)M * (double)d * (2.0 + 0.5 + 1.0 / 32.0);
     sh.nt_codes = !adaln && (tn.code_stores == 2 || (tn.code_stores == 0 && footprint > (double)kMallBytes));
     return sh.grid > 0x7FFFFFFF ? hipErrorInvalidConfiguration : hipSuccess;
