@@ -16,9 +16,12 @@ scales.
   comparison = in the same run and on the same input: 384 per-block factor sets,
               the SmoothQuant kernel, the butterfly variant, the K2 (LU) form,
               the Walsh-Hadamard-32 kernel and the 4:1 copy ceiling (every copy
-              form, the fastest reported); plus per-shape entries for the DiT
-              CFG batch (8192 x 1152, 8192 x 4608) and the double-stream
-              12288-wide input (4608 x 12288)
+              form, the fastest reported); plus per-shape entries (KroQuant,
+              SmoothQuant, copy ceiling) for every other configured workload
+              but the tiny one: the DiT CFG batch (8192 x 1152, 8192 x 4608),
+              the mid widths (2048 x 2240, 2048 x 8960), the double-stream
+              inputs (4608 x 3072, 4608 x 12288) and the sweep (4096 and
+              16384 x 12288)
   cpu_baseline = the CPU oracle on the first 4096 rows of the same input
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
@@ -50,7 +53,11 @@ HBM_PEAK_GBS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 ROTATE_BYTES = 1 << 30
 HEADLINE = ("sweep_65536", 65536, 12288)
-PER_SHAPE = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608), ("dbl_12288", 4608, 12288)]
+# every other configured workload except the tiny one, KroQuant (its configured
+# factors), SmoothQuant and the copy ceiling each
+PER_SHAPE = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608), ("mid_2240", 2048, 2240), ("mid_8960", 2048, 8960),
+             ("dbl_3072", 4608, 3072), ("dbl_12288", 4608, 12288), ("sweep_4096", 4096, 12288),
+             ("sweep_16384", 16384, 12288)]
 KERNEL_SYMBOL = "kq_mfma_kernel<true"
 RAMP_S = 0.3  # untimed replays before the warm-up steps, for the GPU clocks to leave their idle state
 CPU_ROWS = 4096  # rows of the headline input the CPU oracle is timed on
@@ -806,7 +813,7 @@ def main():
                      "GB/s at 2.5 B per element)",
         }
         del scale_d
-        # ---- per-shape entries: the DiT CFG batch and the double-stream 12288-wide input
+        # ---- per-shape entries: every other configured workload but the tiny one
         per_shape = {}
         for sname, sM, sd in PER_SHAPE:
             xs = I.make_activation(sname)
