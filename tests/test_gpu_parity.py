@@ -388,6 +388,29 @@ def test_kq_mfma_strip_widths(K, strip, M, d, shared):
     assert np.all(err <= P.TOL * z + P.TOL_ABS), float((err / (z + 1e-300)).max())
 
 
+# The automatic launch shapes the library documents for MI355X (256 CUs), so a
+# change of the launch rules shows up here: the persistent round of long runs,
+# the one-round-per-CU shape of mid-size runs, the XCD-grouped round at 8192 x
+# 4608 and contiguous groups in strips of 4 at 8192 x 1152.
+AUTO_SHAPES = [((65536, 12288), dict(strip=16, tiles_per_wg=205, interleave=1, flat=1, grid=240, nt_codes=1)),
+               ((16384, 12288), dict(strip=16, tiles_per_wg=52, interleave=1, flat=1, grid=240, nt_codes=1)),
+               ((8192, 4608), dict(strip=16, tiles_per_wg=11, interleave=1, flat=0, grid=216, nt_codes=0)),
+               ((8192, 1152), dict(strip=4, tiles_per_wg=6, interleave=0, flat=0, grid=432, nt_codes=0)),
+               ((4608, 3072), dict(strip=8, tiles_per_wg=7, interleave=1, flat=1, grid=252, nt_codes=0)),
+               ((4608, 12288), dict(strip=16, tiles_per_wg=15, interleave=1, flat=1, grid=240, nt_codes=0)),
+               ((2048, 8960), dict(strip=8, tiles_per_wg=10, interleave=1, flat=1, grid=245, nt_codes=0))]
+
+
+@pytest.mark.parametrize("shape,want", AUTO_SHAPES, ids=[f"{m}x{d}" for (m, d), _ in AUTO_SHAPES])
+def test_automatic_launch_shapes(K, shape, want):
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the documented shapes are those of a 256-CU MI355X")
+    M, d = shape
+    got = K.kq_launch_shape(M, d)
+    say(f"[launch shape] {M}x{d}: {got}")
+    assert got == want
+
+
 # ---------------------------------------------------------------------------
 # K2 form: factor sets as 15 LU scalars, rebuilt in the kernel
 # ---------------------------------------------------------------------------
