@@ -24,7 +24,7 @@ scales.
               16384 x 12288)
   cpu_baseline = the CPU oracle on the first 4096 rows of the same input
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu] [--no-per-shape]
 
 HBM traffic (the roofline's "traffic" field) comes from two rocprofv3 counter
 passes over `bench.py --traffic-run` (FETCH_SIZE, then WRITE_SIZE), which
@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="skip the comparison legs and per-shape entries")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-per-shape", action="store_true",
+                    help="skip the per-shape entries (the comparison legs at the headline shape still run)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU-oracle baseline")
     ap.add_argument("--traffic-run", action="store_true",
                     help="eager calibration copy + quantizer steps only, for rocprofv3 counter passes")
@@ -82,6 +84,9 @@ def parse():
                     help="W4A4 consumer (mx_gemm) on the DiT layer shapes, against its roofline")
     ap.add_argument("--gemm-library", action="store_true",
                     help="mx_gemm against torch's MXFP4 scaled_mm (hipBLASLt) on the qkv and proj layer shapes")
+    ap.add_argument("--summarize-trace-runs", metavar="KERNEL_TRACE_CSV",
+                    help="per-leg kernel times from a rocprofv3 --kernel-trace csv: runs of consecutive dispatches "
+                         "of one kernel and grid (no GPU needed)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic profile from two rocprofv3 --pmc output folders (no GPU needed)")
     return ap.parse_args()
@@ -130,6 +135,31 @@ def _read_counters(folder):
     if not rows:
         raise SystemExit(f"no counter_collection.csv under {folder}")
     return sorted(rows)
+
+
+def summarize_trace_runs(path, min_calls=5):
+    """Kernel durations of a rocprofv3 --kernel-trace csv, split into runs of
+    consecutive dispatches of one kernel at one grid size: each timed leg of
+    this script is such a run (its ramp, warm-up and timed graph), so a
+    run's statistics are that leg's kernel time.  Prints one line per run of
+    at least min_calls dispatches."""
+    import csv
+    import re
+    with open(path) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows:
+        key = (re.sub(r"\(.*", "", r["Kernel_Name"]), r.get("Grid_Size_X", ""))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(dur)
+        else:
+            runs.append([key, [dur]])
+    for i, ((name, grid), v) in enumerate(runs):
+        if len(v) < min_calls:
+            continue
+        v = sorted(v)
+        print(f"| {i} | `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | {v[0]:.2f} |")
 
 
 def summarize_traffic(fetch_dir, write_dir):
@@ -637,6 +667,9 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
+    if args.summarize_trace_runs:
+        summarize_trace_runs(args.summarize_trace_runs)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantizer shards by "
               f"rows with no communication, so N GPUs run N independent copies of this step)", file=sys.stderr)
@@ -815,7 +848,7 @@ def main():
         del scale_d
         # ---- per-shape entries: every other configured workload but the tiny one
         per_shape = {}
-        for sname, sM, sd in PER_SHAPE:
+        for sname, sM, sd in ([] if args.no_per_shape else PER_SHAPE):
             xs = I.make_activation(sname)
             fs = torch.from_numpy(I.make_factors(sname)).to(dev)
             ss = torch.from_numpy(I.smoothquant_scale(xs)).to(dev)
