@@ -200,6 +200,26 @@ def test_adaln_stats_agree_across_forms(K):
         assert np.array_equal(a, b) and np.array_equal(a, c), f"{M}x{d}: statistics differ between forms"
 
 
+def test_adaln_one_launch_too_wide(K):
+    # a row too wide for the one-launch form's LDS (one row of h, its codes and
+    # the staging need more than 160 KB at d = 65536): the forced form returns
+    # KQ_ERR_HIP and launches nothing; the automatic form runs two launches
+    M, d, T = 2, 65536, 2
+    say(f"[adaln one-launch too wide] M={M} d={d}")
+    h = I.act_dit_lognormal(M, d, 8360)[0]
+    shift, scale = I.adaln_modulation(1, d, 8361)
+    hd, sh, sc = dev_bf16(h), dev_f32(shift), dev_f32(scale)
+    fd = dev_f32(I.random_factors(d // 32, 8362))
+    with pytest.raises(K.KQError) as ei:
+        K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd, tuning={"adaln_pass": 3})
+    assert ei.value.status == K.KQ_ERR_HIP
+    q, s = K.kq_adaln_quantize(hd, sh, sc, T, EPS, fd)
+    x = K.adaln_modulate(hd, sh, sc, T, EPS)
+    q2, s2 = K.kq_quantize(x, fd)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2)
+
+
 def test_adaln_stats_workspace(K):
     # the caller's workspace holds each row's mean and 1/sqrt(var + eps) in
     # double after the call (numpy's float64 statistics of the same bf16 rows)
