@@ -13,10 +13,12 @@ scales.
               algorithmic bytes = 2.53125 B per element (2 read, 0.5 + 1/32 written)
   roofline  = the quantizer kernel's average launch against the 8 TB/s HBM peak,
               timed with HIP events on the launch stream around the timed graph
-  comparison = in the same run and on the same input: 384 per-block factor sets,
-              the SmoothQuant kernel, the butterfly variant, the K2 (LU) form,
-              the Walsh-Hadamard-32 kernel and the 4:1 copy ceiling (every copy
-              form, the fastest reported); plus per-shape entries (KroQuant,
+  comparison = in the same run and on the same input: the strip kernel on the
+              same shared set, 384 per-block factor sets, the SmoothQuant
+              kernel, the butterfly variant, the K2 (LU) form, the
+              Walsh-Hadamard-32 kernel and the 4:1 copy ceiling (every copy
+              form, the fastest reported); plus per-shape entries (KroQuant with
+              the configuration's per-block sets and with one shared set,
               SmoothQuant, copy ceiling) for every other configured workload
               but the tiny one: the DiT CFG batch (8192 x 1152, 8192 x 4608),
               the mid widths (2048 x 2240, 2048 x 8960), the double-stream
@@ -53,12 +55,12 @@ HBM_PEAK_GBS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 ROTATE_BYTES = 1 << 30
 HEADLINE = ("sweep_65536", 65536, 12288)
-# every other configured workload except the tiny one, KroQuant (its configured
-# factors), SmoothQuant and the copy ceiling each
+# every other configured workload except the tiny one: KroQuant (its configured
+# per-block factor sets, and one shared set), SmoothQuant and the copy ceiling each
 PER_SHAPE = [("dit_1152", 8192, 1152), ("dit_4608", 8192, 4608), ("mid_2240", 2048, 2240), ("mid_8960", 2048, 8960),
              ("dbl_3072", 4608, 3072), ("dbl_12288", 4608, 12288), ("sweep_4096", 4096, 12288),
              ("sweep_16384", 16384, 12288)]
-KERNEL_SYMBOL = "kq_mfma_kernel<true"
+KERNEL_SYMBOL = "kq_flat_kernel<true"  # the headline's kernel (one shared factor set)
 RAMP_S = 0.3  # untimed replays before the warm-up steps, for the GPU clocks to leave their idle state
 CPU_ROWS = 4096  # rows of the headline input the CPU oracle is timed on
 
@@ -100,7 +102,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kq_mfma_sweep65536_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kq_flat_sweep65536_traffic.md")
 # calibration copy of the counter runs: bf16 -> fp32, 2^27 elements
 CAL_ELEMS = 1 << 27
 CAL_READ, CAL_WRITE = 2 * CAL_ELEMS, 4 * CAL_ELEMS
@@ -327,7 +329,8 @@ def best_copy(K, src_of, dst_of, nsets, steps):
 
 def all_configs(args):
     """Every configured shape (except the tiny smoke case): the MFMA quantizer
-    with per-block and with shared factors, the butterfly variant, SmoothQuant
+    with per-block factors (strip kernel) and with one shared set (flat kernel,
+    and the strip kernel beside it), the butterfly variant, SmoothQuant
     and the 4:1 copy ceiling, each as a graph of `--steps` launches over
     rotating buffers (>= 1 GB per cycle), timed with HIP events.  Inputs are
     N(0,1) bf16 with 1% outlier channels x50 drawn on the GPU (the kernels'
@@ -365,6 +368,8 @@ def all_configs(args):
         legs = {
             "kq_mfma_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=1),
             "kq_mfma_shared": lambda b: K.kq_quantize(b["x"], f_sh, b["q"], b["s"], stream=cur(), variant=1),
+            "kq_strip_shared": lambda b: K.kq_quantize(b["x"], f_sh, b["q"], b["s"], stream=cur(), variant=1,
+                                                       tuning={"shared_form": 1}),
             "kq_butterfly_perblock": lambda b: K.kq_quantize(b["x"], f_pb, b["q"], b["s"], stream=cur(), variant=2),
             "kq_lu_perblock": lambda b: K.kq_quantize_lu(b["x"], lu_pb, b["q"], b["s"], stream=cur()),
             "fwht": lambda b: K.fwht_quantize(b["x"], b["q"], b["s"], stream=cur()),
@@ -401,22 +406,27 @@ def all_configs(args):
         row["copy41"] = {"us": round(cp * 1e6, 2), "GB/s": round(elems * 2.5 / cp / 1e9, 1),
                          "hbm_pct": round(100 * elems * 2.5 / cp / 1e9 / HBM_PEAK_GBS, 1), "form": cp_form}
         row["kq_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_perblock"]["us"], 4)
+        row["kq_shared_over_sq_speed"] = round(row["smoothquant"]["us"] / row["kq_mfma_shared"]["us"], 4)
         row["kq_over_copy41_speed"] = round(row["copy41"]["us"] / row["kq_mfma_perblock"]["us"], 4)
         row["k2_lu_over_fwht_speed"] = round(row["fwht"]["us"] / row["kq_lu_perblock"]["us"], 4)
         table.append(row)
         print(json.dumps(row), flush=True)
         del bufs
         torch.cuda.empty_cache()
-    print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ MFMA shared us | KQ butterfly us | "
-          "K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | copy 4:1 us (GB/s) | KQ/SQ speed | "
-          "KQ/copy speed | K2/FWHT speed | KQ16 butterfly us (GB/s) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ shared, flat kernel us (GB/s, %peak) | "
+          "KQ shared, strip kernel us | KQ butterfly us | K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | "
+          "copy 4:1 us (GB/s) | KQ/SQ speed (per-block, shared) | KQ/copy speed | K2/FWHT speed | "
+          "KQ16 butterfly us (GB/s) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in table:
-        a, b, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_butterfly_perblock",
-                                                   "kq_lu_perblock", "fwht", "smoothquant", "copy41"))
-        print(f"| {r['config']} | {r['M']}x{r['d']} | {a['us']} ({a['GB/s']}, {a['hbm_pct']}%) | {b['us']} | "
+        a, b, bs, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_strip_shared",
+                                                       "kq_butterfly_perblock", "kq_lu_perblock", "fwht",
+                                                       "smoothquant", "copy41"))
+        print(f"| {r['config']} | {r['M']}x{r['d']} | {a['us']} ({a['GB/s']}, {a['hbm_pct']}%) | "
+              f"{b['us']} ({b['GB/s']}, {b['hbm_pct']}%) | {bs['us']} | "
               f"{c['us']} | {l2['us']} | {fw['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | "
-              f"{cp['us']} ({cp['GB/s']}) | {r['kq_over_sq_speed']} | {r['kq_over_copy41_speed']} | "
+              f"{cp['us']} ({cp['GB/s']}) | {r['kq_over_sq_speed']}, {r['kq_shared_over_sq_speed']} | "
+              f"{r['kq_over_copy41_speed']} | "
               f"{r['k2_lu_over_fwht_speed']} | {r['kq16_perblock']['us']} ({r['kq16_perblock']['GB/s']}) |", flush=True)
 
 
@@ -763,10 +773,9 @@ def main():
     value = step_bytes * args.steps / wall / 1e9
     avg_launch = ev / args.steps
     achieved = step_bytes / avg_launch / 1e9
-    shape = K.kq_launch_shape(M, d)
+    shape = K.kq_flat_launch_shape(M, d)
     src_hash = kernel_source_hash()
-    strip = shape["strip"]
-    kname = f"kq_mfma_kernel<true, {strip}, false, {'true' if shape['nt_codes'] else 'false'}>"
+    kname = f"kq_flat_kernel<true, {'true' if shape['nt_codes'] else 'false'}, {shape['ring']}>"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(src_hash),
                 "kernel": kname, "avg_launch_us": round(avg_launch * 1e6, 2), "launches_timed": args.steps,
@@ -812,6 +821,8 @@ def main():
         b = lambda i: sets[i]
         t = {
             "kq_hadamard_shared": avg_launch,
+            "kq_hadamard_shared_strip_kernel": leg(lambda i: K.kq_quantize(b(i)["x"], fh_d, b(i)["q"], b(i)["s"],
+                                                                           stream=cur(), tuning={"shared_form": 1})),
             "kq_perblock_384": leg(lambda i: K.kq_quantize(b(i)["x"], f_pb, b(i)["q"], b(i)["s"], stream=cur())),
             "kq_identity": leg(lambda i: K.kq_quantize(b(i)["x"], f_id, b(i)["q"], b(i)["s"], stream=cur())),
             "smoothquant": leg(lambda i: K.sq_quantize(b(i)["x"], scale_d, b(i)["q"], b(i)["s"], stream=cur())),
@@ -837,6 +848,7 @@ def main():
             "smoothquant_rows/s": legs["smoothquant"]["rows/s"],
             "smoothquant_hbm_pct": legs["smoothquant"]["hbm_pct"],
             "kroquant_over_smoothquant_speed": round(sq / avg_launch, 4),
+            "flat_over_strip_kernel_speed": round(t["kq_hadamard_shared_strip_kernel"] / avg_launch, 4),
             "kroquant_perblock_over_smoothquant_speed": round(sq / t["kq_perblock_384"], 4),
             "k2_lu_over_fwht_speed": round(t["fwht"] / t["k2_lu_perblock"], 4),
             "copy41_ceiling_GB/s": legs["copy41_ceiling"]["GB/s"],
@@ -851,6 +863,7 @@ def main():
         for sname, sM, sd in ([] if args.no_per_shape else PER_SHAPE):
             xs = I.make_activation(sname)
             fs = torch.from_numpy(I.make_factors(sname)).to(dev)
+            fsh = torch.from_numpy(I.make_factors(sname, shared=True)).to(dev)
             ss = torch.from_numpy(I.smoothquant_scale(xs)).to(dev)
             sbytes = sM * sd * BYTES_PER_ELEM
             ns = max(2, int(np.ceil(ROTATE_BYTES / sbytes)))
@@ -860,6 +873,8 @@ def main():
             torch.cuda.synchronize()
             kq_t = _time_leg(lambda i: K.kq_quantize(bufs[i]["x"], fs, bufs[i]["q"], bufs[i]["s"], stream=cur()),
                              ns, steps)
+            kqs_t = _time_leg(lambda i: K.kq_quantize(bufs[i]["x"], fsh, bufs[i]["q"], bufs[i]["s"], stream=cur()),
+                              ns, steps)
             sq_t = _time_leg(lambda i: K.sq_quantize(bufs[i]["x"], ss, bufs[i]["q"], bufs[i]["s"], stream=cur()),
                              ns, steps)
             cp_t, cp_form, _ = best_copy(K, lambda i: bufs[i]["x"], lambda i: bufs[i]["q"], ns, steps)
@@ -867,6 +882,10 @@ def main():
                 "M": sM, "d": sd, "nT": sd // 32, "launch_shape": K.kq_launch_shape(sM, sd),
                 "kq_us": round(kq_t * 1e6, 2), "kq_GB/s": round(sbytes / kq_t / 1e9, 1),
                 "kq_hbm_pct": round(100 * sbytes / kq_t / 1e9 / HBM_PEAK_GBS, 2), "kq_rows/s": round(sM / kq_t, 1),
+                "kq_shared_us": round(kqs_t * 1e6, 2), "kq_shared_GB/s": round(sbytes / kqs_t / 1e9, 1),
+                "kq_shared_hbm_pct": round(100 * sbytes / kqs_t / 1e9 / HBM_PEAK_GBS, 2),
+                "kq_shared_launch_shape": K.kq_flat_launch_shape(sM, sd),
+                "kq_shared_over_sq_speed": round(sq_t / kqs_t, 4),
                 "sq_us": round(sq_t * 1e6, 2), "sq_GB/s": round(sbytes / sq_t / 1e9, 1),
                 "sq_rows/s": round(sM / sq_t, 1), "kq_over_sq_speed": round(sq_t / kq_t, 4),
                 "copy41_us": round(cp_t * 1e6, 2), "copy41_form": cp_form,

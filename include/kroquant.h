@@ -78,6 +78,9 @@ extern "C" {
 /*
  * kq_quantize: KroQuant online quantizer.  For every block, y = x_blk . K_j in
  * fp32 accumulation, then MXFP4 quantization of y (abstract; key_machinery).
+ * With nT = d/32 (a set per block) the strip kernel runs; with nT = 1 (one set
+ * shared by every block) the flat kernel, which treats x as one run of M*d/32
+ * blocks.  Both compute the same values bit for bit.
  *   x        dev, bf16 bits [M, d], 16-byte aligned
  *   factors  dev, float32 [nT, 5, 2, 2], nT = 1 or d/32, 4-byte aligned
  *   q        dev, uint8 [M, d/2], 16-byte aligned
@@ -94,10 +97,11 @@ int kq_quantize_ex(const uint16_t *x, int64_t M, int64_t d, const float *factors
 
 /*
  * kq_transform_f32: the transformed values y = x_blk . K_j (fp32) that
- * kq_quantize quantizes, written out for inspection.  Same transform code and
- * the same launch shape (strip width, token groups, workgroup order) as
- * kq_quantize for the same (M, d); only the MX step is replaced by fp32
- * stores of y.  kq_transform_tuned (below) selects the butterfly variant.
+ * kq_quantize quantizes, written out for inspection.  Same transform code,
+ * same kernel and the same launch shape (strip kernel: strip width, token
+ * groups, workgroup order; flat kernel: ring depth and grid) as kq_quantize
+ * for the same (M, d, nT); only the MX step is replaced by fp32 stores of y.
+ * kq_transform_tuned (below) selects the butterfly variant.
  *   y  dev, float32 [M, d], 16-byte aligned
  */
 int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, float *y,
@@ -311,6 +315,11 @@ typedef struct kq_tuning {
                                       rows in LDS; KQ_ERR_HIP when they do not fit) */
     int32_t adaln_strip;           /* its matrix-core strip width: 4 or 8 blocks */
     int32_t adaln_blocks_per_wave; /* butterfly / adaln_modulate pass: row blocks per wave, 1..256 */
+    int32_t shared_form;           /* MFMA quantizer with one shared factor set: 1 the strip kernel, 2 the
+                                      flat kernel (the default when no mfma_* field is set) */
+    int32_t flat_wgs;              /* flat kernel: workgroups of 4 waves, 1..2^20 */
+    int32_t flat_ring;             /* flat kernel: register ring of 2 or 3 units of 32 blocks */
+    int32_t mfma_ring;             /* strip kernel (and the AdaLN second pass): register ring of 2 or 4 tiles */
 } kq_tuning;
 
 /* kq_quantize_ex / kq_transform_f32 / mx_gemm / kq_adaln_quantize with
@@ -327,13 +336,24 @@ int kq_adaln_quantize_tuned(const uint16_t *h, int64_t M, int64_t d, const float
                             int64_t tokens_per_sample, float eps, const float *factors, int64_t nT, double *stats,
                             uint8_t *q, uint8_t *s, const kq_tuning *tuning, void *stream);
 
-/* The launch shape the MFMA quantizer takes for an [M, d] input on the
- * current device (adaln = 1: the AdaLN second pass), with the given overrides
- * (NULL: automatic, as kq_quantize and kq_transform_f32).  shape receives
+/* The launch shape the strip kernel of the MFMA quantizer (per-block factor
+ * sets, or a shared set with an mfma_* override) takes for an [M, d] input on
+ * the current device (adaln = 1: the AdaLN second pass), with the given
+ * overrides (NULL: automatic, as kq_quantize and kq_transform_f32).  shape receives
  * {strip width in blocks, tiles per workgroup, interleaved (0/1), flat order
- * (0/1), grid size in workgroups, nontemporal code stores (0/1)}.  Queries the
- * device (occupancy); launches nothing.  Same argument errors as kq_quantize. */
-int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[6]);
+ * (0/1), grid size in workgroups, nontemporal code stores (0/1), register ring
+ * depth in tiles}.  Queries the device (occupancy); launches nothing.  Same
+ * argument errors as kq_quantize. */
+int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[7]);
+
+/* The launch shape of the flat form, the MFMA quantizer's kernel for one
+ * shared factor set (kq_quantize, kq_transform_f32, kq_quantize_lu and
+ * kq_transform_lu_f32 with nT = 1 and no strip override), for an [M, d]
+ * input on the current device with the given overrides (NULL: automatic).
+ * shape receives {register ring depth in units of 32 blocks, workgroups of 4
+ * waves, nontemporal code stores (0/1)}.  Queries the device; launches
+ * nothing.  Same argument errors as kq_quantize. */
+int kq_flat_launch_shape(int64_t M, int64_t d, const kq_tuning *tuning, int64_t shape[3]);
 
 /* Copy kernels with the quantizer's 4:1 read:write footprint, timed by the
  * benchmark as the practical HBM ceiling: src_bytes of src are read (16-byte
@@ -342,7 +362,7 @@ int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, in
  * sweeps (1..KQ_COPY_FORMS-1).  src: dev, 16-byte aligned, src_bytes a
  * multiple of 1024; dst: dev, 16-byte aligned, not overlapping src.  One
  * launch on `stream`. */
-#define KQ_COPY_FORMS 6
+#define KQ_COPY_FORMS 10
 int kq_measure_copy41(const void *src, int64_t src_bytes, void *dst, int form, void *stream);
 
 /* Text for a status code (static storage). */

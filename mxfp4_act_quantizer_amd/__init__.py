@@ -14,7 +14,8 @@ _BINDING_NAMES = (
     "EXPORTS", "KQ_ERR_ALIGN", "KQ_ERR_ARG", "KQ_ERR_HIP", "KQ_ERR_OVERLAP", "KQ_ERR_SHAPE", "KQ_ERR_SINGULAR",
     "KQ_OK", "KQ_VARIANT_AUTO", "KQ_VARIANT_BUTTERFLY", "KQ_VARIANT_MFMA", "LIB_PATH", "KQError",
     "kq_block_inverse", "kq_block_matrix", "kq_build_info", "kq_factor_inverse", "kq_fold_weight", "kq_quantize",
-    "kq_quantize_ex", "kq_status_string", "kq_transform_f32", "lib", "mx_quantize_f32", "kq_launch_shape", "Tuning", "TUNING_FIELDS", "KQ_COPY_FORMS",
+    "kq_quantize_ex", "kq_status_string", "kq_transform_f32", "lib", "mx_quantize_f32", "kq_launch_shape",
+    "kq_flat_launch_shape", "Tuning", "TUNING_FIELDS", "KQ_COPY_FORMS",
     "sq_quantize", "measure_copy41", "kq_quantize_lu", "kq_transform_lu_f32", "fwht_quantize",
     "fwht_transform_f32", "kq_lu_factors", "mx_gemm", "kq_adaln_quantize", "adaln_modulate",
     "kq_quantize16", "kq_transform16_f32", "kq_adaln_quantize_noalloc", "KQ_NOALLOC_MAX_ROWS",

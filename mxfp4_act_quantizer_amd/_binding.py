@@ -35,16 +35,18 @@ EXPORTS = (
     "kq_build_info", "kq_last_hip_error", "kq_hip_error_name",
     # measurement and test interface
     "kq_quantize_tuned", "kq_transform_tuned", "mx_gemm_tuned", "kq_adaln_quantize_tuned", "kq_launch_shape",
+    "kq_flat_launch_shape",
     "kq_measure_copy41",
     # for callers that cannot allocate
     "kq_adaln_quantize_noalloc",
 )
 KQ_NOALLOC_MAX_ROWS = 131072
-KQ_COPY_FORMS = 6
+KQ_COPY_FORMS = 10
 
 # launch-shape overrides (kq_tuning in kroquant.h); 0 keeps the automatic choice
 TUNING_FIELDS = ("mfma_tiles_per_wg", "mfma_groups", "mfma_strip", "mfma_order", "code_stores",
-                 "stream_rows_per_wave", "gemm_kernel", "adaln_pass", "adaln_strip", "adaln_blocks_per_wave")
+                 "stream_rows_per_wave", "gemm_kernel", "adaln_pass", "adaln_strip", "adaln_blocks_per_wave",
+                 "shared_form", "flat_wgs", "flat_ring", "mfma_ring")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m mxfp4_act_quantizer_amd.build` "
@@ -78,6 +80,7 @@ _lib.kq_transform_tuned.argtypes = [_P, _I64, _I64, _P, _I64, _P, _INT, _P, _P]
 _lib.mx_gemm_tuned.argtypes = [_P, _P, _I64, _P, _P, _I64, _I64, _P, _INT, _P, _P]
 _lib.kq_adaln_quantize_tuned.argtypes = [_P, _I64, _I64, _P, _P, _I64, ctypes.c_float, _P, _I64, _P, _P, _P, _P, _P]
 _lib.kq_launch_shape.argtypes = [_I64, _I64, _INT, _P, _P]
+_lib.kq_flat_launch_shape.argtypes = [_I64, _I64, _P, _P]
 _lib.sq_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P]
 _lib.mx_quantize_f32.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.kq_quantize_lu.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, _P]
@@ -229,10 +232,19 @@ def kq_transform_f32(x, factors, y=None, stream=None, variant=KQ_VARIANT_AUTO, t
 
 def kq_launch_shape(M, d, adaln=False, tuning=None):
     """Launch shape of the MFMA quantizer for [M, d] on the current device:
-    dict of strip, tiles_per_wg, interleave, flat, grid, nt_codes."""
-    out = (ctypes.c_int64 * 6)()
+    dict of strip, tiles_per_wg, interleave, flat, grid, nt_codes, ring."""
+    out = (ctypes.c_int64 * 7)()
     _check(_lib.kq_launch_shape(int(M), int(d), 1 if adaln else 0, _tuning(tuning), out), "kq_launch_shape")
-    return dict(zip(("strip", "tiles_per_wg", "interleave", "flat", "grid", "nt_codes"), (int(v) for v in out)))
+    return dict(zip(("strip", "tiles_per_wg", "interleave", "flat", "grid", "nt_codes", "ring"),
+                    (int(v) for v in out)))
+
+
+def kq_flat_launch_shape(M, d, tuning=None):
+    """Launch shape of the flat form (one shared factor set) for [M, d] on the
+    current device: dict of ring, workgroups, nt_codes."""
+    out = (ctypes.c_int64 * 3)()
+    _check(_lib.kq_flat_launch_shape(int(M), int(d), _tuning(tuning), out), "kq_flat_launch_shape")
+    return dict(zip(("ring", "workgroups", "nt_codes"), (int(v) for v in out)))
 
 
 def _nT_lu(lu):

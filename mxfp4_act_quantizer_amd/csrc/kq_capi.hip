@@ -82,7 +82,9 @@ int check_tuning(const kq_tuning *t)
                     (t->mfma_strip == 0 || t->mfma_strip == 4 || t->mfma_strip == 8 || t->mfma_strip == 16) && in(t->mfma_order, 1, 2) &&
                     in(t->code_stores, 1, 2) && in(t->stream_rows_per_wave, 1, 256) && in(t->gemm_kernel, 1, 3) &&
                     in(t->adaln_pass, 1, 3) && (t->adaln_strip == 0 || t->adaln_strip == 4 || t->adaln_strip == 8) &&
-                    in(t->adaln_blocks_per_wave, 1, 256);
+                    in(t->adaln_blocks_per_wave, 1, 256) && in(t->shared_form, 1, 2) &&
+                    in(t->flat_wgs, 1, 1 << 20) && in(t->flat_ring, 2, 3) &&
+                    (t->mfma_ring == 0 || t->mfma_ring == 2 || t->mfma_ring == 4);
     return ok ? KQ_OK : KQ_ERR_ARG;
 }
 
@@ -218,7 +220,7 @@ int kq_transform_f32(const uint16_t *x, int64_t M, int64_t d, const float *facto
     return kq_transform_tuned(x, M, d, factors, nT, y, KQ_VARIANT_AUTO, nullptr, stream);
 }
 
-int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[6])
+int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, int64_t shape[7])
 {
     int st = check_md(M, d);
     if (st)
@@ -236,6 +238,24 @@ int kq_launch_shape(int64_t M, int64_t d, int adaln, const kq_tuning *tuning, in
     shape[3] = sh.flat;
     shape[4] = sh.grid;
     shape[5] = sh.nt_codes;
+    shape[6] = sh.ring;
+    return KQ_OK;
+}
+
+int kq_flat_launch_shape(int64_t M, int64_t d, const kq_tuning *tuning, int64_t shape[3])
+{
+    int st = check_md(M, d);
+    if (st)
+        return st;
+    if (!shape)
+        return KQ_ERR_ARG;
+    if ((st = check_tuning(tuning)))
+        return st;
+    kq::FlatShape sh{};
+    kq::flat_launch_shape(M, d, tuning_of(tuning), sh);
+    shape[0] = sh.ring;
+    shape[1] = sh.wgs;
+    shape[2] = sh.nt_codes;
     return KQ_OK;
 }
 

@@ -29,8 +29,21 @@ struct MfmaShape {
     int flat;
     int64_t grid;
     int nt_codes; // 1 when the code stores are nontemporal
+    int ring;     // register ring depth in tiles (2 or 4)
 };
 hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln, MfmaShape &out);
+
+// Launch shape of the flat form (one shared factor set): register ring depth
+// in units of 32 blocks, workgroups of 4 waves, nontemporal code stores.
+// kq_quantize / kq_transform_f32 / the LU calls take this form when nT = 1
+// and no strip-kernel override is set (flat_form).
+struct FlatShape {
+    int ring;
+    int64_t wgs;
+    int nt_codes;
+};
+bool flat_form(int64_t nT, const Tuning &tn);
+void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &out);
 
 // factors: [nT,5,2,2] 2x2 factors (lu = 0) or [nT,5,3] LU scalars (lu = 1)
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,

@@ -191,6 +191,42 @@ __device__ __forceinline__ void stage_x(WgStage<kW> &st, int par, const XIn &in,
                          [(lane % S::kLanesPerRow) * 16] = in.v[k];
 }
 
+// The transform of one 32 x 32 MFMA tile: Y^T = K^T X^T with K^T in its three
+// exact bf16 terms, smallest first (lo, mid, hi), two k-steps of 16 each.
+// bv[j] holds, in lane (column c = l % 32, half h = l / 32), input channels
+// 16j + 8h .. +7 of column c's block.
+__device__ __forceinline__ f32x16 block_product(const bf16x8 (&A)[3][2], const bf16x8 (&bv)[2])
+{
+    f32x16 acc = {};
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][j], bv[j], acc, 0, 0, 0);
+    return acc;
+}
+
+// MX step of one MFMA tile: acc holds output channels 16h .. 16h+15 of the
+// lane's column block (h = l / 32), the other 16 sit in lane l ^ 32.  Returns
+// the block's E8M0 byte; w0, w1 receive the lane's 8 code bytes (all zero
+// for a NaN/Inf block).
+__device__ __forceinline__ unsigned mx_tile(const f32x16 &acc, unsigned &w0, unsigned &w1)
+{
+    float m = __builtin_fabsf(acc[0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v)
+        m = amax_step(m, acc[v]);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const unsigned b = e8m0_byte(m);
+    const float sc = scale_operand(b);
+    w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
+    w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
+    if (b == 0xFFu)
+        w0 = w1 = 0u;
+    return b;
+}
+
 // Transform one tile on the matrix cores; quantize into the staging buffer
 // (or write y directly).  Lane l takes token l%32 and, for MFMA j, channels
 // 16j + 8h .. +7 of block `wave` of the strip (h = l/32).
@@ -203,27 +239,10 @@ __device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<k
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         bv[j] = *(const bf16x8 *)&stc.x[par][tl][wave * 64 + 32 * j + 16 * h];
-    f32x16 acc = {};
-    // smallest terms first: lo, mid, hi
-#pragma unroll
-    for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][j], bv[j], acc, 0, 0, 0);
+    const f32x16 acc = block_product(A, bv);
     if constexpr (kQuant) {
-        float m = __builtin_fabsf(acc[0]);
-#pragma unroll
-        for (int v = 1; v < 16; ++v)
-            m = amax_step(m, acc[v]);
-        // the other 16 channels of the token sit in lane l^32
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        m = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
-        const unsigned b = e8m0_byte(m);
-        const float sc = scale_operand(b);
-        unsigned w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
-        unsigned w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
-        if (b == 0xFFu)
-            w0 = w1 = 0u;
+        unsigned w0, w1;
+        const unsigned b = mx_tile(acc, w0, w1);
         // lane half h holds q bytes 8h..8h+7 of block `wave` of the strip
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
         *(u32x2 *)&st.q[par][tl][wave * 16 + 8 * h] = u32x2{w0, w1};
@@ -287,11 +306,9 @@ __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool 
 // this tile from LDS into the staging buffer.  One barrier per tile orders all of it
 // (the LDS buffers alternate by tile parity).  Every load instruction is
 // issued unconditionally; those of look-ahead steps past the last tile have
-// an empty range and fetch nothing.
-#ifndef KQ_RING
-#define KQ_RING 4
-#endif
-constexpr int kRing = KQ_RING; // tiles in flight per wave: kRing - 1 ahead of the one being staged
+// an empty range and fetch nothing.  kRing: tiles in the register ring of a
+// wave, kRing - 1 of them in flight ahead of the one being staged (the
+// launcher picks 2 or 4).
 
 // With kAd the kernel is the second pass of the AdaLN front-end: x holds h,
 // and each lane normalises and modulates its two 16-byte pieces of a tile in
@@ -309,7 +326,7 @@ struct AdArgs {
 // compiler spills, and that measured no faster).
 constexpr int kAdOcc = 2;
 
-template <bool kQuant, int kW, bool kAd = false, bool kNT = false>
+template <bool kQuant, int kW, bool kAd = false, bool kNT = false, int kRing = 4>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? kAdOcc : 4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
@@ -447,6 +464,143 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
         __syncthreads();
         store_prev(n - 1);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Flat form of the MFMA quantizer, for one factor set shared by every block.
+//
+// With a single set every block goes through the same transform, so the row
+// structure plays no part: x is one flat run of M*d/32 blocks of 64 bytes, q
+// one of 16-byte code blocks and s one of scale bytes (block b at byte 64b,
+// 16b and b).  The 32 columns of an MFMA tile are 32 consecutive blocks, a
+// unit: per unit a wave reads 2 KB of contiguous x and writes 512 contiguous
+// code bytes and 32 scale bytes, with no LDS and no barrier.  The A operand,
+// the products and the MX step are those of kq_mfma_kernel (build_a_operands,
+// block_product, mx_tile), each column of a tile being computed alone, so the
+// two kernels give the same values bit for bit.
+//
+// Loads.  Step j of the product wants, in lane (column c = l % 32, half h =
+// l / 32), input channels 16j + 8h .. +7 of column c's block.  Load i (i = 0,
+// 1) reads 1 KB of contiguous x, blocks 16i .. 16i + 15 of the unit: lane
+// (c, h) takes the 16 bytes at 32 (c / 16) + 16h of block 16i + c % 16.  So
+// lanes with c < 16 receive step 0 of block 16i + c, lanes with c >= 16 step 1
+// of block 16i + c - 16.  One permlane16 swap per register (the odd 16-lane
+// rows of load 0 with the even rows of load 1) leaves load 0 holding step 0
+// and load 1 step 1 of block c, for every column c.
+//
+// Work split: wave g of G walks units g, g + G, g + 2G, ...: the waves keep
+// one compact band of x in flight, and the 4 units whose scale bytes share a
+// 128-byte line run on the 4 waves of one workgroup.  A register ring of kFR
+// units keeps kFR - 1 units of loads in flight while one is transformed (the
+// launcher picks kFR and G; few bytes in flight per CU measured fastest).
+// Buffer ranges hold exactly a unit's blocks below the end, so the missing
+// blocks of the last unit and the look-ahead past a wave's last unit fetch
+// and store nothing; every load and store instruction is issued
+// unconditionally (exact memory-counter waits, as in kq_mfma_kernel).
+// ---------------------------------------------------------------------------
+constexpr int kFlatWaves = 4; // waves per workgroup
+
+template <bool kQuant, bool kNT, int kFR>
+__global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t *__restrict__ x, int64_t nblk,
+                                                                  const float *__restrict__ factors, int lu,
+                                                                  uint8_t *__restrict__ q, uint8_t *__restrict__ s,
+                                                                  float *__restrict__ y)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const int lane = threadIdx.x & 63;
+    const int64_t G = (int64_t)gridDim.x * kFlatWaves;
+    const int64_t g = (int64_t)blockIdx.x * kFlatWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nunits = (nblk + 31) / 32;
+    if (g >= nunits)
+        return; // wave-uniform; this kernel has no barrier
+    const int n = (int)((nunits - g + G - 1) / G); // units of this wave
+    const int col = lane & 31, h = lane >> 5;
+    const unsigned xoff = (unsigned)(64 * (col & 15) + 32 * (col >> 4) + 16 * h);
+
+    // the wave's k-th unit (steps past its last unit name that unit again)
+    // and its blocks below the end (none past the last unit)
+    auto unit_of = [&](int k) -> int64_t { return g + (int64_t)(k < n ? k : n - 1) * G; };
+    auto blocks_of = [&](int k) -> int {
+        const int64_t left = nblk - unit_of(k) * 32;
+        return k < n ? (int)(left < 32 ? left : 32) : 0;
+    };
+    auto load_unit = [&](XIn &in, int k) {
+        const __amdgpu_buffer_rsrc_t rx =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(x + unit_of(k) * 1024), 0, blocks_of(k) * 64, kBufWord3);
+        in.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xoff, 0, kAuxNT));
+        in.v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xoff + 1024), 0, kAuxNT));
+    };
+    // outputs of unit u with nb blocks (nb = 0 drops every lane): lane (c, h)
+    // holds code bytes 8h .. 8h+7 of block c, and lanes h = 0 its scale byte;
+    // or (y) output channels 16h .. 16h+15 of block c
+    auto emit_q = [&](unsigned w0, unsigned w1, unsigned b, int64_t u, int nb) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, out_buffer(q + u * 512, nb * 16), 16 * col + 8 * h, 0,
+                                              kNT ? kAuxNT : 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, out_buffer(s + u * 32, nb),
+                                             (int)((unsigned)col | ((unsigned)h << 31)), 0, 0);
+    };
+    auto emit_y = [&](const f32x16 &acc, int64_t u, int nb) {
+        const __amdgpu_buffer_rsrc_t ry = out_buffer(y + u * 1024, nb * 128);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, f32x4{acc[4 * v], acc[4 * v + 1], acc[4 * v + 2], acc[4 * v + 3]}), ry,
+                128 * col + 64 * h + 16 * v, 0, 0);
+    };
+
+    // Each prologue load is followed by the step's stores with every lane
+    // dropped, so the memory counter holds the same sequence on entry to the
+    // loop as after a loop step.
+    XIn ring[kFR];
+#pragma unroll
+    for (int k = 0; k < kFR - 1; ++k) {
+        load_unit(ring[k], k);
+        if constexpr (kQuant)
+            emit_q(0u, 0u, 0u, 0, 0);
+        else
+            emit_y(f32x16{}, 0, 0);
+    }
+    bf16x8 A[3][2];
+    build_a_operands(A, factors, lu, lane);
+
+    // The scheduling barriers keep each step's work after its look-ahead load
+    // and before the next step's: hoisting the swaps of later units would
+    // move their memory-counter waits up and drain the ring.
+    auto step = [&](XIn &cur, XIn &ld, int kk) {
+        load_unit(ld, kk + kFR - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 b0, b1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const auto r = __builtin_amdgcn_permlane16_swap(cur.v[0][i], cur.v[1][i], false, false);
+            b0[i] = r[0];
+            b1[i] = r[1];
+        }
+        const bf16x8 bv[2] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1)};
+        const f32x16 acc = block_product(A, bv);
+        const int64_t u = g + (int64_t)kk * G;
+        const int64_t left = nblk - u * 32;
+        const int nb = (int)(left < 32 ? left : 32);
+        if constexpr (kQuant) {
+            unsigned w0, w1;
+            const unsigned b = mx_tile(acc, w0, w1);
+            emit_q(w0, w1, b, u, nb);
+        } else {
+            emit_y(acc, u, nb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int it = 0;
+    for (; it + kFR - 1 < n; it += kFR) {
+#pragma unroll
+        for (int k = 0; k < kFR; ++k)
+            step(ring[k], ring[(k + kFR - 1) % kFR], it + k);
+    }
+    // fewer than kFR units left, already in ring[0 ..]; their look-ahead loads are empty
+#pragma unroll
+    for (int k = 0; k < kFR - 1; ++k)
+        if (it + k < n)
+            step(ring[k], ring[kFR - 1], it + k);
 }
 
 // ---------------------------------------------------------------------------
@@ -628,25 +782,9 @@ __global__ __launch_bounds__(64 * kRowsWaves) void adaln_rows_kernel(
                 adaln_bf16x8(*(const u32x4 *)(xrow + oct * 16), mu, rstd, g, sh, xw);
                 bv[j] = __builtin_bit_cast(bf16x8, u32x4{xw[0], xw[1], xw[2], xw[3]});
             }
-            f32x16 acc = {};
-            // smallest terms first: lo, mid, hi (as kq_mfma_kernel)
-#pragma unroll
-            for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][j], bv[j], acc, 0, 0, 0);
-            float m = __builtin_fabsf(acc[0]);
-#pragma unroll
-            for (int v = 1; v < 16; ++v)
-                m = amax_step(m, acc[v]);
-            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-            m = vmax(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-            const unsigned bs = e8m0_byte(m);
-            const float sc = scale_operand(bs);
-            unsigned w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
-            unsigned w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
-            if (bs == 0xFFu)
-                w0 = w1 = 0u;
+            const f32x16 acc = block_product(A, bv);
+            unsigned w0, w1;
+            const unsigned bs = mx_tile(acc, w0, w1);
             if (tl < rows) {
                 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
                 *(u32x2 *)(lds + L.qoff + tl * L.qrow + jb * 16 + 8 * h2) = u32x2{w0, w1};
@@ -948,10 +1086,20 @@ int64_t mfma_wgs_per_xcd(const void *fn, int threads)
     return v < 1 ? 1 : v;
 }
 
-// The quantizing instance of a strip width: the launch shape of every form
-// (quantizer, transform export, nontemporal stores) is taken from its occupancy.
-const void *mfma_shape_fn(int w, bool adaln)
+// The quantizing instance of a strip width and ring depth: the launch shape of
+// every form (quantizer, transform export, nontemporal stores) is taken from
+// its occupancy.
+const void *mfma_shape_fn(int w, bool adaln, int ring)
 {
+    if (ring == 2) {
+        if (adaln)
+            return w == 4 ? (const void *)kq_mfma_kernel<true, 4, true, false, 2>
+                          : (const void *)kq_mfma_kernel<true, 8, true, false, 2>;
+        if (w == 4)
+            return (const void *)kq_mfma_kernel<true, 4, false, false, 2>;
+        return w == 16 ? (const void *)kq_mfma_kernel<true, 16, false, false, 2>
+                       : (const void *)kq_mfma_kernel<true, 8, false, false, 2>;
+    }
     if (adaln)
         return w == 4 ? (const void *)kq_mfma_kernel<true, 4, true> : (const void *)kq_mfma_kernel<true, 8, true>;
     if (w == 4)
@@ -966,12 +1114,12 @@ constexpr int64_t kMallBytes = (int64_t)256 << 20;
 
 // Token grouping for strip width w: tiles per workgroup, interleaved or
 // contiguous groups, flat or XCD-grouped order.
-void mfma_groups(int64_t M, int64_t d, int w, bool adaln, const Tuning &tn, MfmaShape &sh)
+void mfma_groups(int64_t M, int64_t d, int w, bool adaln, int ring, const Tuning &tn, MfmaShape &sh)
 {
     const int64_t nB = d / 32;
     const int64_t nBG = (nB + w - 1) / w;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const int64_t resident = mfma_wgs_per_xcd(mfma_shape_fn(w, adaln), 64 * w);
+    const int64_t resident = mfma_wgs_per_xcd(mfma_shape_fn(w, adaln, ring), 64 * w);
     int64_t tpw = tn.mfma_tiles_per_wg;
     int interleave = tn.mfma_groups == 2 ? 1 : 0;
     bool flat = tn.mfma_order == 2;
@@ -1041,7 +1189,7 @@ void mfma_groups(int64_t M, int64_t d, int w, bool adaln, const Tuning &tn, Mfma
     sh.grid = nGpad * nBG;
 }
 
-template <int kW, bool kAd, bool kNT>
+template <int kW, bool kAd, bool kNT, int kRing>
 hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
                                 uint8_t *q, uint8_t *s, float *y, int lu, const MfmaShape &sh, hipStream_t stream,
                                 AdArgs ad)
@@ -1050,9 +1198,10 @@ hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const f
         return hipErrorInvalidConfiguration;
     const void *fn;
     if constexpr (kAd)
-        fn = (const void *)kq_mfma_kernel<true, kW, true>;
+        fn = (const void *)kq_mfma_kernel<true, kW, true, false, kRing>;
     else
-        fn = y ? (const void *)kq_mfma_kernel<false, kW> : (const void *)kq_mfma_kernel<true, kW, false, kNT>;
+        fn = y ? (const void *)kq_mfma_kernel<false, kW, false, false, kRing>
+               : (const void *)kq_mfma_kernel<true, kW, false, kNT, kRing>;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
     int nbg = (int)((d / 32 + kW - 1) / kW);
@@ -1080,7 +1229,7 @@ bool mfma_long_run(int64_t M, int64_t d, MfmaShape &sh)
     const int w = nB % 16 == 0 ? 16 : 8;
     const int64_t nBG = (nB + w - 1) / w;
     const int64_t nTiles = (M + kTileT - 1) / kTileT;
-    const int64_t slots = mfma_wgs_per_xcd(mfma_shape_fn(w, false), 64 * w) * kXcds;
+    const int64_t slots = mfma_wgs_per_xcd(mfma_shape_fn(w, false, 2), 64 * w) * kXcds;
     const int64_t groups = slots / nBG;
     if (groups < 1 || 5 * groups * nBG < 4 * slots)
         return false;
@@ -1170,7 +1319,7 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
         } else if (w != 4 && w != 8 && w != 16) {
             w = 8;
             if (nB % 16 == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups != 1) {
-                int64_t gx = mfma_wgs_per_xcd(mfma_shape_fn(16, false), 64 * 16) / (nB / 16);
+                int64_t gx = mfma_wgs_per_xcd(mfma_shape_fn(16, false, 2), 64 * 16) / (nB / 16);
                 if (gx < 1)
                     gx = 1;
                 const int64_t nTiles = (M + kTileT - 1) / kTileT;
@@ -1180,32 +1329,97 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
             }
         }
     }
+    // Register ring: 2 tiles (one in flight ahead) except in the longest
+    // persistent runs and the AdaLN second pass, which keep 4.  Measured with
+    // per-block factor sets against rings of 3 and 4: 2-8% faster at every
+    // configured shape up to 16384 x 12288 (8192 x 1152: 7.4 against 8.1 us;
+    // 16384 x 12288: 83.3 against 86.2 us), 3.5% slower at 65536 x 12288 (205
+    // tiles per workgroup: 338 against 327 us).
+    const int ring = tn.mfma_ring ? tn.mfma_ring : (adaln || (long_run && sh.tiles_per_wg > 128)) ? 4 : 2;
     if (!long_run) {
-        mfma_groups(M, d, w, adaln, tn, sh);
+        mfma_groups(M, d, w, adaln, ring, tn, sh);
         if (!adaln && automatic && (sh.grid > device_cus() || sh.tiles_per_wg < 8))
             mfma_one_per_cu(M, d, sh);
     }
+    sh.ring = ring;
     const double footprint = (double)M * (double)d * (2.0 + 0.5 + 1.0 / 32.0);
     sh.nt_codes = !adaln && (tn.code_stores == 2 || (tn.code_stores == 0 && footprint > (double)kMallBytes));
     return sh.grid > 0x7FFFFFFF ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
+template <int kRing>
+hipError_t launch_mfma_ring(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
+                            uint8_t *s, float *y, int lu, const MfmaShape &sh, hipStream_t stream)
+{
+    const AdArgs ad{};
+    const bool nt = sh.nt_codes && !y;
+    if (sh.strip == 16)
+        return nt ? launch_mfma_instance<16, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                  : launch_mfma_instance<16, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+    if (sh.strip == 4)
+        return nt ? launch_mfma_instance<4, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                  : launch_mfma_instance<4, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+    return nt ? launch_mfma_instance<8, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+              : launch_mfma_instance<8, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+}
+
+// Flat form (one shared factor set).  Measured on MI355X over the configured
+// shapes (rotating inputs, graphs of 40 launches; ring depths 2..10 against
+// 128..1024 workgroups of 4 waves): the fastest launches keep few loads in
+// flight.  While x, q and s together fit the last-level cache: a ring of 2
+// units and 2 workgroups per CU (8192 x 4608: 16.7 us; rings of 3-5 or 1, 3
+// or 4 workgroups per CU 17.5-23.0).  Above it: a ring of 3 units and one
+// workgroup per CU (65536 x 12288: 322 us; a ring of 2 at 2 per CU 379, any
+// ring at 3 or 4 per CU 380-400).  Fractions of a workgroup per CU leave the
+// CUs unevenly loaded and were slower at every size.
+bool flat_form(int64_t nT, const Tuning &tn)
+{
+    if (nT != 1 || tn.shared_form == 1)
+        return false;
+    return tn.shared_form == 2 ||
+           (tn.mfma_strip == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups == 0 && tn.mfma_order == 0);
+}
+
+void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &sh)
+{
+    const double footprint = (double)M * (double)d * (2.0 + 0.5 + 1.0 / 32.0);
+    const bool big = footprint > (double)kMallBytes;
+    sh.nt_codes = tn.code_stores == 2 || (tn.code_stores == 0 && big);
+    sh.ring = tn.flat_ring ? tn.flat_ring : (big ? 3 : 2);
+    int64_t wgs = tn.flat_wgs > 0 ? tn.flat_wgs : (int64_t)(big ? 1 : 2) * device_cus();
+    const int64_t nunits = (M * (d / 32) + 31) / 32;
+    const int64_t need = (nunits + kFlatWaves - 1) / kFlatWaves;
+    sh.wgs = wgs < need ? wgs : need;
+}
+
+hipError_t launch_kq_flat(const uint16_t *x, int64_t M, int64_t d, const float *factors, uint8_t *q, uint8_t *s,
+                          float *y, int lu, const Tuning &tn, hipStream_t stream)
+{
+    FlatShape sh{};
+    flat_launch_shape(M, d, tn, sh);
+    const int64_t nblk = M * (d / 32);
+    const void *fn;
+    if (sh.ring == 3)
+        fn = y ? (const void *)kq_flat_kernel<false, false, 3>
+             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 3> : (const void *)kq_flat_kernel<true, false, 3>;
+    else
+        fn = y ? (const void *)kq_flat_kernel<false, false, 2>
+             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 2> : (const void *)kq_flat_kernel<true, false, 2>;
+    void *args[] = {(void *)&x, (void *)&nblk, (void *)&factors, (void *)&lu, (void *)&q, (void *)&s, (void *)&y};
+    return hipLaunchKernel(fn, dim3((unsigned)sh.wgs), dim3(64 * kFlatWaves), args, 0, stream);
+}
+
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                           uint8_t *s, float *y, int lu, const Tuning &tn, hipStream_t stream)
 {
+    if (flat_form(nT, tn))
+        return launch_kq_flat(x, M, d, factors, q, s, y, lu, tn, stream);
     MfmaShape sh{};
     hipError_t e = mfma_launch_shape(M, d, tn, false, sh);
     if (e != hipSuccess)
         return e;
-    const AdArgs ad{};
-    if (sh.strip == 16)
-        return sh.nt_codes && !y ? launch_mfma_instance<16, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-                                 : launch_mfma_instance<16, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
-    if (sh.strip == 4)
-        return sh.nt_codes && !y ? launch_mfma_instance<4, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-                                 : launch_mfma_instance<4, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
-    return sh.nt_codes && !y ? launch_mfma_instance<8, false, true>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-                             : launch_mfma_instance<8, false, false>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+    return sh.ring == 2 ? launch_mfma_ring<2>(x, M, d, factors, nT, q, s, y, lu, sh, stream)
+                        : launch_mfma_ring<4>(x, M, d, factors, nT, q, s, y, lu, sh, stream);
 }
 
 // One-launch AdaLN form.  Rows per tile R: enough for every CU to take at most
@@ -1275,9 +1489,13 @@ hipError_t launch_adaln_mfma(const uint16_t *h, int64_t M, int64_t d, const doub
     if (e != hipSuccess)
         return e;
     const AdArgs ad{stats, shift, scale, T};
+    if (sh.ring == 2)
+        return sh.strip == 4
+                   ? launch_mfma_instance<4, true, false, 2>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad)
+                   : launch_mfma_instance<8, true, false, 2>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
     if (sh.strip == 4)
-        return launch_mfma_instance<4, true, false>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
-    return launch_mfma_instance<8, true, false>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
+        return launch_mfma_instance<4, true, false, 4>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
+    return launch_mfma_instance<8, true, false, 4>(h, M, d, factors, nT, q, s, nullptr, 0, sh, stream, ad);
 }
 
 static hipError_t launch_stream(int mode, const void *x, int64_t M, int64_t d, const float *aux, int per_block,

@@ -370,21 +370,27 @@ def test_tuning_validation():
     x, q, s, f, y = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
     bad = [("mfma_tiles_per_wg", 257), ("mfma_tiles_per_wg", -1), ("mfma_groups", 3), ("mfma_strip", 12), ("mfma_strip", 2),
            ("mfma_order", 3), ("code_stores", 3), ("stream_rows_per_wave", 300), ("gemm_kernel", 4),
-           ("adaln_pass", 4), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000)]
+           ("adaln_pass", 4), ("adaln_strip", 16), ("adaln_blocks_per_wave", 0x10000), ("shared_form", 3),
+           ("flat_wgs", -2), ("flat_wgs", (1 << 20) + 1), ("flat_ring", 1), ("flat_ring", 4),
+           ("mfma_ring", 3), ("mfma_ring", 1)]
     for field, val in bad:
         t = ctypes.byref(K.Tuning(**{field: val}))
         assert raw("kq_quantize_tuned", x, 4, 64, f, 1, q, s, 0, t, None) == K.KQ_ERR_ARG, field
         assert raw("kq_transform_tuned", x, 4, 64, f, 1, y, 0, t, None) == K.KQ_ERR_ARG, field
         assert raw("mx_gemm_tuned", q, s, 4, q, s, 4, 64, y, 0, t, None) == K.KQ_ERR_ARG, field
-        shape = (ctypes.c_int64 * 6)()
+        shape = (ctypes.c_int64 * 7)()
         assert raw("kq_launch_shape", 4, 64, 0, t, shape) == K.KQ_ERR_ARG, field
+        assert raw("kq_flat_launch_shape", 4, 64, t, shape) == K.KQ_ERR_ARG, field
     ok = ctypes.byref(K.Tuning(mfma_strip=16, code_stores=2, gemm_kernel=3))
     # a valid override still fails the other checks first (no GPU is touched)
     assert raw("kq_quantize_tuned", x + 2, 4, 64, f, 1, q, s, 0, ok, None) == K.KQ_ERR_ALIGN
     assert raw("kq_quantize_tuned", x, 0, 64, f, 1, q, s, 0, ok, None) == K.KQ_OK
-    assert raw("kq_launch_shape", 4, 48, 0, None, (ctypes.c_int64 * 6)()) == K.KQ_ERR_SHAPE
-    assert raw("kq_launch_shape", 4, 64, 2, None, (ctypes.c_int64 * 6)()) == K.KQ_ERR_ARG
+    assert raw("kq_launch_shape", 4, 48, 0, None, (ctypes.c_int64 * 7)()) == K.KQ_ERR_SHAPE
+    assert raw("kq_launch_shape", 4, 64, 2, None, (ctypes.c_int64 * 7)()) == K.KQ_ERR_ARG
     assert raw("kq_launch_shape", 4, 64, 0, None, None) == K.KQ_ERR_ARG
+    assert raw("kq_flat_launch_shape", 4, 48, None, (ctypes.c_int64 * 3)()) == K.KQ_ERR_SHAPE
+    assert raw("kq_flat_launch_shape", -1, 64, None, (ctypes.c_int64 * 3)()) == K.KQ_ERR_ARG
+    assert raw("kq_flat_launch_shape", 4, 64, None, None) == K.KQ_ERR_ARG
     with pytest.raises(ValueError):
         K.kq_launch_shape(4, 64, tuning={"no_such_field": 1})
     assert not hasattr(K.lib(), "kq_set_tuning")

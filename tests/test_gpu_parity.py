@@ -355,7 +355,9 @@ def test_graph_replay_matches_eager(K):
 
 def test_copy_ceiling_kernel_output(K):
     # the benchmark's 4:1 measurement copies, every form: word i of dst = xor
-    # of the four words of src piece i; nothing past dst's n16 words is written
+    # of the four words of src piece i (the ring forms, which mirror the flat
+    # quantizer's lane layout, write each 64-byte group's words in the order
+    # 0, 2, 1, 3); nothing past dst's n16 words is written
     for n16 in (64, 64 * 255, 64 * (2048 * 4 + 77)):
         rng = np.random.default_rng(n16)
         src = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
@@ -367,19 +369,23 @@ def test_copy_ceiling_kernel_output(K):
             K.measure_copy41(s_dev, d_dev[:n16], form=form)
             torch.cuda.synchronize()
             got = d_dev.cpu().numpy().view(np.uint32)
-            assert np.array_equal(got[:n16], want), form
+            exp = want.reshape(-1, 4)[:, [0, 2, 1, 3]].ravel() if form >= 6 else want
+            assert np.array_equal(got[:n16], exp), form
             assert not got[n16:].any(), form
 
 
+@pytest.mark.parametrize("ring", [2, 4])
 @pytest.mark.parametrize("strip", [4, 8, 16])
 @pytest.mark.parametrize("M,d,shared", [(67, 1152, False), (33, 160, True), (130, 4608, False), (5, 544, False)])
-def test_kq_mfma_strip_widths(K, strip, M, d, shared):
-    # both workgroup strip widths of the MFMA quantizer, forced, on ragged shapes
-    # (blocks past the row end inside a strip, rows past M inside a tile)
+def test_kq_mfma_strip_widths(K, strip, ring, M, d, shared):
+    # every workgroup strip width and register ring depth of the strip kernel,
+    # forced, on ragged shapes (blocks past the row end inside a strip, rows
+    # past M inside a tile)
     x, _ = I.act_gaussian_outliers(M, d, 7000 + M + d, max(1, d // 100), 50.0)
     f = I.random_factors(1 if shared else d // 32, 7100 + d)
-    tn = {"mfma_strip": strip}
-    assert K.kq_launch_shape(M, d, tuning=tn)["strip"] == strip
+    tn = {"mfma_strip": strip, "mfma_ring": ring}
+    sh = K.kq_launch_shape(M, d, tuning=tn)
+    assert sh["strip"] == strip and sh["ring"] == ring
     check_kq(K, f"strip={strip} shared={shared}", x, f, VARIANTS["mfma"], tuning=tn)
     y = K.kq_transform_f32(dev_bf16(x), dev_f32(f), variant=VARIANTS["mfma"], tuning=tn)
     torch.cuda.synchronize()
@@ -388,17 +394,18 @@ def test_kq_mfma_strip_widths(K, strip, M, d, shared):
     assert np.all(err <= P.TOL * z + P.TOL_ABS), float((err / (z + 1e-300)).max())
 
 
-# The automatic launch shapes the library documents for MI355X (256 CUs), so a
-# change of the launch rules shows up here: the persistent round of long runs,
-# the one-round-per-CU shape of mid-size runs, the XCD-grouped round at 8192 x
-# 4608 and contiguous groups in strips of 4 at 8192 x 1152.
-AUTO_SHAPES = [((65536, 12288), dict(strip=16, tiles_per_wg=205, interleave=1, flat=1, grid=240, nt_codes=1)),
-               ((16384, 12288), dict(strip=16, tiles_per_wg=52, interleave=1, flat=1, grid=240, nt_codes=1)),
-               ((8192, 4608), dict(strip=16, tiles_per_wg=11, interleave=1, flat=0, grid=216, nt_codes=0)),
-               ((8192, 1152), dict(strip=4, tiles_per_wg=6, interleave=0, flat=0, grid=432, nt_codes=0)),
-               ((4608, 3072), dict(strip=8, tiles_per_wg=7, interleave=1, flat=1, grid=252, nt_codes=0)),
-               ((4608, 12288), dict(strip=16, tiles_per_wg=15, interleave=1, flat=1, grid=240, nt_codes=0)),
-               ((2048, 8960), dict(strip=8, tiles_per_wg=10, interleave=1, flat=1, grid=245, nt_codes=0))]
+# The automatic launch shapes of the strip kernel the library documents for
+# MI355X (256 CUs), so a change of the launch rules shows up here: the
+# persistent round of long runs (a ring of 4 tiles at 205 tiles per workgroup,
+# else 2), the one-round-per-CU shape of mid-size runs, the XCD-grouped round
+# at 8192 x 4608 and contiguous groups of 3 tiles in strips of 4 at 8192 x 1152.
+AUTO_SHAPES = [((65536, 12288), dict(strip=16, tiles_per_wg=205, interleave=1, flat=1, grid=240, nt_codes=1, ring=4)),
+               ((16384, 12288), dict(strip=16, tiles_per_wg=52, interleave=1, flat=1, grid=240, nt_codes=1, ring=2)),
+               ((8192, 4608), dict(strip=16, tiles_per_wg=11, interleave=1, flat=0, grid=216, nt_codes=0, ring=2)),
+               ((8192, 1152), dict(strip=4, tiles_per_wg=3, interleave=0, flat=0, grid=792, nt_codes=0, ring=2)),
+               ((4608, 3072), dict(strip=8, tiles_per_wg=7, interleave=1, flat=1, grid=252, nt_codes=0, ring=2)),
+               ((4608, 12288), dict(strip=16, tiles_per_wg=15, interleave=1, flat=1, grid=240, nt_codes=0, ring=2)),
+               ((2048, 8960), dict(strip=8, tiles_per_wg=10, interleave=1, flat=1, grid=245, nt_codes=0, ring=2))]
 
 
 @pytest.mark.parametrize("shape,want", AUTO_SHAPES, ids=[f"{m}x{d}" for (m, d), _ in AUTO_SHAPES])
