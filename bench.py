@@ -151,7 +151,7 @@ def summarize_trace_runs(path, min_calls=5):
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
     runs = []
     for r in rows:
-        key = (re.sub(r"\(.*", "", r["Kernel_Name"]), r.get("Grid_Size_X", ""))
+        key = (re.sub(r"\(.*", "", r["Kernel_Name"].replace("(anonymous namespace)::", "")), r.get("Grid_Size_X", ""))
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         if runs and runs[-1][0] == key:
             runs[-1][1].append(dur)

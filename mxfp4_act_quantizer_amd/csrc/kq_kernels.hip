@@ -1329,13 +1329,14 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
             }
         }
     }
-    // Register ring: 2 tiles (one in flight ahead) except in the longest
-    // persistent runs and the AdaLN second pass, which keep 4.  Measured with
-    // per-block factor sets against rings of 3 and 4: 2-8% faster at every
-    // configured shape up to 16384 x 12288 (8192 x 1152: 7.4 against 8.1 us;
-    // 16384 x 12288: 83.3 against 86.2 us), 3.5% slower at 65536 x 12288 (205
-    // tiles per workgroup: 338 against 327 us).
-    const int ring = tn.mfma_ring ? tn.mfma_ring : (adaln || (long_run && sh.tiles_per_wg > 128)) ? 4 : 2;
+    // Register ring: 2 tiles (one in flight ahead) except in the persistent
+    // long runs and the AdaLN second pass, which keep 4.  Measured with
+    // per-block factor sets, ring 2 against ring 4 in the same runs (three
+    // boxes): 2-8% faster at every configured shape below the long runs
+    // (8192 x 1152: 7.5 against 8.0 us; 8192 x 4608: 18.6 against 19.5), at
+    // 16384 x 12288 1% slower on two boxes of three (85.0 against 84.0), at
+    // 65536 x 12288 within the spread of identical legs.
+    const int ring = tn.mfma_ring ? tn.mfma_ring : (adaln || long_run) ? 4 : 2;
     if (!long_run) {
         mfma_groups(M, d, w, adaln, ring, tn, sh);
         if (!adaln && automatic && (sh.grid > device_cus() || sh.tiles_per_wg < 8))

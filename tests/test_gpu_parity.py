@@ -396,11 +396,11 @@ def test_kq_mfma_strip_widths(K, strip, ring, M, d, shared):
 
 # The automatic launch shapes of the strip kernel the library documents for
 # MI355X (256 CUs), so a change of the launch rules shows up here: the
-# persistent round of long runs (a ring of 4 tiles at 205 tiles per workgroup,
-# else 2), the one-round-per-CU shape of mid-size runs, the XCD-grouped round
+# persistent round of long runs (a ring of 4 tiles; 2 elsewhere), the
+# one-round-per-CU shape of mid-size runs, the XCD-grouped round
 # at 8192 x 4608 and contiguous groups of 3 tiles in strips of 4 at 8192 x 1152.
 AUTO_SHAPES = [((65536, 12288), dict(strip=16, tiles_per_wg=205, interleave=1, flat=1, grid=240, nt_codes=1, ring=4)),
-               ((16384, 12288), dict(strip=16, tiles_per_wg=52, interleave=1, flat=1, grid=240, nt_codes=1, ring=2)),
+               ((16384, 12288), dict(strip=16, tiles_per_wg=52, interleave=1, flat=1, grid=240, nt_codes=1, ring=4)),
                ((8192, 4608), dict(strip=16, tiles_per_wg=11, interleave=1, flat=0, grid=216, nt_codes=0, ring=2)),
                ((8192, 1152), dict(strip=4, tiles_per_wg=3, interleave=0, flat=0, grid=792, nt_codes=0, ring=2)),
                ((4608, 3072), dict(strip=8, tiles_per_wg=7, interleave=1, flat=1, grid=252, nt_codes=0, ring=2)),
