@@ -363,6 +363,7 @@ def all_configs(args):
         f_sh = torch.from_numpy(I.random_factors(1, I.factor_seed(name))).to(dev)
         lu_pb = torch.from_numpy(I.random_lu(d // 32, I.factor_seed(name) + 77)).to(dev)
         f16 = torch.from_numpy(I.random_factors16(d // 16, I.factor_seed(name) + 16)).to(dev)
+        f16_sh = torch.from_numpy(I.random_factors16(1, I.factor_seed(name) + 16)).to(dev)
         torch.cuda.synchronize()
         cur = torch.cuda.current_stream
         legs = {
@@ -374,6 +375,7 @@ def all_configs(args):
             "kq_lu_perblock": lambda b: K.kq_quantize_lu(b["x"], lu_pb, b["q"], b["s"], stream=cur()),
             "fwht": lambda b: K.fwht_quantize(b["x"], b["q"], b["s"], stream=cur()),
             "kq16_perblock": lambda b: K.kq_quantize16(b["x"], f16, b["q"], b["s16"], stream=cur()),
+            "kq16_shared": lambda b: K.kq_quantize16(b["x"], f16_sh, b["q"], b["s16"], stream=cur()),
             "smoothquant": lambda b: K.sq_quantize(b["x"], scale, b["q"], b["s"], stream=cur()),
         }
         row = {"config": name, "M": M, "d": d, "algorithmic_bytes": int(alg)}
@@ -399,7 +401,7 @@ def all_configs(args):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps
             # copy: 2 + 0.5 B per element; 16-element blocks: 2 + 0.5 + 1/16
-            nbytes = elems * (2.5 + 1.0 / 16) if leg == "kq16_perblock" else alg
+            nbytes = elems * (2.5 + 1.0 / 16) if leg.startswith("kq16") else alg
             row[leg] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
                         "hbm_pct": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1), "rows/s": round(M / us * 1e6, 1)}
         cp, cp_form, _ = best_copy(K, lambda i: bufs[i]["x"], lambda i: bufs[i]["q"], nsets, args.steps)
@@ -416,8 +418,8 @@ def all_configs(args):
     print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ shared, flat kernel us (GB/s, %peak) | "
           "KQ shared, strip kernel us | KQ butterfly us | K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | "
           "copy 4:1 us (GB/s) | KQ/SQ speed (per-block, shared) | KQ/copy speed | K2/FWHT speed | "
-          "KQ16 butterfly us (GB/s) |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "KQ16 per-block, butterfly us (GB/s) | KQ16 shared, flat kernel us (GB/s) |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in table:
         a, b, bs, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_strip_shared",
                                                        "kq_butterfly_perblock", "kq_lu_perblock", "fwht",
@@ -427,7 +429,8 @@ def all_configs(args):
               f"{c['us']} | {l2['us']} | {fw['us']} | {q['us']} ({q['GB/s']}, {q['hbm_pct']}%) | "
               f"{cp['us']} ({cp['GB/s']}) | {r['kq_over_sq_speed']}, {r['kq_shared_over_sq_speed']} | "
               f"{r['kq_over_copy41_speed']} | "
-              f"{r['k2_lu_over_fwht_speed']} | {r['kq16_perblock']['us']} ({r['kq16_perblock']['GB/s']}) |", flush=True)
+              f"{r['k2_lu_over_fwht_speed']} | {r['kq16_perblock']['us']} ({r['kq16_perblock']['GB/s']}) | "
+              f"{r['kq16_shared']['us']} ({r['kq16_shared']['GB/s']}) |", flush=True)
 
 
 FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak (TFLOP/s)

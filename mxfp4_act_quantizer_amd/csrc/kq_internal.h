@@ -43,7 +43,8 @@ struct FlatShape {
     int nt_codes;
 };
 bool flat_form(int64_t nT, const Tuning &tn);
-void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &out);
+// b16: 16-element blocks (one scale byte per 16 elements in the footprint)
+void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &out, bool b16 = false);
 
 // factors: [nT,5,2,2] 2x2 factors (lu = 0) or [nT,5,3] LU scalars (lu = 1)
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,

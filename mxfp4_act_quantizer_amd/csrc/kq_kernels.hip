@@ -73,11 +73,24 @@ __device__ __forceinline__ float bf16_val(unsigned short h) { return __uint_as_f
 // factor is rebuilt first as G = [[1, 0], [c, 1]] [[a, b], [0, -1/a]] =
 // [[a, b], [c a, c b - 1/a]], in fp32 with the operations kq_lu_factors
 // performs on the host (correctly rounded 1/a, c*a, fma(c, b, -1/a)).
+//
+// With kB16 (16-element blocks) F holds the four factors of K16 = A1 (x) A2 (x)
+// A3 (x) A4 and the block is built as I (x) K16: an identity first factor, so
+// each half of the 32 x 32 block is one 16-element block.
+template <bool kB16 = false>
 __device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lu, int lane)
 {
     // the set is the same for the whole wave: scalar loads, then per-lane selects
     float f[20];
-    if (lu) {
+    if constexpr (kB16) {
+        f[0] = 1.0f;
+        f[1] = 0.0f;
+        f[2] = 0.0f;
+        f[3] = 1.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            f[4 + i] = F[i];
+    } else if (lu) {
 #pragma unroll
         for (int k = 0; k < 5; ++k) {
             const float a = F[3 * k], b = F[3 * k + 1], c = F[3 * k + 2];
@@ -218,6 +231,44 @@ __device__ __forceinline__ unsigned mx_tile(const f32x16 &acc, unsigned &w0, uns
         m = amax_step(m, acc[v]);
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
     m = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const unsigned b = e8m0_byte(m);
+    const float sc = scale_operand(b);
+    w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
+    w1 = cvt8(acc[8], acc[9], acc[10], acc[11], acc[12], acc[13], acc[14], acc[15], sc);
+    if (b == 0xFFu)
+        w0 = w1 = 0u;
+    return b;
+}
+
+// The same for I (x) K16 (16-element blocks): half h of a column (output
+// channels 16h .. 16h+15) depends only on its own 16 inputs, taken by k-step
+// h, so each half accumulates its own step alone and the lane keeps its
+// half's sums.  A NaN or Inf input then reaches only its own 16-element
+// block, where a single sum over both steps would have spread it through the
+// zero entries of the other half.
+__device__ __forceinline__ f32x16 block_product16(const bf16x8 (&A)[3][2], const bf16x8 (&bv)[2], int h)
+{
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][0], bv[0], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[sp][1], bv[1], acc1, 0, 0, 0);
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        acc[v] = h ? acc1[v] : acc0[v];
+    return acc;
+}
+
+// MX step of one half column (16-element blocks): the lane's 16 accumulators
+// are one block; no exchange between lanes.
+__device__ __forceinline__ unsigned mx_tile16(const f32x16 &acc, unsigned &w0, unsigned &w1)
+{
+    float m = __builtin_fabsf(acc[0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v)
+        m = amax_step(m, acc[v]);
     const unsigned b = e8m0_byte(m);
     const float sc = scale_operand(b);
     w0 = cvt8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7], sc);
@@ -500,8 +551,8 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
 // ---------------------------------------------------------------------------
 constexpr int kFlatWaves = 4; // waves per workgroup
 
-template <bool kQuant, bool kNT, int kFR>
-__global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t *__restrict__ x, int64_t nblk,
+template <bool kQuant, bool kNT, int kFR, bool kB16 = false>
+__global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t *__restrict__ x, int64_t nelem,
                                                                   const float *__restrict__ factors, int lu,
                                                                   uint8_t *__restrict__ q, uint8_t *__restrict__ s,
                                                                   float *__restrict__ y)
@@ -510,7 +561,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t
     const int lane = threadIdx.x & 63;
     const int64_t G = (int64_t)gridDim.x * kFlatWaves;
     const int64_t g = (int64_t)blockIdx.x * kFlatWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nunits = (nblk + 31) / 32;
+    const int64_t nunits = (nelem + 1023) / 1024;
     if (g >= nunits)
         return; // wave-uniform; this kernel has no barrier
     const int n = (int)((nunits - g + G - 1) / G); // units of this wave
@@ -518,29 +569,34 @@ __global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t
     const unsigned xoff = (unsigned)(64 * (col & 15) + 32 * (col >> 4) + 16 * h);
 
     // the wave's k-th unit (steps past its last unit name that unit again)
-    // and its blocks below the end (none past the last unit)
+    // and its elements below the end (none past the last unit)
     auto unit_of = [&](int k) -> int64_t { return g + (int64_t)(k < n ? k : n - 1) * G; };
-    auto blocks_of = [&](int k) -> int {
-        const int64_t left = nblk - unit_of(k) * 32;
-        return k < n ? (int)(left < 32 ? left : 32) : 0;
+    auto elems_of = [&](int k) -> int {
+        const int64_t left = nelem - unit_of(k) * 1024;
+        return k < n ? (int)(left < 1024 ? left : 1024) : 0;
     };
     auto load_unit = [&](XIn &in, int k) {
         const __amdgpu_buffer_rsrc_t rx =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(x + unit_of(k) * 1024), 0, blocks_of(k) * 64, kBufWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void *)(x + unit_of(k) * 1024), 0, elems_of(k) * 2, kBufWord3);
         in.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xoff, 0, kAuxNT));
         in.v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xoff + 1024), 0, kAuxNT));
     };
-    // outputs of unit u with nb blocks (nb = 0 drops every lane): lane (c, h)
-    // holds code bytes 8h .. 8h+7 of block c, and lanes h = 0 its scale byte;
-    // or (y) output channels 16h .. 16h+15 of block c
-    auto emit_q = [&](unsigned w0, unsigned w1, unsigned b, int64_t u, int nb) {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, out_buffer(q + u * 512, nb * 16), 16 * col + 8 * h, 0,
+    // outputs of unit u with ne elements (ne = 0 drops every lane): lane (c, h)
+    // holds code bytes 8h .. 8h+7 of column c's 32 elements and either (32-
+    // element blocks) the block's scale byte, stored by lanes h = 0, or
+    // (16-element blocks, kB16) the scale byte of its own 16 elements, block
+    // 2c + h of the unit; or (y) output channels 16h .. 16h+15 of column c
+    auto emit_q = [&](unsigned w0, unsigned w1, unsigned b, int64_t u, int ne) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, out_buffer(q + u * 512, ne / 2), 16 * col + 8 * h, 0,
                                               kNT ? kAuxNT : 0);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, out_buffer(s + u * 32, nb),
-                                             (int)((unsigned)col | ((unsigned)h << 31)), 0, 0);
+        if constexpr (kB16)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, out_buffer(s + u * 64, ne / 16), 2 * col + h, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, out_buffer(s + u * 32, ne / 32),
+                                                 (int)((unsigned)col | ((unsigned)h << 31)), 0, 0);
     };
-    auto emit_y = [&](const f32x16 &acc, int64_t u, int nb) {
-        const __amdgpu_buffer_rsrc_t ry = out_buffer(y + u * 1024, nb * 128);
+    auto emit_y = [&](const f32x16 &acc, int64_t u, int ne) {
+        const __amdgpu_buffer_rsrc_t ry = out_buffer(y + u * 1024, ne * 4);
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             __builtin_amdgcn_raw_buffer_store_b128(
@@ -561,7 +617,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t
             emit_y(f32x16{}, 0, 0);
     }
     bf16x8 A[3][2];
-    build_a_operands(A, factors, lu, lane);
+    build_a_operands<kB16>(A, factors, lu, lane);
 
     // The scheduling barriers keep each step's work after its look-ahead load
     // and before the next step's: hoisting the swaps of later units would
@@ -577,16 +633,16 @@ __global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t
             b1[i] = r[1];
         }
         const bf16x8 bv[2] = {__builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1)};
-        const f32x16 acc = block_product(A, bv);
+        const f32x16 acc = kB16 ? block_product16(A, bv, h) : block_product(A, bv);
         const int64_t u = g + (int64_t)kk * G;
-        const int64_t left = nblk - u * 32;
-        const int nb = (int)(left < 32 ? left : 32);
+        const int64_t left = nelem - u * 1024;
+        const int ne = (int)(left < 1024 ? left : 1024);
         if constexpr (kQuant) {
             unsigned w0, w1;
-            const unsigned b = mx_tile(acc, w0, w1);
-            emit_q(w0, w1, b, u, nb);
+            const unsigned b = kB16 ? mx_tile16(acc, w0, w1) : mx_tile(acc, w0, w1);
+            emit_q(w0, w1, b, u, ne);
         } else {
-            emit_y(acc, u, nb);
+            emit_y(acc, u, ne);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -1381,33 +1437,42 @@ bool flat_form(int64_t nT, const Tuning &tn)
            (tn.mfma_strip == 0 && tn.mfma_tiles_per_wg <= 0 && tn.mfma_groups == 0 && tn.mfma_order == 0);
 }
 
-void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &sh)
+void flat_launch_shape(int64_t M, int64_t d, const Tuning &tn, FlatShape &sh, bool b16)
 {
-    const double footprint = (double)M * (double)d * (2.0 + 0.5 + 1.0 / 32.0);
+    const double footprint = (double)M * (double)d * (2.0 + 0.5 + (b16 ? 1.0 / 16.0 : 1.0 / 32.0));
     const bool big = footprint > (double)kMallBytes;
     sh.nt_codes = tn.code_stores == 2 || (tn.code_stores == 0 && big);
     sh.ring = tn.flat_ring ? tn.flat_ring : (big ? 3 : 2);
     int64_t wgs = tn.flat_wgs > 0 ? tn.flat_wgs : (int64_t)(big ? 1 : 2) * device_cus();
-    const int64_t nunits = (M * (d / 32) + 31) / 32;
+    const int64_t nunits = (M * d + 1023) / 1024;
     const int64_t need = (nunits + kFlatWaves - 1) / kFlatWaves;
     sh.wgs = wgs < need ? wgs : need;
+}
+
+template <bool kB16>
+hipError_t launch_flat_instance(const uint16_t *x, int64_t M, int64_t d, const float *factors, uint8_t *q,
+                                uint8_t *s, float *y, int lu, const Tuning &tn, hipStream_t stream)
+{
+    FlatShape sh{};
+    flat_launch_shape(M, d, tn, sh, kB16);
+    const int64_t nelem = M * d;
+    const void *fn;
+    if (sh.ring == 3)
+        fn = y ? (const void *)kq_flat_kernel<false, false, 3, kB16>
+             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 3, kB16>
+                           : (const void *)kq_flat_kernel<true, false, 3, kB16>;
+    else
+        fn = y ? (const void *)kq_flat_kernel<false, false, 2, kB16>
+             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 2, kB16>
+                           : (const void *)kq_flat_kernel<true, false, 2, kB16>;
+    void *args[] = {(void *)&x, (void *)&nelem, (void *)&factors, (void *)&lu, (void *)&q, (void *)&s, (void *)&y};
+    return hipLaunchKernel(fn, dim3((unsigned)sh.wgs), dim3(64 * kFlatWaves), args, 0, stream);
 }
 
 hipError_t launch_kq_flat(const uint16_t *x, int64_t M, int64_t d, const float *factors, uint8_t *q, uint8_t *s,
                           float *y, int lu, const Tuning &tn, hipStream_t stream)
 {
-    FlatShape sh{};
-    flat_launch_shape(M, d, tn, sh);
-    const int64_t nblk = M * (d / 32);
-    const void *fn;
-    if (sh.ring == 3)
-        fn = y ? (const void *)kq_flat_kernel<false, false, 3>
-             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 3> : (const void *)kq_flat_kernel<true, false, 3>;
-    else
-        fn = y ? (const void *)kq_flat_kernel<false, false, 2>
-             : sh.nt_codes ? (const void *)kq_flat_kernel<true, true, 2> : (const void *)kq_flat_kernel<true, false, 2>;
-    void *args[] = {(void *)&x, (void *)&nblk, (void *)&factors, (void *)&lu, (void *)&q, (void *)&s, (void *)&y};
-    return hipLaunchKernel(fn, dim3((unsigned)sh.wgs), dim3(64 * kFlatWaves), args, 0, stream);
+    return launch_flat_instance<false>(x, M, d, factors, q, s, y, lu, tn, stream);
 }
 
 hipError_t launch_kq_mfma(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
@@ -1536,9 +1601,14 @@ hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const fl
     return launch_stream(y ? kBflyT : kBflyQ, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 
+// One shared set: the flat matrix-core kernel with the 32 x 32 block I (x) K16
+// (measured against the butterfly streaming kernel below); a set per block:
+// the butterfly streaming kernel.
 hipError_t launch_kq16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                        uint8_t *s, float *y, const Tuning &tn, hipStream_t stream)
 {
+    if (nT == 1 && tn.shared_form != 1)
+        return launch_flat_instance<true>(x, M, d, factors, q, s, y, 0, tn, stream);
     return launch_stream(y ? kBfly16T : kBfly16Q, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 

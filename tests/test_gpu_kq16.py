@@ -1,5 +1,6 @@
 """GPU parity of the 16-element-block quantizer (kq_quantize16,
-kq_transform16_f32) against the oracle, through the C ABI: transformed
+kq_transform16_f32; one shared set on the matrix cores, a set per block on
+the butterfly kernel) against the oracle, through the C ABI: transformed
 values within 2e-6 z + 2^-146, codes and scales bit-exact except
 tolerance-boundary elements (tests/parity.py with 16-element blocks),
 identity factors fully bit-exact.  Every case prints its shape and seed
@@ -98,6 +99,50 @@ def test_kq16_special_blocks(K):
     s = K.kq_quantize16(dev_bf16(x), dev_f32(f))[1].cpu().numpy()
     assert s[2, 3] == 0xFF and s[3, 4] == 0xFF and s[0, 1] == 0x00
     assert res["ok"]
+
+
+def test_kq16_shared_special_blocks_stay_in_their_block(K):
+    # one shared set takes the matrix-core kernel, whose 32 x 32 block pairs
+    # two 16-element blocks (I (x) K16): a NaN or Inf in one of them must not
+    # reach its partner
+    M, d = 6, 256
+    say(f"[kq16 shared specials] M={M} d={d}")
+    rng = np.random.default_rng(9750)
+    v = rng.standard_normal((M, d)).astype(np.float32)
+    v[0, 16:32] = 0.0
+    v[1, 32:48] *= 2.0 ** -130
+    v[2, 48 + 5] = np.nan   # block 3: its partner is block 2
+    v[3, 64 + 9] = np.inf   # block 4: its partner is block 5
+    v[4, 80:96] = -0.0
+    v[5, 0] = -np.inf       # block 0 of the last row
+    x = I.f32_to_bf16_bits(v)
+    f = I.random_factors16(1, 9751)
+    check(K, x, f, "shared specials")
+    s = K.kq_quantize16(dev_bf16(x), dev_f32(f))[1].cpu().numpy()
+    assert s[2, 3] == 0xFF and s[3, 4] == 0xFF and s[5, 0] == 0xFF and s[0, 1] == 0x00
+    assert s[2, 2] != 0xFF and s[3, 5] != 0xFF and s[5, 1] != 0xFF
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["dit_4608", "sweep_16384"])
+def test_kq16_shared_full_size_sampled_rows(K, name):
+    # one shared set at full size, in both launch shapes of the matrix-core
+    # kernel (below and above the last-level cache size)
+    M, d, _ = I.CONFIGS[name]
+    say(f"[kq16 shared full] {name} M={M} d={d}")
+    x = I.make_activation(name) if name != "sweep_16384" else I.act_sweep_special(M, d, I.data_seed(name))[0]
+    f = I.random_factors16(1, I.factor_seed(name) + 17)
+    q, s = K.kq_quantize16(dev_bf16(x), dev_f32(f))
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    rng = np.random.default_rng(9850)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)]))
+    qr, sr, y32 = O.kq_quantize16(x[rows], f, want_y32=True)
+    _, z = O.kq_transform16(x[rows], f)
+    ef, bf = P.boundary_flags(z, y32, bw=16)
+    res = P.compare(q[rows], s[rows], qr, sr, ef, bf)
+    say(f"    {len(rows)} rows: {res}")
+    assert res["ok"], res
 
 
 def test_kq16_empty(K):
