@@ -1332,6 +1332,13 @@ void mfma_one_per_cu(int64_t M, int64_t d, MfmaShape &sh)
     }
     if (best_w == 0)
         return;
+    // In strips of 16 (16-wave workgroups) the longest runs of the range, 16
+    // tiles, while they still give three CUs of four a workgroup: fewer
+    // loads in flight per round measured faster (with the ring of 2, two
+    // boxes: 4608 x 12288 26.8 against 28.1-29.9 us for 15 tiles on 240
+    // workgroups; 4096 x 12288 25.5 against 27.3-29.4 for 13 tiles).
+    if (best_w == 16 && best_t < 16 && 4 * ((nTiles + 15) / 16) * (nB / 16) >= 3 * cus)
+        best_t = 16;
     sh.strip = best_w;
     sh.tiles_per_wg = (int)best_t;
     sh.interleave = 1;

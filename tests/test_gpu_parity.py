@@ -404,7 +404,8 @@ AUTO_SHAPES = [((65536, 12288), dict(strip=16, tiles_per_wg=205, interleave=1, f
                ((8192, 4608), dict(strip=16, tiles_per_wg=11, interleave=1, flat=0, grid=216, nt_codes=0, ring=2)),
                ((8192, 1152), dict(strip=4, tiles_per_wg=3, interleave=0, flat=0, grid=792, nt_codes=0, ring=2)),
                ((4608, 3072), dict(strip=8, tiles_per_wg=7, interleave=1, flat=1, grid=252, nt_codes=0, ring=2)),
-               ((4608, 12288), dict(strip=16, tiles_per_wg=15, interleave=1, flat=1, grid=240, nt_codes=0, ring=2)),
+               ((4608, 12288), dict(strip=16, tiles_per_wg=16, interleave=1, flat=1, grid=216, nt_codes=0, ring=2)),
+               ((4096, 12288), dict(strip=16, tiles_per_wg=16, interleave=1, flat=1, grid=192, nt_codes=0, ring=2)),
                ((2048, 8960), dict(strip=8, tiles_per_wg=10, interleave=1, flat=1, grid=245, nt_codes=0, ring=2))]
 
 
