@@ -418,7 +418,7 @@ def all_configs(args):
     print("| config | M x d | KQ MFMA per-block us (GB/s, %peak) | KQ shared, flat kernel us (GB/s, %peak) | "
           "KQ shared, strip kernel us | KQ butterfly us | K2 LU us | FWHT us | SmoothQuant us (GB/s, %peak) | "
           "copy 4:1 us (GB/s) | KQ/SQ speed (per-block, shared) | KQ/copy speed | K2/FWHT speed | "
-          "KQ16 per-block, butterfly us (GB/s) | KQ16 shared, flat kernel us (GB/s) |")
+          "KQ16 per-block, strip kernel us (GB/s) | KQ16 shared, flat kernel us (GB/s) |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for r in table:
         a, b, bs, c, l2, fw, q, cp = (r[k] for k in ("kq_mfma_perblock", "kq_mfma_shared", "kq_strip_shared",

@@ -170,11 +170,13 @@ int fwht_transform_f32(const uint16_t *x, int64_t M, int64_t d, float *y, void *
  * 16-channel block (A1 on the most significant bit of the 4-bit in-block
  * index), y = x_blk . K16_j in fp32, and the MX rules applied to 16-element
  * blocks: one E8M0 scale per 16 elements, E2M1 codes, element 2i in the low
- * nibble.  With a set per block (nT = d/16) the transform runs as four
- * butterfly stages (one cross-lane stage over a lane pair by DPP, three
- * in-lane stages); with one shared set (nT = 1) on the matrix cores as the
- * 32 x 32 block I (x) K16, each half of which is one 16-element block summed
- * on its own (a NaN or Inf input stays in its own block).
+ * nibble.  The transform runs on the matrix cores as a 32 x 32 block per
+ * pair of 16-element blocks: I (x) K16 with one shared set (nT = 1), and
+ * diag(K16_2j, K16_2j+1) with a set per block (nT = d/16) when d % 32 == 0;
+ * each half is one 16-element block summed on its own (a NaN or Inf input
+ * stays in its own block).  A set per block with d % 32 == 16 runs as four
+ * butterfly stages instead (one cross-lane stage over a lane pair by DPP,
+ * three in-lane stages).  Both give the same results up to fp32 rounding.
  *   x        dev, bf16 [M, d], d % 16 == 0, 16-byte aligned
  *   factors  dev, float32 [nT, 4, 2, 2], nT = 1 or d/16, 4-byte aligned
  *   q        dev, u8 [M, d/2], 16-byte aligned

@@ -36,7 +36,8 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
 // Launch shape of the flat form (one shared factor set): register ring depth
 // in units of 32 blocks, workgroups of 4 waves, nontemporal code stores.
 // kq_quantize / kq_transform_f32 / the LU calls take this form when nT = 1
-// and no strip-kernel override is set (flat_form).
+// and no strip-kernel override is set (flat_form); kq_quantize16 and
+// kq_transform16_f32 with nT = 1 take its 16-element form (b16).
 struct FlatShape {
     int ring;
     int64_t wgs;

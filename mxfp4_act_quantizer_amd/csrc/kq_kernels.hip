@@ -15,9 +15,15 @@
 //   kq_mfma_kernel   dense 32x32 block on bf16 MFMA (v_mfma_f32_32x32x16_bf16).
 //                    K is held as an exact 3-term bf16 split (hi + mid + lo == K
 //                    in fp32), so bf16 x times each term is exact and the
-//                    accumulation is fp32.  The pages run the block as "small
-//                    tensor-core GEMMs"; here the GEMM is Y^T = K^T X^T so one
-//                    token's 32 outputs land in 2 lanes x 16 accumulators.
+//                    accumulation is fp32.  The pages run the block as small
+//                    GEMMs on the matrix units; here the GEMM is
+//                    Y^T = K^T X^T so one token's 32 outputs land in 2 lanes x
+//                    16 accumulators.  The strip kernel: 32-token tiles of a
+//                    strip of blocks staged in LDS (a factor set per block).
+//   kq_flat_kernel   the same products with 32 consecutive blocks of the
+//                    flattened input as the MFMA columns (one shared set; also
+//                    16-element blocks): contiguous 1 KB loads and 512-byte
+//                    code stores, no LDS.
 //   stream_kernel    one lane per 8 consecutive channels, 4 lanes per block,
 //                    used for: the butterfly transform (five 2x2 stages, the
 //                    two cross-lane stages via DPP quad permutes), SmoothQuant
@@ -73,24 +79,11 @@ __device__ __forceinline__ float bf16_val(unsigned short h) { return __uint_as_f
 // factor is rebuilt first as G = [[1, 0], [c, 1]] [[a, b], [0, -1/a]] =
 // [[a, b], [c a, c b - 1/a]], in fp32 with the operations kq_lu_factors
 // performs on the host (correctly rounded 1/a, c*a, fma(c, b, -1/a)).
-//
-// With kB16 (16-element blocks) F holds the four factors of K16 = A1 (x) A2 (x)
-// A3 (x) A4 and the block is built as I (x) K16: an identity first factor, so
-// each half of the 32 x 32 block is one 16-element block.
-template <bool kB16 = false>
 __device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float *__restrict__ F, int lu, int lane)
 {
     // the set is the same for the whole wave: scalar loads, then per-lane selects
     float f[20];
-    if constexpr (kB16) {
-        f[0] = 1.0f;
-        f[1] = 0.0f;
-        f[2] = 0.0f;
-        f[3] = 1.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            f[4 + i] = F[i];
-    } else if (lu) {
+    if (lu) {
 #pragma unroll
         for (int k = 0; k < 5; ++k) {
             const float a = F[3 * k], b = F[3 * k + 1], c = F[3 * k + 2];
@@ -135,6 +128,51 @@ __device__ __forceinline__ void build_a_operands(bf16x8 (&A)[3][2], const float 
     }
 }
 
+// The A operands for two 16-element blocks (four factors per set, K16 = A1
+// (x) A2 (x) A3 (x) A4 with A1 on the most significant bit of the 4-bit in-block
+// index): the 32 x 32 block diag(K16 of set F0, K16 of set F1), so input half
+// j (k-step j) belongs to set j and feeds only output half j; with F0 == F1
+// it is I (x) K16.  Same lane layout, product order ((A1 A2) A3) A4 and exact
+// three-term split as build_a_operands.
+__device__ __forceinline__ void build_a_operands16(bf16x8 (&A)[3][2], const float *__restrict__ F0,
+                                                   const float *__restrict__ F1, int lane)
+{
+    const int h = lane >> 5;
+    const int i = lane & 31;
+    const int c = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+    const int c4 = (c >> 4) & 1;
+    const bool c3 = (c >> 3) & 1, c2 = (c >> 2) & 1, c1 = (c >> 1) & 1, c0 = c & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float *F = j ? F1 : F0;
+        float f[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            f[k] = F[k];
+        // f[4k + 2r + col] is entry (r, col) of factor A_{k+1} of the set
+        const float a1 = h ? (c3 ? f[3] : f[2]) : (c3 ? f[1] : f[0]);
+        const float a2_0 = c2 ? f[5] : f[4], a2_1 = c2 ? f[7] : f[6];
+        const float a3_0 = c1 ? f[9] : f[8], a3_1 = c1 ? f[11] : f[10];
+        const float a4_0 = c0 ? f[13] : f[12], a4_1 = c0 ? f[15] : f[14];
+        const float p = c4 == j ? a1 : 0.0f;
+        bf16x8 hi, mid, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float k = ((p * ((e & 4) ? a2_1 : a2_0)) * ((e & 2) ? a3_1 : a3_0)) * ((e & 1) ? a4_1 : a4_0);
+            const unsigned short bh = bf16_rne(k);
+            const float r1 = k - bf16_val(bh);
+            const unsigned short bm = bf16_rne(r1);
+            const float r2 = r1 - bf16_val(bm);
+            hi[e] = __builtin_bit_cast(__bf16, bh);
+            mid[e] = __builtin_bit_cast(__bf16, bm);
+            lo[e] = __builtin_bit_cast(__bf16, bf16_rne(r2));
+        }
+        A[0][j] = lo;
+        A[1][j] = mid;
+        A[2][j] = hi;
+    }
+}
+
 // ---- workgroup tile of the MFMA variant ----------------------------------
 // A workgroup of kW waves owns a strip of kW adjacent blocks (kW * 32
 // channels, kW * 64 bytes of a token row: 512 bytes for kW = 8, 1 KB for
@@ -152,11 +190,12 @@ struct Strip {
     static_assert(kRowsPerWave == 2 * kRowsPerLoad, "two load instructions per wave and tile");
 };
 
-template <int kW>
+// kB16: 16-element blocks, two scale bytes per 32-element block of the strip
+template <int kW, bool kB16 = false>
 struct __align__(16) WgStage {
-    unsigned char x[2][kTileT][Strip<kW>::kXRow]; // x tile, double-buffered by tile parity
-    unsigned char q[2][kTileT][Strip<kW>::kQRow]; // staged codes
-    unsigned char s[2][kTileT][kW];               // staged scale bytes
+    unsigned char x[2][kTileT][Strip<kW>::kXRow];    // x tile, double-buffered by tile parity
+    unsigned char q[2][kTileT][Strip<kW>::kQRow];    // staged codes
+    unsigned char s[2][kTileT][kB16 ? 2 * kW : kW]; // staged scale bytes
 };
 
 // Raw x of one tile for one wave: two load instructions, rows
@@ -194,8 +233,8 @@ __device__ __forceinline__ void load_x(XIn &in, const uint16_t *__restrict__ x, 
     }
 }
 
-template <int kW>
-__device__ __forceinline__ void stage_x(WgStage<kW> &st, int par, const XIn &in, int wave, int lane)
+template <int kW, bool kB16>
+__device__ __forceinline__ void stage_x(WgStage<kW, kB16> &st, int par, const XIn &in, int wave, int lane)
 {
     using S = Strip<kW>;
 #pragma unroll
@@ -281,23 +320,26 @@ __device__ __forceinline__ unsigned mx_tile16(const f32x16 &acc, unsigned &w0, u
 // Transform one tile on the matrix cores; quantize into the staging buffer
 // (or write y directly).  Lane l takes token l%32 and, for MFMA j, channels
 // 16j + 8h .. +7 of block `wave` of the strip (h = l/32).
-template <bool kQuant, int kW>
-__device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<kW> &st, int par, const bf16x8 (&A)[3][2],
-                                               int64_t t, int64_t M, int d, int jb, bool jb_valid, int h, int wave,
-                                               int tl, float *__restrict__ y)
+template <bool kQuant, int kW, bool kB16>
+__device__ __forceinline__ void transform_tile(const WgStage<kW, kB16> &stc, WgStage<kW, kB16> &st, int par,
+                                               const bf16x8 (&A)[3][2], int64_t t, int64_t M, int d, int jb,
+                                               bool jb_valid, int h, int wave, int tl, float *__restrict__ y)
 {
     bf16x8 bv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
         bv[j] = *(const bf16x8 *)&stc.x[par][tl][wave * 64 + 32 * j + 16 * h];
-    const f32x16 acc = block_product(A, bv);
+    const f32x16 acc = kB16 ? block_product16(A, bv, h) : block_product(A, bv);
     if constexpr (kQuant) {
         unsigned w0, w1;
-        const unsigned b = mx_tile(acc, w0, w1);
-        // lane half h holds q bytes 8h..8h+7 of block `wave` of the strip
+        const unsigned b = kB16 ? mx_tile16(acc, w0, w1) : mx_tile(acc, w0, w1);
+        // lane half h holds q bytes 8h..8h+7 of block `wave` of the strip (and
+        // with kB16 the scale byte of 16-element block 2 wave + h)
         typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
         *(u32x2 *)&st.q[par][tl][wave * 16 + 8 * h] = u32x2{w0, w1};
-        if (h == 0)
+        if constexpr (kB16)
+            st.s[par][tl][2 * wave + h] = (unsigned char)b;
+        else if (h == 0)
             st.s[par][tl][wave] = (unsigned char)b;
     } else {
         // waves past the row end computed a stand-in block: nothing to write
@@ -326,9 +368,9 @@ __device__ __forceinline__ void transform_tile(const WgStage<kW> &stc, WgStage<k
 // DiT qkv shape (8192 x 1152 by 3456) nontemporal code stores made the
 // quantizer alone 3-6% faster but quantize-then-product 8% slower (41.7
 // against 38.4 us).  Scale bytes always keep the default policy.
-template <int kW, bool kNT>
-__device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool valid, int bg, int nB, int d, int wave,
-                                           int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
+template <int kW, bool kNT, bool kB16>
+__device__ __forceinline__ void store_tile(const WgStage<kW, kB16> &st, int par, bool valid, int bg, int nB, int d,
+                                           int wave, int lane, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs)
 {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     constexpr int kLQ = 2 * kW; // lanes per token for the codes
@@ -339,11 +381,21 @@ __device__ __forceinline__ void store_tile(const WgStage<kW> &st, int par, bool 
     __builtin_amdgcn_raw_buffer_store_b64(v, rq, (int)((unsigned)(tq * (d >> 1) + bg * kW * 16 + c8 * 8) | drop_q), 0,
                                           kNT ? kAuxNT : 0);
     const int f = wave * 64 + lane; // flat lane of the workgroup
-    const int ts = (f / kW) % kTileT;
-    const int cs = f % kW;
-    const unsigned drop_s = (unsigned)(bg * kW + cs >= nB || !valid || f >= kTileT * kW) << 31;
-    __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs, (int)((unsigned)(ts * nB + bg * kW + cs) | drop_s), 0,
-                                         0);
+    if constexpr (kB16) {
+        // two scale bytes per 32-element block: every lane stores one
+        const int ts = f / (2 * kW);
+        const int cs = f % (2 * kW);
+        const int nB16 = 2 * nB;
+        const unsigned drop_s = (unsigned)(2 * bg * kW + cs >= nB16 || !valid) << 31;
+        __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs,
+                                             (int)((unsigned)(ts * nB16 + 2 * bg * kW + cs) | drop_s), 0, 0);
+    } else {
+        const int ts = (f / kW) % kTileT;
+        const int cs = f % kW;
+        const unsigned drop_s = (unsigned)(bg * kW + cs >= nB || !valid || f >= kTileT * kW) << 31;
+        __builtin_amdgcn_raw_buffer_store_b8(st.s[par][ts][cs], rs, (int)((unsigned)(ts * nB + bg * kW + cs) | drop_s),
+                                             0, 0);
+    }
 }
 
 // One workgroup: a strip of kW blocks (one per wave for the transform) and
@@ -377,13 +429,16 @@ struct AdArgs {
 // compiler spills, and that measured no faster).
 constexpr int kAdOcc = 2;
 
-template <bool kQuant, int kW, bool kAd = false, bool kNT = false, int kRing = 4>
+// kB16: 16-element blocks with four factors per set (a pair of sets per
+// 32-element block of the strip, build_a_operands16); s has d / 16 bytes per
+// row.
+template <bool kQuant, int kW, bool kAd = false, bool kNT = false, int kRing = 4, bool kB16 = false>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? kAdOcc : 4))) void kq_mfma_kernel(
     const uint16_t *__restrict__ x, int64_t M, int d, const float *__restrict__ factors, int per_block,
     uint8_t *__restrict__ q, uint8_t *__restrict__ s, float *__restrict__ y, int nBG, int tiles_per_wg,
     int order, int lu, AdArgs ad)
 {
-    __shared__ WgStage<kW> st;
+    __shared__ WgStage<kW, kB16> st;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // order bit 0: interleaved token groups (else contiguous runs of tiles).
@@ -466,8 +521,9 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
     auto store_prev = [&](int kp) {
         const int64_t r0 = trow(kp < 0 ? 0 : kp);
         const int64_t rows = (M - r0) < kTileT ? (M - r0) : kTileT;
-        store_tile<kW, kNT>(st, kp & 1, kp >= 0, bg, nB, d, wave, lane, out_buffer(q + r0 * (d >> 1), rows * (d >> 1)),
-                   out_buffer(s + r0 * nB, rows * nB));
+        const int sB = kB16 ? 2 * nB : nB; // scale bytes per row
+        store_tile<kW, kNT, kB16>(st, kp & 1, kp >= 0, bg, nB, d, wave, lane,
+                                  out_buffer(q + r0 * (d >> 1), rows * (d >> 1)), out_buffer(s + r0 * sB, rows * sB));
     };
     // Each prologue load is followed by a store pair with every lane dropped
     // (no memory access), so the memory counter holds the same sequence on
@@ -484,7 +540,11 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
     }
 
     bf16x8 A[3][2];
-    build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * (lu ? 15 : 20), lu, lane);
+    if constexpr (kB16)
+        build_a_operands16(A, factors + (int64_t)(per_block ? 2 * jb : 0) * 16,
+                           factors + (int64_t)(per_block ? 2 * jb + 1 : 0) * 16, lane);
+    else
+        build_a_operands(A, factors + (int64_t)(per_block ? jb : 0) * (lu ? 15 : 20), lu, lane);
 
     auto step = [&](XIn &cur, XIn &ld, const u32x4 &rcur, u32x4 &rld, int kk) {
         if constexpr (kAd)
@@ -496,7 +556,7 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
         __syncthreads();
         if (kQuant)
             store_prev(kk - 1);
-        transform_tile<kQuant, kW>(st, st, kk & 1, A, trow(kk) + tl, M, d, jb, jb_raw < nB, h, wave, tl, y);
+        transform_tile<kQuant, kW, kB16>(st, st, kk & 1, A, trow(kk) + tl, M, d, jb, jb_raw < nB, h, wave, tl, y);
     };
 
     int it = 0;
@@ -548,6 +608,13 @@ __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kAd ? k
 // blocks of the last unit and the look-ahead past a wave's last unit fetch
 // and store nothing; every load and store instruction is issued
 // unconditionally (exact memory-counter waits, as in kq_mfma_kernel).
+//
+// With kB16 the kernel runs 16-element blocks with one shared set of four
+// factors: the 32 x 32 block is I (x) K16 (build_a_operands16), each half
+// column sums only its own k-step (block_product16) and is one 16-element
+// block with its own scale byte (mx_tile16; 64 scale bytes per unit).  nelem
+// is M * d, a multiple of 16 with kB16 and of 32 otherwise; a unit is 1024
+// elements either way.
 // ---------------------------------------------------------------------------
 constexpr int kFlatWaves = 4; // waves per workgroup
 
@@ -617,7 +684,10 @@ __global__ __launch_bounds__(64 * kFlatWaves) void kq_flat_kernel(const uint16_t
             emit_y(f32x16{}, 0, 0);
     }
     bf16x8 A[3][2];
-    build_a_operands<kB16>(A, factors, lu, lane);
+    if constexpr (kB16)
+        build_a_operands16(A, factors, factors, lane);
+    else
+        build_a_operands(A, factors, lu, lane);
 
     // The scheduling barriers keep each step's work after its look-ahead load
     // and before the next step's: hoisting the swaps of later units would
@@ -1245,7 +1315,7 @@ void mfma_groups(int64_t M, int64_t d, int w, bool adaln, int ring, const Tuning
     sh.grid = nGpad * nBG;
 }
 
-template <int kW, bool kAd, bool kNT, int kRing>
+template <int kW, bool kAd, bool kNT, int kRing, bool kB16 = false>
 hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT,
                                 uint8_t *q, uint8_t *s, float *y, int lu, const MfmaShape &sh, hipStream_t stream,
                                 AdArgs ad)
@@ -1256,8 +1326,8 @@ hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const f
     if constexpr (kAd)
         fn = (const void *)kq_mfma_kernel<true, kW, true, false, kRing>;
     else
-        fn = y ? (const void *)kq_mfma_kernel<false, kW, false, false, kRing>
-               : (const void *)kq_mfma_kernel<true, kW, false, kNT, kRing>;
+        fn = y ? (const void *)kq_mfma_kernel<false, kW, false, false, kRing, kB16>
+               : (const void *)kq_mfma_kernel<true, kW, false, kNT, kRing, kB16>;
     int di = (int)d;
     int per_block = nT > 1 ? 1 : 0;
     int nbg = (int)((d / 32 + kW - 1) / kW);
@@ -1411,20 +1481,30 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
     return sh.grid > 0x7FFFFFFF ? hipErrorInvalidConfiguration : hipSuccess;
 }
 
-template <int kRing>
+template <int kRing, bool kB16 = false>
 hipError_t launch_mfma_ring(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                             uint8_t *s, float *y, int lu, const MfmaShape &sh, hipStream_t stream)
 {
     const AdArgs ad{};
     const bool nt = sh.nt_codes && !y;
     if (sh.strip == 16)
-        return nt ? launch_mfma_instance<16, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-                  : launch_mfma_instance<16, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
-    if (sh.strip == 4)
-        return nt ? launch_mfma_instance<4, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-                  : launch_mfma_instance<4, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
-    return nt ? launch_mfma_instance<8, false, true, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
-              : launch_mfma_instance<8, false, false, kRing>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
+        return nt ? launch_mfma_instance<16, false, true, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+                  : launch_mfma_instance<16, false, false, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh, stream,
+                                                                        ad);
+    if (sh.strip == 4) {
+        // 16-element blocks reach the ring of 4 only in the persistent long
+        // runs, whose strips are 16 or 8 blocks wide; that instance (which
+        // spills two registers) is not built.
+        if constexpr (kB16 && kRing == 4)
+            return hipErrorInvalidConfiguration;
+        else
+            return nt ? launch_mfma_instance<4, false, true, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh, stream,
+                                                                          ad)
+                      : launch_mfma_instance<4, false, false, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh,
+                                                                           stream, ad);
+    }
+    return nt ? launch_mfma_instance<8, false, true, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad)
+              : launch_mfma_instance<8, false, false, kRing, kB16>(x, M, d, factors, nT, q, s, y, lu, sh, stream, ad);
 }
 
 // Flat form (one shared factor set).  Measured on MI355X over the configured
@@ -1608,14 +1688,26 @@ hipError_t launch_kq_butterfly(const uint16_t *x, int64_t M, int64_t d, const fl
     return launch_stream(y ? kBflyT : kBflyQ, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 
-// One shared set: the flat matrix-core kernel with the 32 x 32 block I (x) K16
-// (measured against the butterfly streaming kernel below); a set per block:
-// the butterfly streaming kernel.
+// One shared set: the flat matrix-core kernel with the 32 x 32 block I (x) K16;
+// a set per block and rows of whole 32-element pairs: the strip kernel with
+// the block diag(K16, K16') of each pair of sets, in the 32-element launch
+// shape; other rows: the butterfly streaming kernel.  Both matrix-core forms
+// measured faster than the butterfly at every configured shape.
 hipError_t launch_kq16(const uint16_t *x, int64_t M, int64_t d, const float *factors, int64_t nT, uint8_t *q,
                        uint8_t *s, float *y, const Tuning &tn, hipStream_t stream)
 {
-    if (nT == 1 && tn.shared_form != 1)
-        return launch_flat_instance<true>(x, M, d, factors, q, s, y, 0, tn, stream);
+    if (tn.shared_form != 1) {
+        if (nT == 1)
+            return launch_flat_instance<true>(x, M, d, factors, q, s, y, 0, tn, stream);
+        if (d % 32 == 0) {
+            MfmaShape sh{};
+            hipError_t e = mfma_launch_shape(M, d, tn, false, sh);
+            if (e != hipSuccess)
+                return e;
+            return sh.ring == 2 ? launch_mfma_ring<2, true>(x, M, d, factors, nT, q, s, y, 0, sh, stream)
+                                : launch_mfma_ring<4, true>(x, M, d, factors, nT, q, s, y, 0, sh, stream);
+        }
+    }
     return launch_stream(y ? kBfly16T : kBfly16Q, x, M, d, factors, nT > 1 ? 1 : 0, q, s, y, tn, stream);
 }
 

@@ -1,6 +1,7 @@
 """GPU parity of the 16-element-block quantizer (kq_quantize16,
-kq_transform16_f32; one shared set on the matrix cores, a set per block on
-the butterfly kernel) against the oracle, through the C ABI: transformed
+kq_transform16_f32) against the oracle, through the C ABI.  One shared set
+runs on the flat matrix-core kernel, a set per block on the strip kernel when
+rows are whole 32-element blocks, the butterfly kernel otherwise.  Transformed
 values within 2e-6 z + 2^-146, codes and scales bit-exact except
 tolerance-boundary elements (tests/parity.py with 16-element blocks),
 identity factors fully bit-exact.  Every case prints its shape and seed
@@ -152,11 +153,15 @@ def test_kq16_empty(K):
     assert q.shape == (0, 32) and s.shape == (0, 4)
 
 
-@pytest.mark.parametrize("name", ["dit_4608", "sweep_4096"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["dit_4608", "sweep_4096", "sweep_16384"])
 def test_kq16_full_size_sampled_rows(K, name):
+    # a set per block on the matrix-core kernel: one resident round of strips
+    # (4608, 4096 tokens) and the persistent long runs with the ring of 4
+    # (16384 tokens)
     M, d, _ = I.CONFIGS[name]
     say(f"[kq16 full] {name} M={M} d={d}")
-    x = I.make_activation(name)
+    x = I.make_activation(name) if name != "sweep_16384" else I.act_sweep_special(M, d, I.data_seed(name))[0]
     f = I.random_factors16(d // 16, I.factor_seed(name) + 16)
     q, s = K.kq_quantize16(dev_bf16(x), dev_f32(f))
     torch.cuda.synchronize()
