@@ -174,3 +174,69 @@ def test_kq16_full_size_sampled_rows(K, name):
     res = P.compare(q[rows], s[rows], qr, sr, ef, bf)
     say(f"    {len(rows)} rows: {res}")
     assert res["ok"], res
+
+
+@pytest.mark.timeout(900)
+def test_kq16_per_block_long_run_strips_of_8(K):
+    # the persistent long runs in strips of 8 blocks (rows of 70 blocks, so
+    # the last strip of each row is ragged) with the ring of 4: the first
+    # token count whose automatic shape is that one
+    d = 2240
+    for M in (65536, 98304, 131072):
+        sh = K.kq_launch_shape(M, d)
+        if sh["strip"] == 8 and sh["ring"] == 4:
+            break
+    else:
+        pytest.fail(f"no long run in strips of 8 at d={d}: {sh}")
+    say(f"[kq16 long run, strips of 8] M={M} d={d} shape={sh}")
+    x = I.act_dit_lognormal(M, d, 9870)[0]
+    f = I.random_factors16(d // 16, 9871)
+    q, s = K.kq_quantize16(dev_bf16(x), dev_f32(f))
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    rng = np.random.default_rng(9872)
+    rows = np.unique(np.concatenate([[0, 31, 32, M - 1], rng.integers(0, M, 28)]))
+    qr, sr, y32 = O.kq_quantize16(x[rows], f, want_y32=True)
+    _, z = O.kq_transform16(x[rows], f)
+    ef, bf = P.boundary_flags(z, y32, bw=16)
+    res = P.compare(q[rows], s[rows], qr, sr, ef, bf)
+    say(f"    {len(rows)} rows: {res}")
+    assert res["ok"], res
+
+
+CANARY16 = [(67, 1152, "per_block"), (45, 2240, "per_block"), (67, 1168, "per_block"), (67, 1168, "shared")]
+
+
+@pytest.mark.parametrize("M,d,sets", CANARY16, ids=[f"{m}x{d}-{s}" for m, d, s in CANARY16])
+def test_kq16_no_stray_writes(K, M, d, sets):
+    # guard bytes around q, s and y; ragged token tiles, ragged strips
+    # (d = 2240), rows with an odd number of 16-element blocks (d = 1168)
+    x = I.act_dit_lognormal(M, d, 9880 + d)[0]
+    f = I.random_factors16(d // 16 if sets == "per_block" else 1, 9881 + d)
+    xd, fd = dev_bf16(x), dev_f32(f)
+    guard = 4096
+    qbuf = torch.full((M * d // 2 + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((M * d // 16 + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    ybuf = torch.full((M * d + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+    q = qbuf[guard:guard + M * d // 2].view(M, d // 2)
+    s = sbuf[guard:guard + M * d // 16].view(M, d // 16)
+    y = ybuf[guard:guard + M * d].view(M, d)
+    say(f"[kq16 canary] M={M} d={d} sets={sets}")
+    K.kq_quantize16(xd, fd, q, s)
+    K.kq_transform16_f32(xd, fd, y)
+    torch.cuda.synchronize()
+    qb, sb, yb = qbuf.cpu().numpy(), sbuf.cpu().numpy(), ybuf.cpu().numpy()
+    assert (qb[:guard] == 0xA5).all() and (qb[-guard:] == 0xA5).all()
+    assert (sb[:guard] == 0x5A).all() and (sb[-guard:] == 0x5A).all()
+    assert (yb[:guard] == 7.0).all() and (yb[-guard:] == 7.0).all()
+    # a second call gives the same bytes
+    q2, s2 = K.kq_quantize16(xd, fd)
+    torch.cuda.synchronize()
+    assert torch.equal(q2, q) and torch.equal(s2, s)
+    qr, sr, y32 = O.kq_quantize16(x, f, want_y32=True)
+    yr, z = O.kq_transform16(x, f)
+    ef, bf = P.boundary_flags(z, y32, bw=16)
+    res = P.compare(q.cpu().numpy(), s.cpu().numpy(), qr, sr, ef, bf)
+    assert res["ok"], res
+    worst, outside = P.transform_error(y.cpu().numpy(), yr, z)
+    assert outside == 0, worst
