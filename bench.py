@@ -776,6 +776,18 @@ def main():
     value = step_bytes * args.steps / wall / 1e9
     avg_launch = ev / args.steps
     achieved = step_bytes / avg_launch / 1e9
+    # per-launch spread, outside the timed region: K single launches on the
+    # same stream, each between its own pair of HIP events
+    pairs = []
+    with torch.cuda.stream(cs_main):
+        for i in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cs_main)
+            step(i)
+            b.record(cs_main)
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    per_launch = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
     shape = K.kq_flat_launch_shape(M, d)
     src_hash = kernel_source_hash()
     kname = f"kq_flat_kernel<true, {'true' if shape['nt_codes'] else 'false'}, {shape['ring']}>"
@@ -784,7 +796,13 @@ def main():
                 "kernel": kname, "avg_launch_us": round(avg_launch * 1e6, 2), "launches_timed": args.steps,
                 "algorithmic_bytes_per_launch": round(step_bytes),
                 "timing": "HIP events on the launch stream around the timed graph of K steps (one launch each)",
-                "launch_shape": shape}
+                "launch_shape": shape,
+                "per_launch_us": {"median": round(float(np.median(per_launch)), 2),
+                                  "mean": round(float(np.mean(per_launch)), 2),
+                                  "min": round(per_launch[0], 2), "max": round(per_launch[-1], 2),
+                                  "launches": len(per_launch),
+                                  "timing": "K more launches after the timed region, each between its own "
+                                            "pair of HIP events on the launch stream"}}
     out = {
         "metric": METRIC,
         "value": round(value, 1),
