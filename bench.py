@@ -206,11 +206,11 @@ def summarize_traffic(fetch_dir, write_dir):
         "",
         "Commands (from the repository root, on one MI355X; each counter pass is a run of its own):",
         "",
-        "    timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+        f"    timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- "
         "python3 bench.py --traffic-run --steps 10",
-        "    timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+        f"    timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- "
         "python3 bench.py --traffic-run --steps 10",
-        "    python3 bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        f"    python3 bench.py --summarize-traffic {fetch_dir} {write_dir}",
         "",
         f"Calibration: a plain bf16->fp32 copy of {CAL_ELEMS} elements reads {CAL_READ} B and writes {CAL_WRITE} B; "
         f"its counters read FETCH_SIZE {blob['calibration']['fetch_kib_median']:.0f} KiB and WRITE_SIZE "
