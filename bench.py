@@ -249,7 +249,7 @@ def cpu_baseline(x_rows, f, tiny, min_seconds=10.0):
     from oracle import oracle as O
     O.lib()
     host_cores = os.cpu_count() or 1
-    threads = max(1, min(16, host_cores))  # the machine's CPU share is 16 threads
+    threads = max(1, min(16, host_cores))  # at most 16 threads: the host CPU share of one GPU
     rows = x_rows.shape[0]
     chunk = max(1, (rows + 4 * threads - 1) // (4 * threads))
     jobs = [np.ascontiguousarray(x_rows[r0:r0 + chunk]) for r0 in range(0, rows, chunk)]

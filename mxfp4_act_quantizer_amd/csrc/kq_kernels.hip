@@ -1280,7 +1280,7 @@ void mfma_groups(int64_t M, int64_t d, int w, bool adaln, int ring, const Tuning
         //  - At exactly 3 tiles per interleaved group, contiguous groups of 6
         //    tiles are faster while they still give 90% of the CUs a
         //    workgroup: half as many workgroups start, each with a longer
-        //    pipeline (measured at 8192 x 1152 on three boxes: 8.3 us against
+        //    pipeline (measured at 8192 x 1152 on three MI355X machines: 8.3 us against
         //    8.5-9.2).
         int64_t gx = resident / nBG; // token groups per XCD in one round
         if (gx < 1)
@@ -1345,7 +1345,7 @@ hipError_t launch_mfma_instance(const uint16_t *x, int64_t M, int64_t d, const f
 // interleave (tile = group + k * groups) and (group, strip) pairs are dealt in
 // flat order, so the workgroups walk one compact band of rows down the matrix
 // and each pays its start-up once.  Strips of 16 blocks when they divide the
-// row (measured on one box, 65536 x 12288: 329 us against 381 for contiguous
+// row (measured on one MI355X, 65536 x 12288: 329 us against 381 for contiguous
 // groups of 4 tiles in strips of 8; 16384 x 12288: 87.2 against 97.5).
 // Taken when that round needs more than 16 tiles per workgroup and fills at
 // least 80% of the resident slots; false otherwise.
@@ -1375,7 +1375,7 @@ bool mfma_long_run(int64_t M, int64_t d, MfmaShape &sh)
 // 16 and 8 blocks (whichever divide the row) the one that gives the longer
 // runs inside that range is taken.  Used when the shape above would put more
 // than one workgroup on a CU or walk fewer than 8 tiles per workgroup
-// (measured on two boxes against that shape: 4608 x 3072 10.1 against 11.2
+// (measured on two MI355X machines against that shape: 4608 x 3072 10.1 against 11.2
 // us, 2048 x 8960 12.0 against 12.8, 4608 x 12288 27.3 against 29.3, 4096 x
 // 12288 24.7 against 25.5, 2048 x 12288 14.4 against 15.0; at 8192 x 4608,
 // where that shape already is one round of 11 tiles per workgroup, this one
@@ -1405,7 +1405,7 @@ void mfma_one_per_cu(int64_t M, int64_t d, MfmaShape &sh)
     // In strips of 16 (16-wave workgroups) the longest runs of the range, 16
     // tiles, while they still give three CUs of four a workgroup: fewer
     // loads in flight per round measured faster (with the ring of 2, two
-    // boxes: 4608 x 12288 26.8 against 28.1-29.9 us for 15 tiles on 240
+    // machines: 4608 x 12288 26.8 against 28.1-29.9 us for 15 tiles on 240
     // workgroups; 4096 x 12288 25.5 against 27.3-29.4 for 13 tiles).
     if (best_w == 16 && best_t < 16 && 4 * ((nTiles + 15) / 16) * (nB / 16) >= 3 * cus)
         best_t = 16;
@@ -1465,9 +1465,9 @@ hipError_t mfma_launch_shape(int64_t M, int64_t d, const Tuning &tn, bool adaln,
     // Register ring: 2 tiles (one in flight ahead) except in the persistent
     // long runs and the AdaLN second pass, which keep 4.  Measured with
     // per-block factor sets, ring 2 against ring 4 in the same runs (three
-    // boxes): 2-8% faster at every configured shape below the long runs
+    // machines): 2-8% faster at every configured shape below the long runs
     // (8192 x 1152: 7.5 against 8.0 us; 8192 x 4608: 18.6 against 19.5), at
-    // 16384 x 12288 1% slower on two boxes of three (85.0 against 84.0), at
+    // 16384 x 12288 1% slower on two machines of three (85.0 against 84.0), at
     // 65536 x 12288 within the spread of identical legs.
     const int ring = tn.mfma_ring ? tn.mfma_ring : (adaln || long_run) ? 4 : 2;
     if (!long_run) {
